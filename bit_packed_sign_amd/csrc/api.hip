@@ -1,0 +1,197 @@
+// api.hip -- the C ABI of libbin1 (declared in include/bin1.h): argument validation,
+// dispatch to the kernels, status codes and the thread-local error text.
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include <cstdarg>
+#include <cstdio>
+#include <string>
+
+#include "bin1.h"
+#include "kernels.hpp"
+
+namespace {
+
+thread_local std::string g_last_error;
+
+int fail(int status, const char *fmt, ...) __attribute__((format(printf, 2, 3)));
+int fail(int status, const char *fmt, ...)
+{
+    char buf[512];
+    va_list ap;
+    va_start(ap, fmt);
+    vsnprintf(buf, sizeof buf, fmt, ap);
+    va_end(ap);
+    g_last_error = buf;
+    return status;
+}
+
+int ok()
+{
+    g_last_error.clear();
+    return BIN1_OK;
+}
+
+bool aligned16(const void *p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+bool overlap(const void *a, size_t na, const void *b, size_t nb)
+{
+    const uintptr_t a0 = reinterpret_cast<uintptr_t>(a), b0 = reinterpret_cast<uintptr_t>(b);
+    return a0 < b0 + nb && b0 < a0 + na;
+}
+
+// The pointer must be device memory (or managed memory) visible on the current device.
+int check_device(const void *p, const char *name)
+{
+    hipPointerAttribute_t attr;
+    hipError_t e = hipPointerGetAttributes(&attr, p);
+    if (e != hipSuccess) {
+        (void)hipGetLastError();
+        return fail(BIN1_ERR_DEVICE, "%s: not a HIP allocation (%s)", name, hipGetErrorString(e));
+    }
+    if (attr.type != hipMemoryTypeDevice && attr.type != hipMemoryTypeManaged)
+        return fail(BIN1_ERR_DEVICE, "%s: not device memory (memory type %d)", name, (int)attr.type);
+    int dev = -1;
+    if (hipGetDevice(&dev) != hipSuccess || attr.device != dev)
+        return fail(BIN1_ERR_DEVICE, "%s: allocated on device %d, current device is %d", name,
+                    attr.device, dev);
+    return BIN1_OK;
+}
+
+int launched(hipError_t e, const char *what)
+{
+    if (e != hipSuccess) return fail(BIN1_ERR_LAUNCH, "%s: %s", what, hipGetErrorString(e));
+    return ok();
+}
+
+// Shared validation of the (x, Wbits, scales, y, M, K, N) products.
+int check_product(const void *x, const void *W, const void *S, const void *y, int M, int K, int N)
+{
+    if (!x || !W || !S || !y) return fail(BIN1_ERR_NULL, "x, Wbits, scales and y must be non-NULL");
+    if (M < 1 || N < 1 || K < 128 || K % 128 != 0)
+        return fail(BIN1_ERR_SHAPE, "need M>=1, N>=1, K>=128, K%%128==0 (got M=%d K=%d N=%d)", M, K, N);
+    if (!aligned16(x) || !aligned16(W) || !aligned16(S) || !aligned16(y))
+        return fail(BIN1_ERR_ALIGN, "x, Wbits, scales and y must be 16-byte aligned");
+    const size_t xb = (size_t)M * K * 2, wb = (size_t)N * (K / 8), sb = (size_t)N * (K / 128) * 2,
+                 yb = (size_t)M * N * 2;
+    if (overlap(y, yb, x, xb) || overlap(y, yb, W, wb) || overlap(y, yb, S, sb))
+        return fail(BIN1_ERR_ALIAS, "y overlaps an input");
+    int st;
+    if ((st = check_device(x, "x")) || (st = check_device(W, "Wbits")) ||
+        (st = check_device(S, "scales")) || (st = check_device(y, "y")))
+        return st;
+    return BIN1_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int bin1_abi_version(void) { return BIN1_ABI_VERSION; }
+
+const char *bin1_last_error(void) { return g_last_error.c_str(); }
+
+const char *bin1_status_string(int status)
+{
+    switch (status) {
+    case BIN1_OK: return "BIN1_OK";
+    case BIN1_ERR_NULL: return "BIN1_ERR_NULL: a required pointer is NULL";
+    case BIN1_ERR_SHAPE: return "BIN1_ERR_SHAPE: a size is out of range";
+    case BIN1_ERR_ALIGN: return "BIN1_ERR_ALIGN: a data pointer is not 16-byte aligned";
+    case BIN1_ERR_ALIAS: return "BIN1_ERR_ALIAS: the output overlaps an input";
+    case BIN1_ERR_DEVICE: return "BIN1_ERR_DEVICE: a pointer is not device memory of the current device";
+    case BIN1_ERR_LAUNCH: return "BIN1_ERR_LAUNCH: the HIP runtime refused the launch";
+    default: return "unknown bin1 status";
+    }
+}
+
+int bin1_gemv(const void *x, const uint32_t *Wbits, const void *scales, void *y, int M, int K,
+              int N, void *stream)
+{
+    int st = check_product(x, Wbits, scales, y, M, K, N);
+    if (st) return st;
+    return launched(bin1::launch_gemv(static_cast<const uint16_t *>(x), Wbits,
+                                      static_cast<const uint16_t *>(scales),
+                                      static_cast<uint16_t *>(y), M, K, N,
+                                      static_cast<hipStream_t>(stream)),
+                    "bin1_gemv");
+}
+
+int bin1_gemm_prefill(const void *x, const uint32_t *Wbits, const void *scales, void *y, int M,
+                      int K, int N, void *stream)
+{
+    int st = check_product(x, Wbits, scales, y, M, K, N);
+    if (st) return st;
+    return launched(bin1::launch_prefill(static_cast<const uint16_t *>(x), Wbits,
+                                         static_cast<const uint16_t *>(scales),
+                                         static_cast<uint16_t *>(y), M, K, N,
+                                         static_cast<hipStream_t>(stream)),
+                    "bin1_gemm_prefill");
+}
+
+int bin1_gemv_pm1(const uint32_t *Abits, const uint32_t *Wbits, int32_t *y, int M, int K, int N,
+                  void *stream)
+{
+    if (!Abits || !Wbits || !y) return fail(BIN1_ERR_NULL, "Abits, Wbits and y must be non-NULL");
+    if (M < 1 || N < 1 || K < 128 || K % 128 != 0)
+        return fail(BIN1_ERR_SHAPE, "need M>=1, N>=1, K>=128, K%%128==0 (got M=%d K=%d N=%d)", M, K, N);
+    if (!aligned16(Abits) || !aligned16(Wbits) || !aligned16(y))
+        return fail(BIN1_ERR_ALIGN, "Abits, Wbits and y must be 16-byte aligned");
+    const size_t ab = (size_t)M * (K / 8), wb = (size_t)N * (K / 8), yb = (size_t)M * N * 4;
+    if (overlap(y, yb, Abits, ab) || overlap(y, yb, Wbits, wb))
+        return fail(BIN1_ERR_ALIAS, "y overlaps an input");
+    int st;
+    if ((st = check_device(Abits, "Abits")) || (st = check_device(Wbits, "Wbits")) ||
+        (st = check_device(y, "y")))
+        return st;
+    return launched(bin1::launch_pm1(Abits, Wbits, y, M, K, N, static_cast<hipStream_t>(stream)),
+                    "bin1_gemv_pm1");
+}
+
+int bin1_xor_patch_apply(uint32_t *Wbits, const int32_t *rowlist, int nrows, int K, int N,
+                         int32_t *bad_rows, void *stream)
+{
+    if (nrows < 0 || N < 1 || K < 128 || K % 128 != 0)
+        return fail(BIN1_ERR_SHAPE, "need nrows>=0, N>=1, K>=128, K%%128==0 (got nrows=%d K=%d N=%d)",
+                    nrows, K, N);
+    if (nrows == 0) return ok();
+    if (!Wbits || !rowlist) return fail(BIN1_ERR_NULL, "Wbits and rowlist must be non-NULL");
+    if (!aligned16(Wbits)) return fail(BIN1_ERR_ALIGN, "Wbits must be 16-byte aligned");
+    if (reinterpret_cast<uintptr_t>(rowlist) & 3u || reinterpret_cast<uintptr_t>(bad_rows) & 3u)
+        return fail(BIN1_ERR_ALIGN, "rowlist and bad_rows must be 4-byte aligned");
+    const size_t wb = (size_t)N * (K / 8);
+    if (overlap(Wbits, wb, rowlist, (size_t)nrows * 4) || (bad_rows && overlap(Wbits, wb, bad_rows, 4)))
+        return fail(BIN1_ERR_ALIAS, "Wbits overlaps rowlist or bad_rows");
+    int st;
+    if ((st = check_device(Wbits, "Wbits")) || (st = check_device(rowlist, "rowlist")) ||
+        (bad_rows && (st = check_device(bad_rows, "bad_rows"))))
+        return st;
+    return launched(bin1::launch_xor_patch(Wbits, rowlist, nrows, K, N, bad_rows,
+                                           static_cast<hipStream_t>(stream)),
+                    "bin1_xor_patch_apply");
+}
+
+int bin1_xor_patch_apply_multi(uint32_t *const *Wtab, const int32_t *Ktab, const int32_t *Ntab,
+                               int nmat, const int32_t *entries, int nentries, int32_t *bad_rows,
+                               void *stream)
+{
+    if (nentries < 0 || nmat < 1)
+        return fail(BIN1_ERR_SHAPE, "need nentries>=0 and nmat>=1 (got %d, %d)", nentries, nmat);
+    if (nentries == 0) return ok();
+    if (!Wtab || !Ktab || !Ntab || !entries)
+        return fail(BIN1_ERR_NULL, "Wtab, Ktab, Ntab and entries must be non-NULL");
+    if (reinterpret_cast<uintptr_t>(Wtab) & 7u || reinterpret_cast<uintptr_t>(Ktab) & 3u ||
+        reinterpret_cast<uintptr_t>(Ntab) & 3u || reinterpret_cast<uintptr_t>(entries) & 3u ||
+        reinterpret_cast<uintptr_t>(bad_rows) & 3u)
+        return fail(BIN1_ERR_ALIGN, "tables must be naturally aligned");
+    int st;
+    if ((st = check_device(Wtab, "Wtab")) || (st = check_device(Ktab, "Ktab")) ||
+        (st = check_device(Ntab, "Ntab")) || (st = check_device(entries, "entries")) ||
+        (bad_rows && (st = check_device(bad_rows, "bad_rows"))))
+        return st;
+    return launched(bin1::launch_xor_patch_multi(Wtab, Ktab, Ntab, nmat, entries, nentries, bad_rows,
+                                                 static_cast<hipStream_t>(stream)),
+                    "bin1_xor_patch_apply_multi");
+}
+
+}  // extern "C"

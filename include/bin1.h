@@ -1,0 +1,125 @@
+/*
+ * bin1.h -- C ABI of libbin1: 1-bit sign-packed GEMV / GEMM and XOR row patching
+ * on AMD Instinct MI355X (gfx950).
+ *
+ * The method (sources are the pages listed here by title and section):
+ *  - Weight format: every weight is a sign in {-1,+1} held in one bit, and each run
+ *    of 128 consecutive weights along K shares one fp16 scale, w = s_g * b, i.e.
+ *    1 + 16/128 = 1.125 bits per weight.  ["Bonsai 27B: ... (feat. PrismML)",
+ *    discuss.pytorch.kr, section "Binary weight format" (이진(Binary) 가중치 형식),
+ *    eq. b_eff]
+ *  - Kernel semantics: the packed codes are consumed directly; the sign codes are
+ *    decoded and the group scale applied inside the fused product, with no dense
+ *    fp16 copy of the weights, and activations/accumulation kept in high precision.
+ *    [same page, section "Low-bit kernels for hybrid attention"
+ *    (하이브리드 어텐션을 위한 저비트 커널)]
+ *  - With +-1 weights the products are additions and subtractions and the matmul
+ *    becomes bit operations.  ["PrismML Bonsai -- 1.15GB ...", jangwook.net,
+ *    section "What 1-bit is" (1-bit이 뭔지부터)]
+ *  - Patch: a list of rows (of a given projection in a given layer) whose bits are
+ *    flipped in place; it adds no matmul at inference and the same XOR removes it.
+ *    It is defined only for true binary weights (for ternary codes an XOR can leave
+ *    the valid states).  ["LocalLLaMA ... XOR patch 'Bankai'", insights.marvin-42.com,
+ *    sections "Key points" and "Why it holds only for true 1-bit models"]
+ *
+ * Layouts (row-major, contiguous, little-endian).  K is the input width, N the number
+ * of output rows, M the number of activation rows (tokens):
+ *   x       fp16   [M][K]
+ *   Wbits   uint32 [N][K/32]  weight (n, k) is bit (k % 32) of word [n][k / 32];
+ *                             bit 1 means +1, bit 0 means -1 (LSB-first along K)
+ *   scales  fp16   [N][K/128] scale of weights k in [128g, 128g+128) of row n
+ *   y       fp16   [M][N]     y[m][n] = sum_k scales[n][k/128] * w(n,k) * x[m][k],
+ *                             accumulated in fp32, rounded once to fp16 (nearest-even)
+ *   Abits   uint32 [M][K/32]  +-1 activations packed like Wbits (popcount mode)
+ *
+ * Conventions for every call:
+ *  - Data pointers are DEVICE pointers on the current HIP device, owned by the caller.
+ *    The library never allocates, frees or synchronises; a call validates its
+ *    arguments on the host and then only enqueues kernels on `stream` (a hipStream_t
+ *    passed as void*; NULL means the legacy default stream).  Calls may therefore be
+ *    captured into a HIP graph.
+ *  - Validation happens before anything is enqueued; on any error nothing is enqueued
+ *    and the outputs are untouched.
+ *  - Requirements: M >= 1, N >= 1, K >= 128, K % 128 == 0; x, Wbits, scales, y, Abits
+ *    16-byte aligned; y must not overlap any input.
+ *  - Device-side faults surface at the caller's next synchronisation, as with any
+ *    HIP kernel.  BIN1_ERR_LAUNCH carries the HIP error text in bin1_last_error().
+ *  - The library is stateless apart from a thread-local error string: calls are
+ *    reentrant and may run concurrently on different streams.
+ */
+#ifndef BIN1_H
+#define BIN1_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define BIN1_ABI_VERSION 1
+
+typedef enum bin1_status {
+    BIN1_OK = 0,
+    BIN1_ERR_NULL = -1,     /* a required pointer is NULL                               */
+    BIN1_ERR_SHAPE = -2,    /* M, N, K (or a count) out of range / K not a multiple of 128 */
+    BIN1_ERR_ALIGN = -3,    /* a data pointer is not 16-byte aligned                     */
+    BIN1_ERR_ALIAS = -4,    /* the output range overlaps an input range                  */
+    BIN1_ERR_DEVICE = -5,   /* a pointer is not device memory of the current device      */
+    BIN1_ERR_LAUNCH = -6    /* the HIP runtime refused the launch (see bin1_last_error)  */
+} bin1_status;
+
+/* Decode GEMV / small-batch product: y = x * W^T with W = scales (x) signs, per the
+ * layouts above.  Tuned for M in 1..16; correct for any M >= 1 (M > 16 is routed to
+ * the prefill kernel).  The signs are expanded without multiplies and the group scale
+ * is applied once per 128-weight group; accumulation is fp32; y is fully overwritten. */
+int bin1_gemv(const void *x, const uint32_t *Wbits, const void *scales, void *y,
+              int M, int K, int N, void *stream);
+
+/* Prefill product, same arguments and result as bin1_gemv; tuned for M >= 256 (the
+ * pages note that prompt processing is compute-bound: ["Bonsai 27B", section "Low-bit
+ * kernels for hybrid attention"]).  Bit tiles are unpacked into LDS as fp16 +-scale
+ * and contracted on the matrix cores with fp32 accumulation.  Correct for any M >= 1. */
+int bin1_gemm_prefill(const void *x, const uint32_t *Wbits, const void *scales, void *y,
+                      int M, int K, int N, void *stream);
+
+/* +-1 activations times +-1 weights, exact:
+ *   y[m][n] = sum_k a(m,k) * w(n,k) = K - 2 * popcount(Abits[m] xor Wbits[n])  (int32).
+ * Scales are not used.  ["PrismML Bonsai -- 1.15GB ...", section "What 1-bit is"] */
+int bin1_gemv_pm1(const uint32_t *Abits, const uint32_t *Wbits, int32_t *y,
+                  int M, int K, int N, void *stream);
+
+/* XOR row patch, in place: for each entry r of rowlist (device int32[nrows]) every
+ * word of row r of Wbits ([N][K/32]) is complemented, i.e. all K signs of output row
+ * r are flipped (y[:, r] -> -y[:, r]); scales are untouched.  Calling it again with
+ * the same list removes the patch.  Entries must be distinct (duplicates within one
+ * call race); entries outside [0, N) are skipped and, if bad_rows (device int32*,
+ * may be NULL) is given, counted into *bad_rows by atomic add (the caller zeroes it).
+ * nrows == 0 is a no-op.  Order the call on the same stream as the products that
+ * read Wbits.  ["LocalLLaMA ... XOR patch 'Bankai'", section "Key points"] */
+int bin1_xor_patch_apply(uint32_t *Wbits, const int32_t *rowlist, int nrows,
+                         int K, int N, int32_t *bad_rows, void *stream);
+
+/* The same patch over many matrices in one launch -- (layer, projection, row) records.
+ * Wtab (device uint32_t*[nmat]), Ktab and Ntab (device int32[nmat]) describe the
+ * matrices; entries (device int32[nentries][2]) holds (matrix id, row) pairs.  Entries
+ * with a matrix id outside [0, nmat), a row outside [0, N_id), or a K_id that is not a
+ * positive multiple of 128 are skipped and counted into *bad_rows when given.  Entries
+ * must be distinct.  nentries == 0 is a no-op. */
+int bin1_xor_patch_apply_multi(uint32_t *const *Wtab, const int32_t *Ktab, const int32_t *Ntab,
+                               int nmat, const int32_t *entries, int nentries,
+                               int32_t *bad_rows, void *stream);
+
+/* Static description of a status code. */
+const char *bin1_status_string(int status);
+
+/* Thread-local detail of the last error returned on this thread ("" if none). */
+const char *bin1_last_error(void);
+
+/* == BIN1_ABI_VERSION */
+int bin1_abi_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* BIN1_H */

@@ -1,0 +1,96 @@
+"""Host-side checks of the C ABI: the library loads, exports every declared symbol, and
+rejects bad arguments before touching the GPU (no kernel is launched by these tests)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "bin1.h")
+
+
+def _declared():
+    src = open(HEADER).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"\b(bin1_[a-z0-9_]+)\s*\(", src)))
+
+
+@pytest.fixture(scope="module")
+def L():
+    from bit_packed_sign_amd import binding
+    if not os.path.exists(binding.LIB_PATH):
+        from bit_packed_sign_amd import build
+        build.build()
+    return binding.lib()
+
+
+def test_header_declares_the_entry_points():
+    names = _declared()
+    for fn in ["bin1_gemv", "bin1_gemm_prefill", "bin1_gemv_pm1", "bin1_xor_patch_apply",
+               "bin1_xor_patch_apply_multi", "bin1_status_string", "bin1_last_error",
+               "bin1_abi_version"]:
+        assert fn in names
+
+
+def test_library_exports_every_declared_symbol(L):
+    raw = ctypes.CDLL(os.path.join(ROOT, "bit_packed_sign_amd", "libbin1.so"))
+    for fn in _declared():
+        assert hasattr(raw, fn), fn
+
+
+def test_binding_covers_every_declared_symbol():
+    from bit_packed_sign_amd import binding
+    assert sorted(binding._SIGS) == _declared()
+
+
+def test_version_and_status_strings(L):
+    assert L.bin1_abi_version() == 1
+    for st in range(0, -7, -1):
+        assert L.bin1_status_string(st).startswith(b"BIN1_")
+    assert b"unknown" in L.bin1_status_string(42)
+
+
+FAKE = 0x10000  # 16-byte-aligned fake address: never dereferenced, checks fail before use
+
+
+@pytest.mark.parametrize("fn", ["bin1_gemv", "bin1_gemm_prefill"])
+def test_product_validation(L, fn):
+    f = getattr(L, fn)
+    assert f(None, FAKE, FAKE, FAKE, 1, 128, 1, None) == -1
+    assert b"non-NULL" in L.bin1_last_error()
+    assert f(FAKE, FAKE, FAKE, FAKE * 2, 0, 128, 1, None) == -2
+    assert f(FAKE, FAKE, FAKE, FAKE * 2, 1, 100, 1, None) == -2
+    assert f(FAKE, FAKE, FAKE, FAKE * 2, 1, 0, 1, None) == -2
+    assert f(FAKE, FAKE, FAKE, FAKE * 2, 1, 128, 0, None) == -2
+    assert f(FAKE + 2, FAKE * 3, FAKE * 4, FAKE * 5, 1, 128, 1, None) == -3
+    # y overlapping x (x occupies M*K*2 bytes from FAKE)
+    assert f(FAKE, FAKE * 8, FAKE * 9, FAKE + 128, 1, 128, 1, None) == -4
+    assert b"overlaps" in L.bin1_last_error()
+
+
+def test_pm1_and_patch_validation(L):
+    assert L.bin1_gemv_pm1(None, FAKE, FAKE, 1, 128, 1, None) == -1
+    assert L.bin1_gemv_pm1(FAKE, FAKE * 2, FAKE * 3, 1, 96, 1, None) == -2
+    assert L.bin1_gemv_pm1(FAKE, FAKE * 2, FAKE + 4, 1, 128, 1, None) == -3
+    # an empty patch is a no-op that succeeds without touching anything
+    assert L.bin1_xor_patch_apply(None, None, 0, 128, 1, None, None) == 0
+    assert L.bin1_xor_patch_apply(FAKE, FAKE * 2, -1, 128, 1, None, None) == -2
+    assert L.bin1_xor_patch_apply(None, FAKE, 3, 128, 1, None, None) == -1
+    assert L.bin1_xor_patch_apply(FAKE + 4, FAKE * 2, 3, 128, 1, None, None) == -3
+    assert L.bin1_xor_patch_apply(FAKE, FAKE, 3, 128, 1, None, None) == -4
+    assert L.bin1_xor_patch_apply_multi(None, None, None, 1, None, 0, None, None) == 0
+    assert L.bin1_xor_patch_apply_multi(FAKE, FAKE, FAKE, 0, FAKE, 1, None, None) == -2
+    assert L.bin1_xor_patch_apply_multi(None, FAKE, FAKE, 1, FAKE, 1, None, None) == -1
+
+
+def test_binding_rejects_cpu_tensors():
+    import torch
+    import bit_packed_sign_amd as b1
+    x = torch.zeros(1, 128, dtype=torch.float16)
+    W = torch.zeros(1, 4, dtype=torch.int32)
+    S = torch.zeros(1, 1, dtype=torch.float16)
+    with pytest.raises(ValueError):
+        b1.gemv(x, W, S)
+    with pytest.raises(ValueError):
+        b1.xor_patch_apply(W, torch.zeros(1, dtype=torch.int32))

@@ -1,0 +1,114 @@
+"""GPU parity of bin1_gemv (decode / small-batch) against the fp64 oracle."""
+import numpy as np
+import pytest
+import torch
+
+import bit_packed_sign_amd as b1
+from bit_packed_sign_amd import synth
+from parity import TOL, dev_tensors, norm_err, sample_rows
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def dev():
+    assert torch.cuda.is_available(), "GPU tests need a GPU"
+    return torch.device("cuda:0")
+
+
+def _case(t, M, K, N):
+    r = synth.rng_for(0, synth.WL_TEST, t)
+    return synth.activations(r, M, K), synth.sign_words(r, N, K), synth.group_scales(r, N, K)
+
+
+SMALL = [(128, 1), (128, 7), (256, 64), (512, 300), (1024, 1000), (4096, 1024), (12288, 130), (17408, 33)]
+
+
+@pytest.mark.parametrize("K,N", SMALL)
+@pytest.mark.parametrize("M", [1, 2, 3, 4, 5, 8, 16])
+def test_gemv_matches_oracle(orc, dev, M, K, N):
+    x, W, S = _case(1000 + K + N + M, M, K, N)
+    ref, nrm = orc.gemv(x, W, S)
+    xd, Wd, Sd = dev_tensors(dev, x, W, S)
+    y = b1.gemv(xd, Wd, Sd)
+    assert norm_err(y, ref, nrm) <= TOL
+
+
+FULL = [(4096, 4096), (4096, 1024), (4096, 12288), (12288, 4096), (4096, 151936),
+        (5120, 5120), (5120, 17408), (17408, 5120)]
+
+
+@pytest.mark.parametrize("K,N", FULL)
+@pytest.mark.parametrize("M", [1, 16])
+def test_gemv_full_size_sampled(orc, dev, M, K, N):
+    """Projection shapes of the 8B and 27B decode steps, every output computed on the GPU,
+    sampled outputs checked against the oracle."""
+    x, W, S = _case(2000 + K + N + M, M, K, N)
+    xd, Wd, Sd = dev_tensors(dev, x, W, S)
+    y = b1.gemv(xd, Wd, Sd).float().cpu().numpy()
+    rows = sample_rows(synth.rng_for(0, synth.WL_TEST, 3000 + N), N)
+    ref, nrm = orc.gemv_rows(x, W, S, rows)
+    assert norm_err(y[:, rows], ref, nrm) <= TOL
+    assert np.all(np.isfinite(y))
+
+
+def test_closed_form_and_one_hot_rows(orc, dev):
+    K = 512
+    r = synth.rng_for(0, synth.WL_TEST, 4000)
+    x = synth.activations(r, 2, K)
+    positions = [0, 1, 31, 32, 63, 127, 128, 300, 511]
+    N = 2 + len(positions)
+    W = np.zeros((N, K // 32), np.uint32)
+    W[0] = 0xFFFFFFFF
+    for n, k in enumerate(positions):
+        W[2 + n, k // 32] = np.uint32(1) << np.uint32(k % 32)
+    S = synth.group_scales(r, N, K)
+    ref, nrm = orc.gemv(x, W, S)
+    y = b1.gemv(*dev_tensors(dev, x, W, S))
+    assert norm_err(y, ref, nrm) <= TOL
+
+
+def test_scale_edge_cases(orc, dev):
+    """Zero, subnormal and negative scales; zero activations."""
+    K, N = 1024, 64
+    x, W, S = _case(4100, 3, K, N)
+    S = S.copy()
+    S[0] = 0
+    S[1] = np.float16(2.0 ** -24)
+    S[2, ::2] = np.float16(3.0e-6)
+    S[3] = -S[3]
+    S[4, 3] = np.float16(-0.0)
+    x = x.copy()
+    x[1] = 0
+    ref, nrm = orc.gemv(x, W, S)
+    y = b1.gemv(*dev_tensors(dev, x, W, S))
+    assert norm_err(y, ref, nrm) <= TOL
+    yn = y.float().cpu().numpy()
+    assert np.all(yn[:, 0] == 0) and np.all(yn[1] == 0)
+
+
+def test_patched_rows_negate_output(dev):
+    """Flipping whole rows negates those outputs bit for bit and leaves the rest unchanged."""
+    M, K, N = 1, 4096, 4096
+    x, W, S = _case(4200, M, K, N)
+    xd, Wd, Sd = dev_tensors(dev, x, W, S)
+    y0 = b1.gemv(xd, Wd, Sd).clone()
+    rows = torch.from_numpy(synth.patch_rows_single()).to(dev)
+    b1.xor_patch_apply(Wd, rows)
+    y1 = b1.gemv(xd, Wd, Sd)
+    b1.xor_patch_apply(Wd, rows)
+    mask = torch.zeros(N, dtype=torch.bool, device=dev)
+    mask[rows.long()] = True
+    assert torch.equal(y1[:, mask], -y0[:, mask])
+    assert torch.equal(y1[:, ~mask], y0[:, ~mask])
+    assert torch.equal(Wd.cpu(), torch.from_numpy(W.view(np.int32)))
+
+
+def test_output_is_fully_overwritten_and_out_argument(orc, dev):
+    M, K, N = 2, 256, 77
+    x, W, S = _case(4300, M, K, N)
+    ref, nrm = orc.gemv(x, W, S)
+    xd, Wd, Sd = dev_tensors(dev, x, W, S)
+    out = torch.full((M, N), float("nan"), dtype=torch.float16, device=dev)
+    b1.gemv(xd, Wd, Sd, out=out)
+    assert norm_err(out, ref, nrm) <= TOL

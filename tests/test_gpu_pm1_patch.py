@@ -1,0 +1,113 @@
+"""GPU checks of the exact paths: +-1 popcount product and XOR row patches (bit-exact)."""
+import numpy as np
+import pytest
+import torch
+
+import bit_packed_sign_amd as b1
+from bit_packed_sign_amd import synth
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def dev():
+    assert torch.cuda.is_available(), "GPU tests need a GPU"
+    return torch.device("cuda:0")
+
+
+def _i32(a):
+    return torch.from_numpy(np.ascontiguousarray(a).view(np.int32))
+
+
+@pytest.mark.parametrize("M,K,N", [(1, 128, 1), (1, 4096, 4096), (3, 512, 77), (16, 12288, 300),
+                                   (9, 17408, 65), (1, 4096, 151936)])
+def test_pm1_bit_exact(orc, dev, M, K, N):
+    r = synth.rng_for(0, synth.WL_TEST, 6000 + M + K + N)
+    A = synth.pm1_words(r, M, K)
+    W = synth.sign_words(r, N, K)
+    y = b1.gemv_pm1(_i32(A).to(dev), _i32(W).to(dev)).cpu().numpy()
+    if N > 5000:
+        rows = np.sort(r.choice(N, 512, replace=False))
+        assert np.array_equal(y[:, rows], orc.pm1(A, W[rows], K))
+    else:
+        assert np.array_equal(y, orc.pm1(A, W, K))
+
+
+def test_pm1_extremes(orc, dev):
+    K = 256
+    A = np.array([[0xFFFFFFFF] * 8, [0] * 8], np.uint32)
+    W = np.array([[0xFFFFFFFF] * 8, [0] * 8, [0xAAAAAAAA] * 8], np.uint32)
+    y = b1.gemv_pm1(_i32(A).to(dev), _i32(W).to(dev)).cpu().numpy()
+    assert np.array_equal(y, orc.pm1(A, W, K))
+    assert y[0, 0] == K and y[0, 1] == -K and y[0, 2] == 0
+
+
+def test_single_matrix_patch_apply_remove(orc, dev):
+    """4096x4096 weights, 64 distinct rows: apply then remove, bit-exact against the oracle."""
+    K = N = 4096
+    W = synth.sign_words(synth.rng_for(0, synth.WL_SINGLE, 0), N, K)
+    rows = synth.patch_rows_single()
+    Wd = _i32(W).to(dev)
+    rd = torch.from_numpy(rows).to(dev)
+    bad = torch.zeros(1, dtype=torch.int32, device=dev)
+    b1.xor_patch_apply(Wd, rd, bad_rows=bad)
+    expect, nbad = orc.xor_patch(W, rows, K)
+    assert np.array_equal(Wd.cpu().numpy().view(np.uint32), expect)
+    b1.xor_patch_apply(Wd, rd, bad_rows=bad)
+    assert np.array_equal(Wd.cpu().numpy().view(np.uint32), W)
+    assert int(bad.item()) == 0 and nbad == 0
+
+
+def test_patch_out_of_range_and_empty(orc, dev):
+    K, N = 256, 40
+    W = synth.sign_words(synth.rng_for(0, synth.WL_TEST, 6100), N, K)
+    rows = np.array([-5, 0, 39, 40, 1000, 7], np.int32)
+    Wd = _i32(W).to(dev)
+    bad = torch.zeros(1, dtype=torch.int32, device=dev)
+    b1.xor_patch_apply(Wd, torch.from_numpy(rows).to(dev), bad_rows=bad)
+    expect, nbad = orc.xor_patch(W, rows, K)
+    assert np.array_equal(Wd.cpu().numpy().view(np.uint32), expect)
+    assert int(bad.item()) == nbad == 3
+    b1.xor_patch_apply(Wd, torch.zeros(0, dtype=torch.int32, device=dev))
+    assert np.array_equal(Wd.cpu().numpy().view(np.uint32), expect)
+    with pytest.raises(ValueError):
+        b1.xor_patch_apply(Wd, torch.tensor([1, 1], dtype=torch.int32, device=dev))
+
+
+def test_multi_matrix_patch_27b_mlp(orc, dev):
+    """2000 distinct (layer, projection, row) flips over all 192 MLP matrices of the 27B
+    decode workload in one launch; every matrix bit-exact after apply and after removal."""
+    mats = synth.mlp_rows_27b()
+    r = synth.rng_for(0, synth.WL_TEST, 6200)
+    host = []
+    for (_, p, n) in mats:
+        K = 5120 if p in ("gate", "up") else 17408
+        host.append(synth.sign_words(r, n, K))
+    devm = [_i32(h).to(dev) for h in host]
+    table = b1.PatchTable(devm)
+    ent = synth.patch_entries_27b()
+    ed = torch.from_numpy(ent).to(dev)
+    bad = torch.zeros(1, dtype=torch.int32, device=dev)
+    b1.xor_patch_apply_multi(table, ed, bad_rows=bad)
+    torch.cuda.synchronize()
+    for mid, (h, d) in enumerate(zip(host, devm)):
+        rows = ent[ent[:, 0] == mid, 1]
+        expect, _ = orc.xor_patch(h, rows, h.shape[1] * 32)
+        assert np.array_equal(d.cpu().numpy().view(np.uint32), expect), mid
+    b1.xor_patch_apply_multi(table, ed, bad_rows=bad)
+    for h, d in zip(host, devm):
+        assert np.array_equal(d.cpu().numpy().view(np.uint32), h)
+    assert int(bad.item()) == 0
+
+
+def test_multi_patch_bad_entries_counted(dev):
+    W = synth.sign_words(synth.rng_for(0, synth.WL_TEST, 6300), 10, 128)
+    Wd = _i32(W).to(dev)
+    table = b1.PatchTable([Wd])
+    ent = torch.tensor([[0, 2], [1, 0], [-1, 0], [0, 10], [0, -1]], dtype=torch.int32, device=dev)
+    bad = torch.zeros(1, dtype=torch.int32, device=dev)
+    b1.xor_patch_apply_multi(table, ent, bad_rows=bad)
+    got = Wd.cpu().numpy().view(np.uint32)
+    expect = W.copy()
+    expect[2] ^= np.uint32(0xFFFFFFFF)
+    assert np.array_equal(got, expect) and int(bad.item()) == 4
