@@ -27,6 +27,7 @@ _i = ctypes.c_int
 _SIGS = {
     "bin1_gemv": [_p, _p, _p, _p, _i, _i, _i, _p],
     "bin1_gemm_prefill": [_p, _p, _p, _p, _i, _i, _i, _p],
+    "bin1_gemv_group": [_p, _i, _p, _p, _p, _p, _i, _i, _p],
     "bin1_gemv_pm1": [_p, _p, _p, _i, _i, _i, _p],
     "bin1_xor_patch_apply": [_p, _p, _i, _i, _i, _p, _p],
     "bin1_xor_patch_apply_multi": [_p, _p, _p, _i, _p, _i, _p, _p],
@@ -109,6 +110,40 @@ def _product(fn: str, x, Wbits, scales, out):
 def gemv(x: torch.Tensor, Wbits: torch.Tensor, scales: torch.Tensor, out: Optional[torch.Tensor] = None):
     """y[M][N] (fp16) = x[M][K] (fp16) times the 1-bit weights (Wbits [N][K/32], scales [N][K/128])."""
     return _product("bin1_gemv", x, Wbits, scales, out)
+
+
+def gemv_group(x: torch.Tensor, Wbits: Sequence[torch.Tensor], scales: Sequence[torch.Tensor],
+               outs: Optional[Sequence[torch.Tensor]] = None):
+    """Products of several matrices with the same activations x (e.g. q/k/v), one launch at M=1.
+    Returns the list of outputs y_i [M][N_i]."""
+    _need(x, "x", (torch.float16,), 2)
+    count = len(Wbits)
+    if count < 1 or count > 4 or len(scales) != count:
+        raise ValueError("need 1..4 matrices with one scale tensor each")
+    M, K = x.shape
+    Ns = []
+    for i, (W, S) in enumerate(zip(Wbits, scales)):
+        _need(W, f"Wbits[{i}]", _BITS, 2)
+        _need(S, f"scales[{i}]", (torch.float16,), 2)
+        if W.shape[1] * 32 != K or tuple(S.shape) != (W.shape[0], K // 128):
+            raise ValueError(f"matrix {i}: shapes do not match x")
+        Ns.append(W.shape[0])
+    if outs is None:
+        outs = [torch.empty((M, n), dtype=torch.float16, device=x.device) for n in Ns]
+    else:
+        for i, o in enumerate(outs):
+            _need(o, f"outs[{i}]", (torch.float16,), 2)
+            if tuple(o.shape) != (M, Ns[i]):
+                raise ValueError(f"outs[{i}] has the wrong shape")
+    arr_p = ctypes.c_void_p * count
+    wp = arr_p(*[W.data_ptr() for W in Wbits])
+    sp = arr_p(*[S.data_ptr() for S in scales])
+    yp = arr_p(*[o.data_ptr() for o in outs])
+    npv = (ctypes.c_int * count)(*Ns)
+    with torch.cuda.device(x.device):
+        _check("bin1_gemv_group", lib().bin1_gemv_group(x.data_ptr(), count, wp, sp, yp, npv, M, K,
+                                                         _stream(x)))
+    return list(outs)
 
 
 def gemm_prefill(x: torch.Tensor, Wbits: torch.Tensor, scales: torch.Tensor, out: Optional[torch.Tensor] = None):

@@ -64,8 +64,8 @@ int launched(hipError_t e, const char *what)
     return ok();
 }
 
-// Shared validation of the (x, Wbits, scales, y, M, K, N) products.
-int check_product(const void *x, const void *W, const void *S, const void *y, int M, int K, int N)
+// Shared validation of the (x, Wbits, scales, y, M, K, N) products: host-side checks first.
+int check_product_host(const void *x, const void *W, const void *S, const void *y, int M, int K, int N)
 {
     if (!x || !W || !S || !y) return fail(BIN1_ERR_NULL, "x, Wbits, scales and y must be non-NULL");
     if (M < 1 || N < 1 || K < 128 || K % 128 != 0)
@@ -76,11 +76,22 @@ int check_product(const void *x, const void *W, const void *S, const void *y, in
                  yb = (size_t)M * N * 2;
     if (overlap(y, yb, x, xb) || overlap(y, yb, W, wb) || overlap(y, yb, S, sb))
         return fail(BIN1_ERR_ALIAS, "y overlaps an input");
+    return BIN1_OK;
+}
+
+int check_product_device(const void *x, const void *W, const void *S, const void *y)
+{
     int st;
     if ((st = check_device(x, "x")) || (st = check_device(W, "Wbits")) ||
         (st = check_device(S, "scales")) || (st = check_device(y, "y")))
         return st;
     return BIN1_OK;
+}
+
+int check_product(const void *x, const void *W, const void *S, const void *y, int M, int K, int N)
+{
+    int st = check_product_host(x, W, S, y, M, K, N);
+    return st ? st : check_product_device(x, W, S, y);
 }
 
 }  // namespace
@@ -115,6 +126,54 @@ int bin1_gemv(const void *x, const uint32_t *Wbits, const void *scales, void *y,
                                       static_cast<uint16_t *>(y), M, K, N,
                                       static_cast<hipStream_t>(stream)),
                     "bin1_gemv");
+}
+
+int bin1_gemv_group(const void *x, int count, const uint32_t *const *Wbits,
+                    const void *const *scales, void *const *y, const int *N, int M, int K,
+                    void *stream)
+{
+    if (count < 1 || count > bin1::kMaxMats)
+        return fail(BIN1_ERR_SHAPE, "count must be 1..%d (got %d)", bin1::kMaxMats, count);
+    if (!Wbits || !scales || !y || !N) return fail(BIN1_ERR_NULL, "pointer arrays must be non-NULL");
+    for (int i = 0; i < count; ++i) {
+        int st = check_product_host(x, Wbits[i], scales[i], y[i], M, K, N[i]);
+        if (st) return st;
+        for (int j = 0; j < count; ++j) {
+            if (j == i) continue;
+            const size_t yb = (size_t)M * N[i] * 2;
+            if (overlap(y[i], yb, y[j], (size_t)M * N[j] * 2) ||
+                overlap(y[i], yb, Wbits[j], (size_t)N[j] * (K / 8)) ||
+                overlap(y[i], yb, scales[j], (size_t)N[j] * (K / 128) * 2))
+                return fail(BIN1_ERR_ALIAS, "y[%d] overlaps an input or output of matrix %d", i, j);
+        }
+    }
+    for (int i = 0; i < count; ++i) {
+        int st = check_product_device(x, Wbits[i], scales[i], y[i]);
+        if (st) return st;
+    }
+    const hipStream_t st = static_cast<hipStream_t>(stream);
+    if (M == 1 && K <= bin1::mx_max_k()) {
+        bin1::MxSet set{};
+        int tiles = 0;
+        for (int i = 0; i < count; ++i) {
+            set.W[i] = Wbits[i];
+            set.S[i] = static_cast<const uint16_t *>(scales[i]);
+            set.y[i] = static_cast<uint16_t *>(y[i]);
+            set.N[i] = N[i];
+            tiles += (N[i] + 15) / 16;
+            set.tile_end[i] = tiles;
+        }
+        set.count = count;
+        return launched(bin1::launch_gemv_mx(static_cast<const uint16_t *>(x), set, K, st),
+                        "bin1_gemv_group");
+    }
+    for (int i = 0; i < count; ++i) {
+        hipError_t e = bin1::launch_gemv(static_cast<const uint16_t *>(x), Wbits[i],
+                                         static_cast<const uint16_t *>(scales[i]),
+                                         static_cast<uint16_t *>(y[i]), M, K, N[i], st);
+        if (e != hipSuccess) return launched(e, "bin1_gemv_group");
+    }
+    return ok();
 }
 
 int bin1_gemm_prefill(const void *x, const uint32_t *Wbits, const void *scales, void *y, int M,

@@ -63,6 +63,13 @@ hipError_t launch_gemv(const uint16_t *x, const uint32_t *W, const uint16_t *S, 
                        int M, int K, int N, hipStream_t st)
 {
     if (M > 16) return launch_prefill(x, W, S, y, M, K, N, st);
+    if (M == 1 && K <= mx_max_k()) {
+        MxSet set{};
+        set.W[0] = W; set.S[0] = S; set.y[0] = y; set.N[0] = N;
+        set.tile_end[0] = (N + 15) / 16;
+        set.count = 1;
+        return launch_gemv_mx(x, set, K, st);
+    }
     dim3 grid((N + 3) / 4), block(256);
     if (M == 1)
         hipLaunchKernelGGL(gemv_select_kernel<1>, grid, block, 0, st, x, W, S, y, M, K, N);

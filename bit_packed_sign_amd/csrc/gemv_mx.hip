@@ -1,0 +1,392 @@
+// gemv_mx.hip -- batch-1 decode GEMV on the gfx950 block-scaled matrix cores.
+//
+// What is computed: y[n] = sum_k s[n][k/128] * w(n,k) * x[k], w = +-1 from one bit each,
+// one fp16 scale per 128 weights ["Bonsai 27B" page, section "Binary weight format",
+// eq. b_eff], decoded inside the product with fp32 accumulation ["Bonsai 27B" page,
+// section "Low-bit kernels for hybrid attention"]; multiply-free +-1 weights ["PrismML
+// Bonsai -- 1.15GB ..." page, section "What 1-bit is"].
+//
+// How (MI355X-specific design):
+//  * The decode GEMV is HBM-bound, so the budget is ~0.7 VALU op per weight at 8 TB/s.
+//    Plain sign expansion into fp16 pairs costs ~1 op per weight.  Instead each packed
+//    word becomes 32 fp4 (e2m1) values +-1 with one shift and one and-or per 8 weights
+//    (the bit goes straight into the nibble's sign position), and the block-scaled MFMA
+//    v_mfma_scale_f32_16x16x128_f8f6f4 does the 4096 +-x adds per instruction.
+//  * The MFMA's other operand must be fp8, so each 32-element block of x is split into
+//    four e4m3 limbs x = 2^(e-7) (L0 + L1/16 + L2/256 + L3/4096) with e the block's max
+//    exponent; the limb exponents go into the MFMA's per-32-element E8M0 scales.  Four
+//    limbs carry >= 16 significant bits, more than fp16's 11, so for normal-range x the
+//    split is exact.  The limbs are built once per workgroup into LDS.
+//  * One 16x16x128 MFMA covers 16 rows x 128 weights: lane (n, g) supplies word t of its
+//    row's group g, and the 16 A rows are (group G, limb r) with A zero outside group G,
+//    so C[4G+r][n] is the unscaled limb-r partial of group G -- exactly what lane (n, G)
+//    holds afterwards.  The fp16 group scale is then applied with one FMA per group.
+//  * Weights are streamed with nontemporal buffer loads, several row tiles ahead per wave.
+//    A lane owns two adjacent scale groups (32 contiguous bytes of its row and one dword of
+//    scales), so each wave reads whole 128-byte lines; the 4 waves of a workgroup split K
+//    in 1024-weight "pairs" (8 groups) and combine their partial rows in LDS.
+//  * Segment sigma (two per pair p, h = sigma % 2) is what one chain of four MFMAs covers:
+//    MFMA K-block G of segment sigma is scale group gamma = 8p + 2G + h.
+#include "common.hpp"
+#include "kernels.hpp"
+
+namespace bin1 {
+
+namespace {
+
+typedef unsigned u4v __attribute__((ext_vector_type(4)));
+
+// Raw buffer resources: loads past num_records return 0 and stores past it are dropped,
+// so ragged tiles and dead ring slots need no branches (branch-free code also lets the
+// compiler count outstanding loads exactly, which keeps the prefetch ring full).
+constexpr int kRsrcFlags = 0x00020000;
+constexpr unsigned kOob = 0x80000000u;          // an offset past every resource
+constexpr int kNT = 2;                           // cache policy: nontemporal (streamed once)
+
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t rsrc(const void *p, unsigned bytes)
+{
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(p), (short)0, (int)bytes, kRsrcFlags);
+}
+
+constexpr int kBlk = 528;          // LDS bytes per (segment, word): 16 rows x 32 B + 16 zero bytes
+constexpr int kZero = 512;         // offset of the zero bytes inside a block
+
+// fp4 (e2m1) expansion of one word: nibble q of register v = 0x2 | bit(4q+v) << 3,
+// i.e. -1.0 for a set bit and +1.0 for a clear one (the sign is undone by the caller).
+__device__ __forceinline__ int8v unpack_fp4(uint32_t w)
+{
+    int8v b;
+    b[0] = (int)(((w << 3) & 0x88888888u) | 0x22222222u);
+    b[1] = (int)(((w << 2) & 0x88888888u) | 0x22222222u);
+    b[2] = (int)(((w << 1) & 0x88888888u) | 0x22222222u);
+    b[3] = (int)((w & 0x88888888u) | 0x22222222u);
+    b[4] = b[5] = b[6] = b[7] = 0;
+    return b;
+}
+
+// A operand of (segment, word t) for this lane, from the limb block in LDS.
+__device__ __forceinline__ int8v load_a(const uint8_t *blk, int lo, int hi)
+{
+    const u4v a0 = *reinterpret_cast<const u4v *>(blk + lo);
+    const u4v a1 = *reinterpret_cast<const u4v *>(blk + hi);
+    int8v a;
+    a[0] = a0.x; a[1] = a0.y; a[2] = a0.z; a[3] = a0.w;
+    a[4] = a1.x; a[5] = a1.y; a[6] = a1.z; a[7] = a1.w;
+    return a;
+}
+
+template <int T>
+__device__ __forceinline__ float4v mma(const int8v &a, uint32_t w, int scA, float4v c)
+{
+    return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a, unpack_fp4(w), c, 0, 4, T, scA, 0, 127);
+}
+
+// x (fp16, K values) -> fp8 limbs in the A-operand order, plus E8M0 exponents, in LDS.
+// Block beta = k/32 holds the 32 activations of packed word beta (word t = beta % 4 of group
+// gamma = beta / 4); within the block, element j pairs with weight bit pi(j) = 4*(j%8) + j/8
+// (the order unpack_fp4 produces).  Task tau covers activations [16 tau, 16 tau + 16); thread
+// t takes tasks t, t+256, ...  The x loads are issued before the weight prefetch (loads retire
+// in order, so waiting on them later does not drain the prefetch).
+template <int XT>
+struct XLoad {
+    u4v v[XT][2];
+};
+
+__device__ __forceinline__ int nseg_of(int K) { return 2 * ((K + 1023) >> 10); }
+
+template <int XT>
+__device__ __forceinline__ void limbs_init(int K, uint8_t *lds, const uint16_t *__restrict__ x, XLoad<XT> &xl)
+{
+    const int nseg = nseg_of(K);
+    uint32_t *sc = reinterpret_cast<uint32_t *>(lds + nseg * 4 * kBlk);
+    const int tid = threadIdx.x;
+    u4v *a16 = reinterpret_cast<u4v *>(lds);
+    for (int i = tid; i < nseg * 4 * kBlk / 16; i += 256) a16[i] = u4v{0, 0, 0, 0};
+    for (int i = tid; i < nseg * 16; i += 256) sc[i] = 0x7F7F7F7Fu;
+    const __amdgpu_buffer_rsrc_t rx = rsrc(x, (unsigned)K * 2u);
+#pragma unroll
+    for (int q = 0; q < XT; ++q) {
+        const unsigned off = 32u * (unsigned)(tid + 256 * q);    // past K: zeros, no traffic
+        xl.v[q][0] = __builtin_amdgcn_raw_buffer_load_b128(rx, off, 0, 0);
+        xl.v[q][1] = __builtin_amdgcn_raw_buffer_load_b128(rx, off + 16u, 0, 0);
+    }
+}
+
+template <int XT>
+__device__ __forceinline__ void limbs_build(int K, uint8_t *lds, const XLoad<XT> &xl)
+{
+    const int nseg = nseg_of(K);
+    uint32_t *sc = reinterpret_cast<uint32_t *>(lds + nseg * 4 * kBlk);
+    const int tid = threadIdx.x;
+    const int ntask = K >> 4;                       // even, so a 32-block's two tasks pair up
+#pragma unroll
+    for (int q = 0; q < XT; ++q) {
+        const int tau = tid + 256 * q;
+        if (256 * q >= ntask) break;                  // uniform: no task of this round
+        const u4v p0 = xl.v[q][0], p1 = xl.v[q][1];
+        const uint32_t hw[8] = {p0.x, p0.y, p0.z, p0.w, p1.x, p1.y, p1.z, p1.w};
+        float u[16];
+        float mx = 0.f;
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+            u[i] = h2f((uint16_t)(hw[i >> 1] >> (16 * (i & 1))));
+            mx = fmaxf(mx, fabsf(u[i]));
+        }
+        mx = fmaxf(mx, __shfl_xor(mx, 1, kWave));        // the other half of the 32-block
+        if (tau < ntask) {
+            const int e0 = mx > 0.f ? __builtin_amdgcn_frexp_expf(mx) - 1 : 0;   // 2^e0 <= mx
+            const float mul = __builtin_ldexpf(1.0f, 7 - e0);
+#pragma unroll
+            for (int i = 0; i < 16; ++i) u[i] *= mul;    // |u| < 256, exact
+            const int beta = tau >> 1, h = tau & 1;
+            const int gamma = beta >> 2, t = beta & 3;
+            const int sigma = 2 * (gamma >> 3) + (gamma & 1), G = (gamma & 7) >> 1;
+            uint8_t *blk = lds + (sigma * 4 + t) * kBlk;
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                int d[4];
+#pragma unroll
+                for (int c = 0; c < 4; ++c) {
+                    int v = __builtin_amdgcn_cvt_pk_fp8_f32(u[c], u[4 + c], 0, false);
+                    d[c] = __builtin_amdgcn_cvt_pk_fp8_f32(u[8 + c], u[12 + c], v, true);
+                    *reinterpret_cast<int *>(blk + (4 * G + r) * 32 + (2 * c + h) * 4) = d[c];
+                }
+                if (h == 0)
+                    reinterpret_cast<uint8_t *>(sc)[(sigma * 16 + 4 * G + r) * 4 + t] =
+                        (uint8_t)(127 + e0 - 7 - 4 * r);
+                if (r < 3) {
+#pragma unroll
+                    for (int c = 0; c < 4; ++c) {
+                        u[c] = (u[c] - __builtin_amdgcn_cvt_f32_fp8(d[c], 0)) * 16.f;
+                        u[4 + c] = (u[4 + c] - __builtin_amdgcn_cvt_f32_fp8(d[c], 1)) * 16.f;
+                        u[8 + c] = (u[8 + c] - __builtin_amdgcn_cvt_f32_fp8(d[c], 2)) * 16.f;
+                        u[12 + c] = (u[12 + c] - __builtin_amdgcn_cvt_f32_fp8(d[c], 3)) * 16.f;
+                    }
+                }
+            }
+        }
+    }
+}
+
+// Locate tile `tile` (16*R rows) of the matrix set: matrix index and first row.
+template <int R>
+__device__ __forceinline__ void locate(const MxSet &set, int tile, int &mi, int &row0)
+{
+    mi = 0;
+#pragma unroll
+    for (int i = 0; i < kMaxMats - 1; ++i)
+        if (i + 1 < set.count && tile >= set.tile_end[i]) mi = i + 1;
+    row0 = (tile - (mi ? set.tile_end[mi - 1] : 0)) * 16 * R;
+}
+
+// One ring slot: for each 16-row block r and each of the wave's pairs, 32 bytes of weights
+// (groups gamma0, gamma0+1) and their two scales (one dword; or two halves when K/128 is odd,
+// where a dword load could straddle rows misaligned).
+template <int SP, int R>
+struct Slot {
+    u4v w[R][SP][2];
+    uint32_t s[R][SP];
+    uint16_t s1[R][SP];
+};
+
+// Sum over the four lanes n, n+16, n+32, n+48 (every lane gets its column's total).
+__device__ __forceinline__ float sum_groups(float v)
+{
+    const int iv = __builtin_bit_cast(int, v);
+    const auto a = __builtin_amdgcn_permlane32_swap(iv, iv, false, false);
+    v = __builtin_bit_cast(float, (int)a[0]) + __builtin_bit_cast(float, (int)a[1]);
+    const int iw = __builtin_bit_cast(int, v);
+    const auto b = __builtin_amdgcn_permlane16_swap(iw, iw, false, false);
+    return __builtin_bit_cast(float, (int)b[0]) + __builtin_bit_cast(float, (int)b[1]);
+}
+
+template <int SP, int P, int R, bool ODD>
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 4)))
+void gemv_mx_kernel(const uint16_t *__restrict__ x, MxSet set, int K, int ntiles)
+{
+    extern __shared__ __attribute__((aligned(16))) uint8_t lds[];
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);      // wave-uniform
+    const int n = lane & 15, g = lane >> 4;
+    const int npair = (K + 1023) >> 10, nseg = 2 * npair;
+    const int wpr = K >> 5, spr = K >> 7;
+    const int my_tiles = blockIdx.x < ntiles ? (ntiles - 1 - blockIdx.x) / gridDim.x + 1 : 0;
+
+    Slot<SP, R> ring[P];
+
+    // Ring slot fill for the workgroup's it-th tile.  Slots past the last tile, rows past N
+    // and groups past K get out-of-range offsets: zero data and zero scales, no traffic.
+    auto issue = [&](int it, Slot<SP, R> &sl) {
+        const bool live = it < my_tiles;
+        int mi, row0;
+        locate<R>(set, live ? blockIdx.x + it * gridDim.x : 0, mi, row0);
+        const int N = set.N[mi];
+        const __amdgpu_buffer_rsrc_t rW = rsrc(set.W[mi], (unsigned)N * (unsigned)wpr * 4u);
+        const __amdgpu_buffer_rsrc_t rS = rsrc(set.S[mi], (unsigned)N * (unsigned)spr * 2u);
+#pragma unroll
+        for (int r = 0; r < R; ++r) {
+            const int row = row0 + 16 * r + n;
+            const bool rok = live && row < N;
+#pragma unroll
+            for (int q = 0; q < SP; ++q) {
+                const int gam = 8 * (wave + 4 * q) + 2 * g;     // this lane's first group
+                const bool ok0 = rok && gam < spr, ok1 = rok && gam + 1 < spr;
+                const unsigned ow = ((unsigned)row * wpr + 4u * gam) * 4u;
+                const unsigned os = ((unsigned)row * spr + gam) * 2u;
+                sl.w[r][q][0] = __builtin_amdgcn_raw_buffer_load_b128(rW, ok0 ? ow : kOob, 0, kNT);
+                sl.w[r][q][1] = __builtin_amdgcn_raw_buffer_load_b128(rW, ok1 ? ow + 16u : kOob, 0, kNT);
+                if (ODD) {
+                    sl.s[r][q] = __builtin_amdgcn_raw_buffer_load_b16(rS, ok0 ? os : kOob, 0, 0);
+                    sl.s1[r][q] = __builtin_amdgcn_raw_buffer_load_b16(rS, ok1 ? os + 2u : kOob, 0, 0);
+                } else {
+                    sl.s[r][q] = __builtin_amdgcn_raw_buffer_load_b32(rS, ok0 ? os : kOob, 0, 0);
+                }
+            }
+        }
+    };
+
+    constexpr int XT = SP;                           // activation tasks per thread (K <= 4096*SP)
+    XLoad<XT> xl;
+    limbs_init<XT>(K, lds, x, xl);
+#pragma unroll
+    for (int p = 0; p < P; ++p) issue(p, ring[p]);
+    __syncthreads();                                  // zero-filled limb area visible
+    limbs_build<XT>(K, lds, xl);
+    __syncthreads();                                  // limbs visible
+
+    const uint32_t *sc = reinterpret_cast<const uint32_t *>(lds + nseg * 4 * kBlk);
+    float *red = reinterpret_cast<float *>(lds + nseg * (4 * kBlk + 64));   // merge table, after the limbs
+    const int m = lane & 15, G = m >> 2;
+    const int lo = (G == (g >> 1)) ? m * 32 + 16 * (g & 1) : kZero;
+    const int hi = (G == 2 + (g >> 1)) ? m * 32 + 16 * (g & 1) : kZero;
+
+    // The wave's A operands (its K-slice of the limbs) stay in registers for the whole
+    // kernel: 8 x 8 registers per pair, read from LDS once.
+    int8v A[SP][2][4];
+    int scA[SP][2];
+#pragma unroll
+    for (int q = 0; q < SP; ++q)
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+            const int sigma = 2 * (wave + 4 * q) + h;
+            const bool v = wave + 4 * q < npair;
+            const uint8_t *blk = lds + (v ? sigma : 0) * 4 * kBlk;
+#pragma unroll
+            for (int t = 0; t < 4; ++t) A[q][h][t] = load_a(blk + t * kBlk, lo, hi);
+            scA[q][h] = (int)sc[(v ? sigma : 0) * 16 + m];
+        }
+
+    // Main loop: no cross-wave synchronisation.  Each wave streams its K-slice of every tile
+    // of this workgroup and parks its partial row sums in LDS; one barrier at the end merges
+    // the four slices and writes y with coalesced stores.
+    for (int it0 = 0; it0 < my_tiles; it0 += P) {
+#pragma unroll
+        for (int p = 0; p < P; ++p) {
+            const int it = it0 + p;
+            if (it >= my_tiles) goto done;            // uniform; the slots left hold dead loads
+            float acc[R];
+#pragma unroll
+            for (int r = 0; r < R; ++r) acc[r] = 0.f;
+#pragma unroll
+            for (int q = 0; q < SP; ++q) {
+                const int pr = wave + 4 * q;
+                if (pr < npair) {                     // wave-uniform
+                    const int gam = 8 * pr + 2 * g;
+#pragma unroll
+                    for (int r = 0; r < R; ++r) {
+                        const uint32_t sv = ring[p].s[r][q];
+                        const float s0 = h2f((uint16_t)(sv & 0xFFFFu));
+                        const float s1 = ODD ? h2f(ring[p].s1[r][q])
+                                             : (gam + 1 < spr ? h2f((uint16_t)(sv >> 16)) : 0.f);
+#pragma unroll
+                        for (int h = 0; h < 2; ++h) {
+                            const u4v w = ring[p].w[r][q][h];
+                            float4v c = {0.f, 0.f, 0.f, 0.f};
+                            c = mma<0>(A[q][h][0], w.x, scA[q][h], c);
+                            c = mma<1>(A[q][h][1], w.y, scA[q][h], c);
+                            c = mma<2>(A[q][h][2], w.z, scA[q][h], c);
+                            c = mma<3>(A[q][h][3], w.w, scA[q][h], c);
+                            // B held -w, so the group's partial is -(c0+c1+c2+c3)
+                            acc[r] = fmaf(-(h ? s1 : s0), (c[0] + c[1]) + (c[2] + c[3]), acc[r]);
+                        }
+                    }
+                }
+            }
+            issue(it + P, ring[p]);
+            float *rb = red + it * (64 * R);          // [tile][16R rows][4 waves]
+#pragma unroll
+            for (int r = 0; r < R; ++r) {
+                const float v = sum_groups(acc[r]);
+                if (lane < 16) rb[(16 * r + lane) * 4 + wave] = v;
+            }
+        }
+    }
+done:
+    __syncthreads();
+    // Merge: thread t finishes rows t, t+256, ... of the workgroup's tiles in order.
+    for (int e = tid; e < my_tiles * 16 * R; e += 256) {
+        const int it = e / (16 * R), j = e - it * (16 * R);
+        int mi, row0;
+        locate<R>(set, blockIdx.x + it * gridDim.x, mi, row0);
+        const int row = row0 + j;
+        const float4v pr4 = *reinterpret_cast<const float4v *>(red + e * 4);
+        const float tot = (pr4[0] + pr4[1]) + (pr4[2] + pr4[3]);
+        if (row < set.N[mi]) set.y[mi][row] = f2h_rne(tot);
+    }
+}
+
+constexpr int kMaxPairs = 20;                         // K <= 20480 (A operands fit in registers)
+constexpr int kMaxTileRows = 2048;                     // rows per workgroup held in the merge table
+// LDS: limb blocks and exponents for K, then the merge table [tile][16R rows][4 waves] fp32.
+constexpr size_t shm_bytes(int K, int rows_per_wg)
+{
+    return (size_t)(2 * ((K + 1023) >> 10)) * (4 * kBlk + 64) + (size_t)rows_per_wg * 4 * 4;
+}
+
+template <int SP, int P, int R, bool ODD>
+hipError_t launch_mx(const uint16_t *x, const MxSet &set0, int K, hipStream_t st)
+{
+    static const hipError_t attr = hipFuncSetAttribute(
+        reinterpret_cast<const void *>(&gemv_mx_kernel<SP, P, R, ODD>),
+        hipFuncAttributeMaxDynamicSharedMemorySize, (int)shm_bytes(kMaxPairs * 1024, kMaxTileRows));
+    if (attr != hipSuccess) return attr;
+    MxSet set = set0;
+    int tiles = 0;
+    for (int i = 0; i < set.count; ++i) {
+        tiles += (set.N[i] + 16 * R - 1) / (16 * R);
+        set.tile_end[i] = tiles;
+    }
+    // Resident workgroups per CU follow the register budget (A operands dominate it); the
+    // grid grows past that only when a workgroup's rows would overflow the merge table.
+    const int cap = SP <= 2 ? 2 * 256 : 256;
+    const int need = (tiles + kMaxTileRows / (16 * R) - 1) / (kMaxTileRows / (16 * R));
+    const int grid = tiles < cap ? tiles : (need > cap ? need : cap);
+    const int rows_per_wg = (tiles + grid - 1) / grid * 16 * R;
+    hipLaunchKernelGGL((gemv_mx_kernel<SP, P, R, ODD>), dim3(grid), dim3(256), shm_bytes(K, rows_per_wg),
+                       st, x, set, K, tiles);
+    return hipGetLastError();
+}
+
+template <bool ODD>
+hipError_t dispatch_mx(const uint16_t *x, const MxSet &set, int K, hipStream_t st)
+{
+    const int SP = (((K + 1023) >> 10) + 3) / 4;        // pairs per wave
+    switch (SP) {
+    case 1: return launch_mx<1, 3, 2, ODD>(x, set, K, st);
+    case 2: return launch_mx<2, 2, 2, ODD>(x, set, K, st);
+    case 3: return launch_mx<3, 2, 2, ODD>(x, set, K, st);
+    case 4: return launch_mx<4, 1, 2, ODD>(x, set, K, st);
+    default: return launch_mx<5, 1, 2, ODD>(x, set, K, st);
+    }
+}
+
+}  // namespace
+
+int mx_max_k() { return kMaxPairs * 1024; }
+
+hipError_t launch_gemv_mx(const uint16_t *x, const MxSet &set, int K, hipStream_t st)
+{
+    return ((K >> 7) & 1) ? dispatch_mx<true>(x, set, K, st) : dispatch_mx<false>(x, set, K, st);
+}
+
+}  // namespace bin1

@@ -7,6 +7,22 @@
 
 namespace bin1 {
 
+// Up to kMaxMats products that read the same activation vector (e.g. q/k/v or gate/up),
+// decoded in one launch.  tile_end[] is filled in by the launcher (cumulative row tiles).
+constexpr int kMaxMats = 4;
+struct MxSet {
+    const uint32_t *W[kMaxMats];
+    const uint16_t *S[kMaxMats];
+    uint16_t *y[kMaxMats];
+    int N[kMaxMats];
+    int tile_end[kMaxMats];
+    int count;
+};
+
+// Largest K the block-scaled decode kernel takes (longer rows use the select kernel).
+int mx_max_k();
+hipError_t launch_gemv_mx(const uint16_t *x, const MxSet &set, int K, hipStream_t st);
+
 hipError_t launch_gemv(const uint16_t *x, const uint32_t *W, const uint16_t *S, uint16_t *y,
                        int M, int K, int N, hipStream_t st);
 hipError_t launch_prefill(const uint16_t *x, const uint32_t *W, const uint16_t *S, uint16_t *y,

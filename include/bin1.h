@@ -75,6 +75,16 @@ typedef enum bin1_status {
 int bin1_gemv(const void *x, const uint32_t *Wbits, const void *scales, void *y,
               int M, int K, int N, void *stream);
 
+/* Same-input fusion: `count` (1..4) products that read the same activations x [M][K]
+ * (such as the q/k/v or gate/up projections of one layer), enqueued as one launch when
+ * M == 1.  Wbits, scales, y and N are HOST arrays of `count` entries; entry i describes
+ * matrix i exactly as in bin1_gemv (Wbits[i] [N[i]][K/32], scales[i] [N[i]][K/128],
+ * y[i] [M][N[i]]).  Every y[i] must be disjoint from every input and from the other
+ * outputs.  Results equal `count` separate bin1_gemv calls. */
+int bin1_gemv_group(const void *x, int count, const uint32_t *const *Wbits,
+                    const void *const *scales, void *const *y, const int *N,
+                    int M, int K, void *stream);
+
 /* Prefill product, same arguments and result as bin1_gemv; tuned for M >= 256 (the
  * pages note that prompt processing is compute-bound: ["Bonsai 27B", section "Low-bit
  * kernels for hybrid attention"]).  Bit tiles are unpacked into LDS as fp16 +-scale

@@ -27,7 +27,7 @@ def L():
 
 def test_header_declares_the_entry_points():
     names = _declared()
-    for fn in ["bin1_gemv", "bin1_gemm_prefill", "bin1_gemv_pm1", "bin1_xor_patch_apply",
+    for fn in ["bin1_gemv", "bin1_gemv_group", "bin1_gemm_prefill", "bin1_gemv_pm1", "bin1_xor_patch_apply",
                "bin1_xor_patch_apply_multi", "bin1_status_string", "bin1_last_error",
                "bin1_abi_version"]:
         assert fn in names
@@ -67,6 +67,19 @@ def test_product_validation(L, fn):
     # y overlapping x (x occupies M*K*2 bytes from FAKE)
     assert f(FAKE, FAKE * 8, FAKE * 9, FAKE + 128, 1, 128, 1, None) == -4
     assert b"overlaps" in L.bin1_last_error()
+
+
+def test_group_validation(L):
+    arr = (ctypes.c_void_p * 2)
+    n = (ctypes.c_int * 2)(8, 8)
+    assert L.bin1_gemv_group(FAKE, 0, None, None, None, None, 1, 128, None) == -2
+    assert L.bin1_gemv_group(FAKE, 5, None, None, None, None, 1, 128, None) == -2
+    assert L.bin1_gemv_group(FAKE, 2, None, None, None, n, 1, 128, None) == -1
+    # y[0] overlaps W[1]
+    W = arr(FAKE * 4, FAKE * 8)
+    S = arr(FAKE * 12, FAKE * 16)
+    Y = arr(FAKE * 8 + 16, FAKE * 20)
+    assert L.bin1_gemv_group(FAKE, 2, W, S, Y, n, 1, 128, None) == -4
 
 
 def test_pm1_and_patch_validation(L):
