@@ -1,15 +1,23 @@
 """Benchmark of the 1-bit sign GEMV decode step on one MI355X.
 
-    python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline] [--extra]
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline] [--no-extra]
+                    [--only NAME]
 
-A step is one batch-1 decode pass of the 8B-class model's GEMVs: 36 layers of
+Headline step: one batch-1 decode pass of the 8B-class model's GEMVs -- 36 layers of
 q 4096x4096, k/v 4096x1024, o 4096x4096, gate/up 4096x12288, down 12288x4096, then
-lm_head 4096x151936 -- 253 products in 145 dependent stages, every stage reading its own
-fp16 activation vector (norms/attention omitted), all weights and activations resident
-in HBM.  The step is captured once into a HIP graph and replayed.
+lm_head 4096x151936: 253 products in 145 dependent stages (q/k/v and gate/up each share
+one activation vector and run as one launch), every stage reading its own fp16 activation
+vector (norms/attention omitted), all weights and activations resident in HBM.  The step
+is captured once into a HIP graph and replayed; K replays are timed between HIP events.
 
 Metric: weight-GB/s = bytes of packed bits + fp16 scales per step (1,064,263,680 B)
-divided by the step time; implied tokens/s = 1 / step time.  One JSON line on stdout.
+divided by the step time; implied tokens/s = 1 / step time.
+
+The other workloads run after the headline and are reported under "extra": one
+4096x4096 GEMV (cache-cold over a >1 GiB pool of copies, and cache-hot) with a 64-row
+patch; the 8B MLP at batch 16; the prefill contraction M=2048, K=4096, N=12288; the 27B
+decode step with a 2000-row multi-matrix patch; and the +-1 popcount product.
+One JSON line on stdout; progress on stderr.
 """
 from __future__ import annotations
 
@@ -25,6 +33,7 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, published
+FP16_MFMA_PEAK_TFLOPS = 2500.0 # MI355X dense fp16/bf16 matrix peak, published
 
 
 def parse():
@@ -33,8 +42,10 @@ def parse():
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--cpu-layers", type=int, default=6,
-                    help="decode layers of the 8B step the oracle runs for the CPU baseline")
+    ap.add_argument("--no-extra", action="store_true")
+    ap.add_argument("--only", default=None,
+                    help="run one workload alone (for profiling): step8b, lmhead, single, mlp16, "
+                         "prefill, step27b, pm1, copy")
     return ap.parse_args()
 
 
@@ -42,16 +53,34 @@ def log(msg):
     print(msg, file=sys.stderr, flush=True)
 
 
-class DecodeStep:
-    """Device-resident weights/activations of a workload and a graph of one step."""
+def events():
+    import torch
+    return torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+
+
+def time_fn(fn, reps, warm=2):
+    """Average ms per call of fn() over `reps` calls, HIP events on the current stream."""
+    import torch
+    for _ in range(warm):
+        fn()
+    torch.cuda.synchronize()
+    e0, e1 = events()
+    e0.record()
+    for _ in range(reps):
+        fn()
+    e1.record()
+    torch.cuda.synchronize()
+    return e0.elapsed_time(e1) / reps
+
+
+class Step:
+    """Device-resident weights/activations of a staged workload and a graph of one pass."""
 
     def __init__(self, wl, device):
         import torch
         from bit_packed_sign_amd import synth
         self.wl = wl
-        self.dev = device
-        # one entry per stage: (x, [W...], [S...], [y...], bytes)
-        self.stages = []
+        self.stages = []                      # (x, [W...], [S...], [y...], bytes)
         t0 = time.time()
         gi = 0
         for s, stage in enumerate(wl.stages):
@@ -65,8 +94,8 @@ class DecodeStep:
                 gi += 1
             self.stages.append((xs, Ws, Ss, ys, sum(g.weight_bytes for g in stage.gemvs)))
         torch.cuda.synchronize()
-        log(f"[bench] {wl.name}: {gi} GEMVs in {len(self.stages)} stages, {wl.weight_bytes / 1e9:.3f} GB resident "
-            f"(generated in {time.time() - t0:.1f} s)")
+        log(f"[bench] {wl.name}: {gi} GEMVs in {len(self.stages)} stages, {wl.weight_bytes / 1e9:.3f} GB "
+            f"resident (generated in {time.time() - t0:.1f} s)")
         self.graph = None
 
     @staticmethod
@@ -75,7 +104,7 @@ class DecodeStep:
         x, Ws, Ss, ys, _ = st
         if len(Ws) == 1:
             b1.gemv(x, Ws[0], Ss[0], out=ys[0])
-        else:                                     # q/k/v or gate/up: same-input fusion
+        else:                                 # q/k/v or gate/up: same-input fusion
             b1.gemv_group(x, Ws, Ss, outs=ys)
 
     def run_eager(self):
@@ -87,7 +116,7 @@ class DecodeStep:
         s = torch.cuda.Stream()
         s.wait_stream(torch.cuda.current_stream())
         with torch.cuda.stream(s):
-            self.run_eager()                      # warm the path outside capture
+            self.run_eager()                  # warm the path outside capture
         torch.cuda.current_stream().wait_stream(s)
         torch.cuda.synchronize()
         self.graph = torch.cuda.CUDAGraph()
@@ -95,16 +124,26 @@ class DecodeStep:
             self.run_eager()
         torch.cuda.synchronize()
 
-    def replay(self):
-        self.graph.replay()
+    def timed(self, steps, warmup):
+        import torch
+        for _ in range(warmup):
+            self.graph.replay()
+        torch.cuda.synchronize()
+        e0, e1 = events()
+        e0.record()
+        for _ in range(steps):
+            self.graph.replay()
+        e1.record()
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) / steps
 
     def per_launch_ms(self, reps=3):
-        """Per-launch kernel durations (one launch per stage) with HIP events recorded on the
+        """Per-launch kernel durations (one launch per stage) from HIP events recorded on the
         stream the kernels are launched on (eager launches)."""
         import torch
         st = torch.cuda.current_stream()
         n = len(self.stages)
-        ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(n)]
+        ev = [events() for _ in range(n)]
         tot = np.zeros(n)
         for _ in range(reps):
             for i, stage in enumerate(self.stages):
@@ -116,15 +155,13 @@ class DecodeStep:
         return tot / reps
 
 
-def cpu_baseline(wl, layers):
-    """The fp64 oracle on the first `layers` decode layers of the step (all their outputs)."""
+def cpu_baseline(wl):
+    """The fp64 oracle over every output of the whole 8B decode step, on the host cores."""
     from bit_packed_sign_amd import synth
     from oracle import oracle
     oracle.lib()
     gi, nbytes, secs = 0, 0, 0.0
     for s, stage in enumerate(wl.stages):
-        if stage.layer >= layers:
-            break
         x = synth.stage_activations(0, wl, s)
         for g in stage.gemvs:
             bits, scales = synth.gemv_tensors(0, wl, gi)
@@ -133,52 +170,170 @@ def cpu_baseline(wl, layers):
             secs += time.perf_counter() - t0
             nbytes += g.weight_bytes
             gi += 1
-    return {"value": nbytes / secs / 1e9, "unit": "GB/s", "cores": oracle.max_threads(), "kind": "oracle",
-            "sample": f"first {layers} of 36 decode layers of the 8B step ({gi} GEMVs, "
-                      f"{nbytes / 1e9:.3f} GB of weights), every output, fp64; {secs:.1f} s wall"}
+    return {"value": round(nbytes / secs / 1e9, 4), "unit": "GB/s", "cores": oracle.max_threads(),
+            "kind": "oracle",
+            "sample": f"the whole 8B decode step: {gi} GEMVs, {nbytes / 1e9:.3f} GB of weights, every output, "
+                      f"fp64 dequantise-and-dot with OpenMP over rows; {secs:.1f} s wall",
+            "ms_per_step": round(secs * 1e3, 1)}
 
 
+# ----------------------------------------------------------------------------------- extras
+def extra_single(dev):
+    """One 4096x4096 GEMV: cache-cold over a pool of copies larger than the 256 MB cache, and
+    cache-hot; plus the 64-row patch applied and removed."""
+    import torch
+    import bit_packed_sign_amd as b1
+    from bit_packed_sign_amd import synth
+    wl = synth.single_gemv()
+    bits, scales = synth.gemv_tensors(0, wl, 0)
+    x = torch.from_numpy(synth.stage_activations(0, wl, 0)).to(dev)
+    W0 = torch.from_numpy(bits.view(np.int32)).to(dev)
+    S0 = torch.from_numpy(scales).to(dev)
+    g = wl.gemvs[0]
+    copies = int(np.ceil((1 << 30) / g.weight_bytes))
+    Ws = [W0.clone() for _ in range(copies)]
+    Ss = [S0.clone() for _ in range(copies)]
+    y = torch.empty((1, 4096), dtype=torch.float16, device=dev)
+    it = iter(range(10 ** 9))
+
+    def cold():
+        i = next(it) % copies
+        b1.gemv(x, Ws[i], Ss[i], out=y)
+    ms_cold = time_fn(cold, reps=copies)
+    ms_hot = time_fn(lambda: b1.gemv(x, W0, S0, out=y), reps=200)
+    rows = torch.from_numpy(synth.patch_rows_single()).to(dev)
+    ms_patch = time_fn(lambda: b1.xor_patch_apply(W0, rows, check_distinct=False), reps=200)
+    del Ws, Ss
+    return {"workload": "4096x4096 GEMV, M=1", "pool_copies": copies,
+            "us_cold": round(ms_cold * 1e3, 2), "gbs_cold": round(g.weight_bytes / ms_cold / 1e6, 1),
+            "us_hot": round(ms_hot * 1e3, 2), "gbs_hot_cache": round(g.weight_bytes / ms_hot / 1e6, 1),
+            "patch_64_rows_us": round(ms_patch * 1e3, 2),
+            "note": "eager launches back to back: each time includes the launch gap"}
+
+
+def extra_step(wl, dev, steps, label):
+    st = Step(wl, dev)
+    st.capture()
+    ms = st.timed(max(5, steps // 2), 2)
+    out = {"workload": label, "ms_per_step": round(ms, 4),
+           "gbs": round(wl.weight_bytes / ms / 1e6, 1), "tok_s": round(1e3 / ms, 1),
+           "pct_hbm_peak": round(100 * wl.weight_bytes / ms / 1e6 / HBM_PEAK_GBS, 2)}
+    return st, out
+
+
+def extra_patch27b(st, dev):
+    """2000 distinct (layer, projection, row) flips over the 27B MLP matrices, one launch."""
+    import bit_packed_sign_amd as b1
+    import torch
+    from bit_packed_sign_amd import synth
+    mlp = []
+    for l in range(64):                       # stages per layer: q|k|v, o, gate|up, down
+        gu = st.stages[4 * l + 2][1]
+        dn = st.stages[4 * l + 3][1]
+        mlp += [gu[0], gu[1], dn[0]]
+    table = b1.PatchTable(mlp)
+    ent_np = synth.patch_entries_27b()
+    ent = torch.from_numpy(ent_np).to(dev)
+    ms = time_fn(lambda: b1.xor_patch_apply_multi(table, ent, check_distinct=False), reps=200)
+    row_bytes = np.array([m.shape[1] * 4 for m in mlp])[ent_np[:, 0]].sum()
+    return {"patch_2000_rows_us": round(ms * 1e3, 2), "patch_bytes_read_and_written": int(2 * row_bytes)}
+
+
+def extra_prefill(dev):
+    import torch
+    import bit_packed_sign_amd as b1
+    from bit_packed_sign_amd import synth
+    M, K, N = synth.PREFILL_M, synth.PREFILL_K, synth.PREFILL_N
+    r = synth.rng_for(0, synth.WL_PREFILL, 0)
+    x = torch.from_numpy(synth.activations(r, M, K)).to(dev)
+    W = torch.from_numpy(synth.sign_words(r, N, K).view(np.int32)).to(dev)
+    S = torch.from_numpy(synth.group_scales(r, N, K)).to(dev)
+    y = torch.empty((M, N), dtype=torch.float16, device=dev)
+    ms = time_fn(lambda: b1.gemm_prefill(x, W, S, out=y), reps=50)
+    tf = 2.0 * M * K * N / (ms * 1e-3) / 1e12
+    return {"workload": "prefill M=2048 K=4096 N=12288", "us": round(ms * 1e3, 2),
+            "tflops": round(tf, 1), "frac_of_fp16_mfma_peak": round(tf / FP16_MFMA_PEAK_TFLOPS, 4)}
+
+
+def extra_pm1(dev):
+    import torch
+    import bit_packed_sign_amd as b1
+    from bit_packed_sign_amd import synth
+    K, N = 4096, 151936
+    r = synth.rng_for(0, synth.WL_TEST, 424242)
+    A = torch.from_numpy(synth.pm1_words(r, 1, K).view(np.int32)).to(dev)
+    W = torch.from_numpy(synth.sign_words(r, N, K).view(np.int32)).to(dev)
+    y = torch.empty((1, N), dtype=torch.int32, device=dev)
+    ms = time_fn(lambda: b1.gemv_pm1(A, W, out=y), reps=50)
+    return {"workload": "+-1 popcount product K=4096 N=151936 M=1", "us": round(ms * 1e3, 2),
+            "gbs": round(N * K / 8 / ms / 1e6, 1)}
+
+
+# ------------------------------------------------------------------------------------ main
 def main():
     args = parse()
     if args.gpus != 1:
-        print(json.dumps({"error": "this benchmark runs on one GPU only; multi-GPU runs are not part of "
-                                   "this build (see the sharding note in the design document)",
+        print(json.dumps({"error": "this benchmark runs on one GPU only; runs on several GPUs are not "
+                                   "part of this build (the design notes describe how the path shards)",
                           "n_gpus": args.gpus}))
         sys.exit(2)
     import torch
     from bit_packed_sign_amd import synth
     dev = torch.device("cuda:0")
+
+    if args.only:
+        run_only(args, dev)
+        return
+
     wl = synth.decode_8b()
-    step = DecodeStep(wl, dev)
+    step = Step(wl, dev)
     step.capture()
-    for _ in range(args.warmup):
-        step.replay()
-    torch.cuda.synchronize()
-    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    e0.record()
-    for _ in range(args.steps):
-        step.replay()
-    e1.record()
-    torch.cuda.synchronize()
-    ms = e0.elapsed_time(e1) / args.steps
+    ms = step.timed(args.steps, args.warmup)
     wbytes = wl.weight_bytes
     gbs = wbytes / (ms * 1e-3) / 1e9
     log(f"[bench] step {ms * 1e3:.1f} us, {gbs:.0f} GB/s, {1e3 / ms:.0f} tok/s")
 
-    # dominant kernel: the decode GEMV kernel; per-launch durations by HIP events
+    # dominant kernel: the decode GEMV kernel (one launch per stage); per-launch HIP events
     per = step.per_launch_ms()
     kern_gbs = wbytes / (per.sum() * 1e-3) / 1e9
-    log(f"[bench] kernel-sum {per.sum() * 1e3:.1f} us over {len(per)} launches -> {kern_gbs:.0f} GB/s")
     big = max(range(len(step.stages)), key=lambda i: step.stages[i][4])
-    log(f"[bench] largest launch (lm_head): {per[big] * 1e3:.1f} us -> "
-        f"{step.stages[big][4] / (per[big] * 1e-3) / 1e9:.0f} GB/s")
+    log(f"[bench] kernel-sum {per.sum() * 1e3:.1f} us over {len(per)} launches -> {kern_gbs:.0f} GB/s; "
+        f"largest launch {per[big] * 1e3:.1f} us -> {step.stages[big][4] / (per[big] * 1e-3) / 1e9:.0f} GB/s")
     roof = {"bound": "hbm", "achieved": round(kern_gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
             "frac": round(kern_gbs / HBM_PEAK_GBS, 4), "traffic": None,
-            "kernel": "gemv_mx_kernel (all 145 launches of the step)",
-            "bytes_per_launch": wbytes / len(per), "avg_launch_us": float(per.mean() * 1e3)}
+            "kernel": "gemv_mx_kernel, all 145 launches of the 8B step (algorithmic bytes / summed launch time)",
+            "bytes_per_launch": round(wbytes / len(per), 1), "avg_launch_us": round(float(per.mean() * 1e3), 3),
+            "largest_launch": {"stage": "lm_head 4096x151936", "bytes": step.stages[big][4],
+                               "us": round(float(per[big] * 1e3), 2),
+                               "gbs": round(step.stages[big][4] / (per[big] * 1e-3) / 1e9, 1)}}
+    del step
+    torch.cuda.empty_cache()
+
+    extra = {}
+    if not args.no_extra:
+        t0 = time.time()
+        extra["single_gemv"] = extra_single(dev)
+        log(f"[bench] single GEMV: {extra['single_gemv']}")
+        st, extra["mlp_8b_m16"] = extra_step(synth.mlp_8b_m16(), dev, args.steps,
+                                             "8B MLP batch 16: 36 x (gate/up 4096x12288, down 12288x4096)")
+        log(f"[bench] mlp m16: {extra['mlp_8b_m16']}")
+        del st
+        torch.cuda.empty_cache()
+        extra["prefill"] = extra_prefill(dev)
+        log(f"[bench] prefill: {extra['prefill']}")
+        st, extra["decode_27b"] = extra_step(synth.decode_27b(), dev, args.steps,
+                                             "27B decode batch 1: 64 x (q/k/v/o 5120x5120, gate/up "
+                                             "5120x17408, down 17408x5120)")
+        extra["decode_27b"].update(extra_patch27b(st, dev))
+        log(f"[bench] 27b: {extra['decode_27b']}")
+        del st
+        torch.cuda.empty_cache()
+        extra["pm1"] = extra_pm1(dev)
+        log(f"[bench] pm1: {extra['pm1']} ({time.time() - t0:.0f} s of extras)")
+
     cpu = None
     if not args.no_cpu_baseline:
-        cpu = cpu_baseline(wl, args.cpu_layers)
+        cpu = cpu_baseline(wl)
         log(f"[bench] cpu baseline {cpu['value']:.3f} GB/s on {cpu['cores']} threads")
     out = {
         "metric": "1-bit decode GEMV weight-GB/s (% of HBM peak) and implied tok/s at 8B shape",
@@ -194,8 +349,53 @@ def main():
         "implied_tok_s": round(1e3 / ms, 1),
         "roofline": roof,
         "cpu_baseline": cpu,
+        "extra": extra,
     }
     print(json.dumps(out), flush=True)
+
+
+def run_only(args, dev):
+    """One workload alone, for profiler runs (rocprofv3 kernel traces and counters)."""
+    import torch
+    import bit_packed_sign_amd as b1
+    from bit_packed_sign_amd import synth
+    name = args.only
+    if name == "step8b":
+        st = Step(synth.decode_8b(), dev)
+        st.capture()
+        ms = st.timed(args.steps, args.warmup)
+        log(f"[bench] step8b {ms * 1e3:.1f} us")
+    elif name == "lmhead":
+        wl = synth.decode_8b()
+        i = len(wl.gemvs) - 1
+        bits, scales = synth.gemv_tensors(0, wl, i)
+        x = torch.from_numpy(synth.stage_activations(0, wl, len(wl.stages) - 1)).to(dev)
+        W = torch.from_numpy(bits.view(np.int32)).to(dev)
+        S = torch.from_numpy(scales).to(dev)
+        y = torch.empty((1, W.shape[0]), dtype=torch.float16, device=dev)
+        ms = time_fn(lambda: b1.gemv(x, W, S, out=y), reps=args.steps)
+        log(f"[bench] lm_head {ms * 1e3:.1f} us")
+    elif name == "single":
+        log(f"[bench] {extra_single(dev)}")
+    elif name == "mlp16":
+        st, o = extra_step(synth.mlp_8b_m16(), dev, args.steps, "mlp16")
+        log(f"[bench] {o}")
+    elif name == "prefill":
+        log(f"[bench] {extra_prefill(dev)}")
+    elif name == "step27b":
+        st, o = extra_step(synth.decode_27b(), dev, args.steps, "27b")
+        log(f"[bench] {o} patch {extra_patch27b(st, dev)}")
+    elif name == "pm1":
+        log(f"[bench] {extra_pm1(dev)}")
+    elif name == "copy":
+        # a plain device copy of known size, to scale the HBM traffic counters
+        src = torch.empty(256 << 20, dtype=torch.uint8, device=dev).fill_(1)
+        dst = torch.empty_like(src)
+        ms = time_fn(lambda: dst.copy_(src), reps=args.steps)
+        log(f"[bench] copy 256 MiB {ms * 1e3:.1f} us")
+    else:
+        raise SystemExit(f"unknown workload {name}")
+    torch.cuda.synchronize()
 
 
 if __name__ == "__main__":

@@ -70,6 +70,7 @@ hipError_t launch_gemv(const uint16_t *x, const uint32_t *W, const uint16_t *S, 
         set.count = 1;
         return launch_gemv_mx(x, set, K, st);
     }
+    if (M >= 2) return launch_gemv_smallm(x, W, S, y, M, K, N, st);
     dim3 grid((N + 3) / 4), block(256);
     if (M == 1)
         hipLaunchKernelGGL(gemv_select_kernel<1>, grid, block, 0, st, x, W, S, y, M, K, N);
