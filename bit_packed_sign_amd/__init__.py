@@ -3,5 +3,5 @@
 The computation lives in libbin1.so (C ABI: include/bin1.h, HIP kernels in csrc/); the
 functions below are its thin torch binding.  ``synth`` holds the seeded input generators.
 """
-from .binding import (Bin1Error, PatchTable, gemm_prefill, gemv, gemv_group, gemv_pm1, lib,  # noqa: F401
+from .binding import (Bin1Error, ChainPlan, PatchTable, gemm_prefill, gemv, gemv_group, gemv_pm1, lib,  # noqa: F401
                       xor_patch_apply, xor_patch_apply_multi)

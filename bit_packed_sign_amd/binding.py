@@ -31,11 +31,25 @@ _SIGS = {
     "bin1_gemv_pm1": [_p, _p, _p, _i, _i, _i, _p],
     "bin1_xor_patch_apply": [_p, _p, _i, _i, _i, _p, _p],
     "bin1_xor_patch_apply_multi": [_p, _p, _p, _i, _p, _i, _p, _p],
+    "bin1_chain_workspace_bytes": [_i],
+    "bin1_chain_prepare": [_p, _i, _p, ctypes.c_size_t, _p],
+    "bin1_gemv_chain": [_p, _p],
+    "bin1_chain_status": [_p, _p, _p],
     "bin1_status_string": [_i],
     "bin1_last_error": [],
     "bin1_abi_version": [],
 }
-_RESTYPE = {"bin1_status_string": ctypes.c_char_p, "bin1_last_error": ctypes.c_char_p}
+_RESTYPE = {"bin1_status_string": ctypes.c_char_p, "bin1_last_error": ctypes.c_char_p,
+            "bin1_chain_workspace_bytes": ctypes.c_size_t}
+
+
+class _Stage(ctypes.Structure):
+    _fields_ = [("x", _p), ("K", _i), ("count", _i), ("Wbits", _p * 4), ("scales", _p * 4),
+                ("y", _p * 4), ("N", _i * 4)]
+
+
+class _Plan(ctypes.Structure):
+    _fields_ = [("workspace", _p), ("nstages", _i), ("spmax", _i), ("max_tiles", _i), ("spin_limit", _i)]
 
 
 class Bin1Error(RuntimeError):
@@ -229,3 +243,62 @@ def xor_patch_apply_multi(table: PatchTable, entries: torch.Tensor, bad_rows: Op
         _check("bin1_xor_patch_apply_multi", lib().bin1_xor_patch_apply_multi(
             table.ptrs.data_ptr(), table.K.data_ptr(), table.N.data_ptr(), len(table),
             entries.data_ptr(), entries.shape[0], bp or None, _stream(table.ptrs)))
+
+
+class ChainPlan:
+    """A decode step as one persistent launch: ``stages`` is a sequence of
+    (x [1][K] fp16, [Wbits...], [scales...], [y...]) -- 1..4 products per stage that share x.
+    Stage s+1 starts after every output of stage s is written.  The device workspace is
+    allocated here with torch; ``run()`` only enqueues the kernel (capturable in a graph)."""
+
+    def __init__(self, stages):
+        if not stages:
+            raise ValueError("need at least one stage")
+        dev = stages[0][0].device
+        arr = (_Stage * len(stages))()
+        self._keep = []
+        for i, (x, Ws, Ss, ys) in enumerate(stages):
+            _need(x, f"stage {i} x", (torch.float16,), 2)
+            if x.shape[0] != 1:
+                raise ValueError("chain stages take one activation row (batch 1)")
+            K = x.shape[1]
+            if not 1 <= len(Ws) <= 4 or len(Ss) != len(Ws) or len(ys) != len(Ws):
+                raise ValueError(f"stage {i}: need 1..4 matrices with scales and outputs")
+            st = arr[i]
+            st.x = x.data_ptr()
+            st.K = K
+            st.count = len(Ws)
+            for j, (W, S, y) in enumerate(zip(Ws, Ss, ys)):
+                _need(W, "Wbits", _BITS, 2)
+                _need(S, "scales", (torch.float16,), 2)
+                _need(y, "y", (torch.float16,), 2)
+                if W.shape[1] * 32 != K or tuple(S.shape) != (W.shape[0], K // 128) or \
+                        tuple(y.shape) != (1, W.shape[0]):
+                    raise ValueError(f"stage {i} matrix {j}: shapes do not match")
+                st.Wbits[j] = W.data_ptr()
+                st.scales[j] = S.data_ptr()
+                st.y[j] = y.data_ptr()
+                st.N[j] = W.shape[0]
+            self._keep.append((x, list(Ws), list(Ss), list(ys)))
+        nbytes = lib().bin1_chain_workspace_bytes(len(stages))
+        self.workspace = torch.empty(nbytes, dtype=torch.uint8, device=dev)
+        self.plan = _Plan()
+        with torch.cuda.device(dev):
+            _check("bin1_chain_prepare", lib().bin1_chain_prepare(
+                ctypes.cast(arr, _p), len(stages), self.workspace.data_ptr(), nbytes, ctypes.byref(self.plan)))
+
+    def set_spin_limit(self, polls: int):
+        """Bound every stage wait to `polls` polls (0 = the library default)."""
+        self.plan.spin_limit = int(polls)
+
+    def run(self):
+        with torch.cuda.device(self.workspace.device):
+            _check("bin1_gemv_chain", lib().bin1_gemv_chain(ctypes.byref(self.plan), _stream(self.workspace)))
+
+    def status(self):
+        """(completed runs, error flag) -- synchronous."""
+        runs, err = ctypes.c_int(0), ctypes.c_int(0)
+        with torch.cuda.device(self.workspace.device):
+            _check("bin1_chain_status", lib().bin1_chain_status(ctypes.byref(self.plan), ctypes.byref(runs),
+                                                                  ctypes.byref(err)))
+        return runs.value, err.value

@@ -16,7 +16,7 @@ ROOT = os.path.dirname(HERE)
 CSRC = os.path.join(HERE, "csrc")
 OBJ = os.path.join(HERE, "_build")
 LIB = os.path.join(HERE, "libbin1.so")
-SOURCES = ["api.hip", "gemv.hip", "gemv_mx.hip", "gemv_smallm.hip", "prefill.hip", "pm1.hip", "patch.hip"]
+SOURCES = ["api.hip", "gemv.hip", "gemv_mx.hip", "gemv_smallm.hip", "gemv_chain.hip", "prefill.hip", "pm1.hip", "patch.hip"]
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 ARCH = "gfx950"

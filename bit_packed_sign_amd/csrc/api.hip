@@ -5,7 +5,9 @@
 
 #include <cstdarg>
 #include <cstdio>
+#include <cstring>
 #include <string>
+#include <vector>
 
 #include "bin1.h"
 #include "kernels.hpp"
@@ -101,6 +103,134 @@ extern "C" {
 int bin1_abi_version(void) { return BIN1_ABI_VERSION; }
 
 const char *bin1_last_error(void) { return g_last_error.c_str(); }
+
+size_t bin1_chain_workspace_bytes(int nstages)
+{
+    if (nstages < 1) return 0;
+    const size_t flags = (size_t)nstages * bin1::kChainWgs * sizeof(int);
+    const size_t table = (size_t)nstages * sizeof(bin1::ChainStage);
+    return sizeof(bin1::ChainHeader) + ((flags + 255) & ~(size_t)255) + table;
+}
+
+int bin1_chain_prepare(const bin1_stage *stages, int nstages, void *workspace, size_t workspace_bytes,
+                       bin1_chain_plan *plan)
+{
+    if (!stages || !workspace || !plan) return fail(BIN1_ERR_NULL, "stages, workspace and plan must be non-NULL");
+    if (nstages < 1) return fail(BIN1_ERR_SHAPE, "need nstages >= 1");
+    const size_t need = bin1_chain_workspace_bytes(nstages);
+    if (workspace_bytes < need)
+        return fail(BIN1_ERR_SHAPE, "workspace too small: %zu bytes, need %zu", workspace_bytes, need);
+    if (reinterpret_cast<uintptr_t>(workspace) & 255u)
+        return fail(BIN1_ERR_ALIGN, "workspace must be 256-byte aligned");
+    int st;
+    if ((st = check_device(workspace, "workspace"))) return st;
+    int dev = 0, cus = 0;
+    if (hipGetDevice(&dev) != hipSuccess ||
+        hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
+        return fail(BIN1_ERR_DEVICE, "cannot query the device");
+    if (cus < bin1::kChainWgs)
+        return fail(BIN1_ERR_DEVICE, "the chain needs %d compute units, the device has %d", bin1::kChainWgs, cus);
+    int spmax = 1;
+    for (int s = 0; s < nstages; ++s) {
+        const bin1_stage &g = stages[s];
+        if (g.count < 1 || g.count > bin1::kMaxMats)
+            return fail(BIN1_ERR_SHAPE, "stage %d: count must be 1..%d", s, bin1::kMaxMats);
+        if (g.K < 256 || g.K % 256 != 0 || g.K > 20 * 1024)
+            return fail(BIN1_ERR_SHAPE, "stage %d: K must be a multiple of 256 in [256, 20480] (got %d)", s, g.K);
+        const int sp = ((g.K >> 10) + 3) / 4;
+        if (sp > spmax) spmax = sp;
+        for (int i = 0; i < g.count; ++i) {
+            if ((st = check_product_host(g.x, g.Wbits[i], g.scales[i], g.y[i], 1, g.K, g.N[i]))) return st;
+            if ((st = check_product_device(g.x, g.Wbits[i], g.scales[i], g.y[i]))) return st;
+        }
+    }
+    // outputs must not overwrite any weight or scale of the chain, nor another output of their stage
+    for (int s = 0; s < nstages; ++s)
+        for (int i = 0; i < stages[s].count; ++i) {
+            const void *y = stages[s].y[i];
+            const size_t yb = (size_t)stages[s].N[i] * 2;
+            for (int t = 0; t < nstages; ++t)
+                for (int j = 0; j < stages[t].count; ++j) {
+                    const bin1_stage &u = stages[t];
+                    if (overlap(y, yb, u.Wbits[j], (size_t)u.N[j] * (u.K / 8)) ||
+                        overlap(y, yb, u.scales[j], (size_t)u.N[j] * (u.K / 128) * 2) ||
+                        (t == s && j != i && overlap(y, yb, u.y[j], (size_t)u.N[j] * 2)))
+                        return fail(BIN1_ERR_ALIAS, "stage %d output %d overlaps stage %d matrix %d", s, i, t, j);
+                }
+        }
+    const int R = bin1::chain_rows_per_tile(spmax) / 16;
+    std::vector<bin1::ChainStage> table(nstages);
+    int max_tiles = 0;
+    for (int s = 0; s < nstages; ++s) {
+        const bin1_stage &g = stages[s];
+        bin1::ChainStage &c = table[s];
+        memset(&c, 0, sizeof c);
+        c.x = static_cast<const uint16_t *>(g.x);
+        c.K = g.K;
+        c.count = g.count;
+        int tiles = 0;
+        for (int i = 0; i < g.count; ++i) {
+            c.W[i] = g.Wbits[i];
+            c.S[i] = static_cast<const uint16_t *>(g.scales[i]);
+            c.y[i] = static_cast<uint16_t *>(g.y[i]);
+            c.N[i] = g.N[i];
+            tiles += (g.N[i] + 16 * R - 1) / (16 * R);
+            c.tile_end[i] = tiles;
+        }
+        c.ntiles = tiles;
+        const int per = (tiles + bin1::kChainWgs - 1) / bin1::kChainWgs;
+        if (per > max_tiles) max_tiles = per;
+    }
+    if (max_tiles * 64 * R * 4 > 64 * 1024)
+        return fail(BIN1_ERR_SHAPE, "a stage has too many rows for one chain (%d tiles per workgroup)", max_tiles);
+    bin1::ChainHeader hdr;
+    memset(&hdr, 0, sizeof hdr);
+    hdr.nstages = nstages;
+    hdr.spmax = spmax;
+    hdr.max_tiles = max_tiles;
+    uint8_t *ws = static_cast<uint8_t *>(workspace);
+    const size_t flags = (size_t)nstages * bin1::kChainWgs * sizeof(int);
+    const size_t toff = sizeof(bin1::ChainHeader) + ((flags + 255) & ~(size_t)255);
+    hipError_t e = hipMemcpy(ws, &hdr, sizeof hdr, hipMemcpyHostToDevice);
+    if (e == hipSuccess) e = hipMemset(ws + sizeof(bin1::ChainHeader), 0, flags);
+    if (e == hipSuccess) e = hipMemcpy(ws + toff, table.data(), table.size() * sizeof(bin1::ChainStage),
+                                       hipMemcpyHostToDevice);
+    if (e != hipSuccess) return fail(BIN1_ERR_LAUNCH, "bin1_chain_prepare: %s", hipGetErrorString(e));
+    plan->workspace = workspace;
+    plan->nstages = nstages;
+    plan->spmax = spmax;
+    plan->max_tiles = max_tiles;
+    plan->spin_limit = 0;
+    return ok();
+}
+
+int bin1_gemv_chain(const bin1_chain_plan *plan, void *stream)
+{
+    if (!plan || !plan->workspace) return fail(BIN1_ERR_NULL, "plan and its workspace must be non-NULL");
+    if (plan->nstages < 1 || plan->spmax < 1 || plan->spmax > 5)
+        return fail(BIN1_ERR_SHAPE, "plan was not prepared");
+    if (plan->spin_limit < 0) return fail(BIN1_ERR_SHAPE, "spin_limit must be >= 0");
+    uint8_t *ws = static_cast<uint8_t *>(plan->workspace);
+    const size_t flags = (size_t)plan->nstages * bin1::kChainWgs * sizeof(int);
+    const size_t toff = sizeof(bin1::ChainHeader) + ((flags + 255) & ~(size_t)255);
+    return launched(bin1::launch_gemv_chain(reinterpret_cast<bin1::ChainHeader *>(ws),
+                                            reinterpret_cast<int *>(ws + sizeof(bin1::ChainHeader)),
+                                            reinterpret_cast<const bin1::ChainStage *>(ws + toff),
+                                            plan->nstages, plan->spmax, plan->max_tiles, plan->spin_limit,
+                                            static_cast<hipStream_t>(stream)),
+                    "bin1_gemv_chain");
+}
+
+int bin1_chain_status(const bin1_chain_plan *plan, int *runs, int *error)
+{
+    if (!plan || !plan->workspace || !runs || !error) return fail(BIN1_ERR_NULL, "NULL argument");
+    bin1::ChainHeader hdr;
+    hipError_t e = hipMemcpy(&hdr, plan->workspace, sizeof hdr, hipMemcpyDeviceToHost);
+    if (e != hipSuccess) return fail(BIN1_ERR_LAUNCH, "bin1_chain_status: %s", hipGetErrorString(e));
+    *runs = hdr.gen;
+    *error = hdr.error;
+    return ok();
+}
 
 const char *bin1_status_string(int status)
 {

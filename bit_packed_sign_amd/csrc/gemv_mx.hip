@@ -29,57 +29,13 @@
 //    MFMA K-block G of segment sigma is scale group gamma = 8p + 2G + h.
 #include "common.hpp"
 #include "kernels.hpp"
+#include "mx_common.hpp"
 
 namespace bin1 {
 
 namespace {
 
-typedef unsigned u4v __attribute__((ext_vector_type(4)));
-
-// Raw buffer resources: loads past num_records return 0 and stores past it are dropped,
-// so ragged tiles and dead ring slots need no branches (branch-free code also lets the
-// compiler count outstanding loads exactly, which keeps the prefetch ring full).
-constexpr int kRsrcFlags = 0x00020000;
-constexpr unsigned kOob = 0x80000000u;          // an offset past every resource
-constexpr int kNT = 2;                           // cache policy: nontemporal (streamed once)
-
-__device__ __forceinline__ __amdgpu_buffer_rsrc_t rsrc(const void *p, unsigned bytes)
-{
-    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(p), (short)0, (int)bytes, kRsrcFlags);
-}
-
-constexpr int kBlk = 528;          // LDS bytes per (segment, word): 16 rows x 32 B + 16 zero bytes
-constexpr int kZero = 512;         // offset of the zero bytes inside a block
-
-// fp4 (e2m1) expansion of one word: nibble q of register v = 0x2 | bit(4q+v) << 3,
-// i.e. -1.0 for a set bit and +1.0 for a clear one (the sign is undone by the caller).
-__device__ __forceinline__ int8v unpack_fp4(uint32_t w)
-{
-    int8v b;
-    b[0] = (int)(((w << 3) & 0x88888888u) | 0x22222222u);
-    b[1] = (int)(((w << 2) & 0x88888888u) | 0x22222222u);
-    b[2] = (int)(((w << 1) & 0x88888888u) | 0x22222222u);
-    b[3] = (int)((w & 0x88888888u) | 0x22222222u);
-    b[4] = b[5] = b[6] = b[7] = 0;
-    return b;
-}
-
-// A operand of (segment, word t) for this lane, from the limb block in LDS.
-__device__ __forceinline__ int8v load_a(const uint8_t *blk, int lo, int hi)
-{
-    const u4v a0 = *reinterpret_cast<const u4v *>(blk + lo);
-    const u4v a1 = *reinterpret_cast<const u4v *>(blk + hi);
-    int8v a;
-    a[0] = a0.x; a[1] = a0.y; a[2] = a0.z; a[3] = a0.w;
-    a[4] = a1.x; a[5] = a1.y; a[6] = a1.z; a[7] = a1.w;
-    return a;
-}
-
-template <int T>
-__device__ __forceinline__ float4v mma(const int8v &a, uint32_t w, int scA, float4v c)
-{
-    return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a, unpack_fp4(w), c, 0, 4, T, scA, 0, 127);
-}
+using namespace mx;
 
 // x (fp16, K values) -> fp8 limbs in the A-operand order, plus E8M0 exponents, in LDS.
 // Block beta = k/32 holds the 32 activations of packed word beta (word t = beta % 4 of group
@@ -124,46 +80,14 @@ __device__ __forceinline__ void limbs_build(int K, uint8_t *lds, const XLoad<XT>
         const int tau = tid + 256 * q;
         if (256 * q >= ntask) break;                  // uniform: no task of this round
         const u4v p0 = xl.v[q][0], p1 = xl.v[q][1];
-        const uint32_t hw[8] = {p0.x, p0.y, p0.z, p0.w, p1.x, p1.y, p1.z, p1.w};
-        float u[16];
-        float mx = 0.f;
-#pragma unroll
-        for (int i = 0; i < 16; ++i) {
-            u[i] = h2f((uint16_t)(hw[i >> 1] >> (16 * (i & 1))));
-            mx = fmaxf(mx, fabsf(u[i]));
-        }
+        float mx = absmax16(p0, p1);
         mx = fmaxf(mx, __shfl_xor(mx, 1, kWave));        // the other half of the 32-block
         if (tau < ntask) {
-            const int e0 = mx > 0.f ? __builtin_amdgcn_frexp_expf(mx) - 1 : 0;   // 2^e0 <= mx
-            const float mul = __builtin_ldexpf(1.0f, 7 - e0);
-#pragma unroll
-            for (int i = 0; i < 16; ++i) u[i] *= mul;    // |u| < 256, exact
             const int beta = tau >> 1, h = tau & 1;
             const int gamma = beta >> 2, t = beta & 3;
             const int sigma = 2 * (gamma >> 3) + (gamma & 1), G = (gamma & 7) >> 1;
-            uint8_t *blk = lds + (sigma * 4 + t) * kBlk;
-#pragma unroll
-            for (int r = 0; r < 4; ++r) {
-                int d[4];
-#pragma unroll
-                for (int c = 0; c < 4; ++c) {
-                    int v = __builtin_amdgcn_cvt_pk_fp8_f32(u[c], u[4 + c], 0, false);
-                    d[c] = __builtin_amdgcn_cvt_pk_fp8_f32(u[8 + c], u[12 + c], v, true);
-                    *reinterpret_cast<int *>(blk + (4 * G + r) * 32 + (2 * c + h) * 4) = d[c];
-                }
-                if (h == 0)
-                    reinterpret_cast<uint8_t *>(sc)[(sigma * 16 + 4 * G + r) * 4 + t] =
-                        (uint8_t)(127 + e0 - 7 - 4 * r);
-                if (r < 3) {
-#pragma unroll
-                    for (int c = 0; c < 4; ++c) {
-                        u[c] = (u[c] - __builtin_amdgcn_cvt_f32_fp8(d[c], 0)) * 16.f;
-                        u[4 + c] = (u[4 + c] - __builtin_amdgcn_cvt_f32_fp8(d[c], 1)) * 16.f;
-                        u[8 + c] = (u[8 + c] - __builtin_amdgcn_cvt_f32_fp8(d[c], 2)) * 16.f;
-                        u[12 + c] = (u[12 + c] - __builtin_amdgcn_cvt_f32_fp8(d[c], 3)) * 16.f;
-                    }
-                }
-            }
+            convert16(p0, p1, mx, lds + (sigma * 4 + t) * kBlk, G, h,
+                      reinterpret_cast<uint8_t *>(sc) + (sigma * 16 + 4 * G) * 4 + t);
         }
     }
 }
@@ -188,17 +112,6 @@ struct Slot {
     uint32_t s[R][SP];
     uint16_t s1[R][SP];
 };
-
-// Sum over the four lanes n, n+16, n+32, n+48 (every lane gets its column's total).
-__device__ __forceinline__ float sum_groups(float v)
-{
-    const int iv = __builtin_bit_cast(int, v);
-    const auto a = __builtin_amdgcn_permlane32_swap(iv, iv, false, false);
-    v = __builtin_bit_cast(float, (int)a[0]) + __builtin_bit_cast(float, (int)a[1]);
-    const int iw = __builtin_bit_cast(int, v);
-    const auto b = __builtin_amdgcn_permlane16_swap(iw, iw, false, false);
-    return __builtin_bit_cast(float, (int)b[0]) + __builtin_bit_cast(float, (int)b[1]);
-}
 
 template <int SP, int P, int R, bool ODD>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 4)))

@@ -19,6 +19,35 @@ struct MxSet {
     int count;
 };
 
+// Persistent chain of dependent decode stages (one launch for a whole decode step).
+constexpr int kChainWgs = 256;                 // workgroups, one per CU of the MI355X
+struct ChainHeader {
+    int nstages;
+    int gen;          // completed runs (only grows)
+    int exit_count;   // workgroups finished, over all runs (only grows)
+    int error;        // set when a stage wait gave up
+    int spmax;
+    int max_tiles;
+    int withhold;     // fault injection for tests: nonzero = workgroup 0 never publishes stage 0,
+                      // so every later wait can only end through its spin limit
+    int pad[9];
+};
+struct ChainStage {
+    const uint16_t *x;
+    const uint32_t *W[kMaxMats];
+    const uint16_t *S[kMaxMats];
+    uint16_t *y[kMaxMats];
+    int N[kMaxMats];
+    int tile_end[kMaxMats];
+    int count;
+    int K;
+    int ntiles;
+    int pad;
+};
+int chain_rows_per_tile(int spmax);
+hipError_t launch_gemv_chain(ChainHeader *hdr, int *done, const ChainStage *table, int nst, int spmax,
+                             int max_tiles, long spin_limit, hipStream_t st);
+
 // Largest K the block-scaled decode kernel takes (longer rows use the select kernel).
 int mx_max_k();
 hipError_t launch_gemv_mx(const uint16_t *x, const MxSet &set, int K, hipStream_t st);

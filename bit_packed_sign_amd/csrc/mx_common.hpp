@@ -1,0 +1,133 @@
+// mx_common.hpp -- pieces shared by the block-scaled (fp4 x fp8) MFMA decode kernels.
+//
+// Weights: one packed word (32 signs, bit 1 = +1) becomes 32 fp4 e2m1 values +-1 (the
+// multiply-free sign expansion of the "PrismML Bonsai -- 1.15GB" page, section "What 1-bit
+// is"); activations: each 32-element block of x becomes four e4m3 limbs with per-block E8M0
+// exponents.  v_mfma_scale_f32_16x16x128_f8f6f4 contracts them, one 128-weight group per
+// chain of four instructions ("Bonsai 27B" page, section "Binary weight format", eq. b_eff).
+#pragma once
+
+#include "common.hpp"
+
+namespace bin1 {
+namespace mx {
+
+typedef unsigned u4v __attribute__((ext_vector_type(4)));
+
+// Raw buffer resources: loads past num_records return 0 and stores past it are dropped,
+// so ragged tiles and dead ring slots need no branches (branch-free code also lets the
+// compiler count outstanding loads exactly, which keeps a prefetch ring full).
+constexpr int kRsrcFlags = 0x00020000;
+constexpr unsigned kOob = 0x80000000u;          // an offset past every resource
+constexpr int kNT = 2;                           // cache policy: nontemporal (streamed once)
+
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t rsrc(const void *p, unsigned bytes)
+{
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(p), (short)0, (int)bytes, kRsrcFlags);
+}
+
+constexpr int kBlk = 528;          // LDS bytes per (segment, word): 16 rows x 32 B + 16 zero bytes
+constexpr int kZero = 512;         // offset of the zero bytes inside a block
+
+// fp4 (e2m1) expansion of one word: nibble q of register v = 0x2 | bit(4q+v) << 3,
+// i.e. -1.0 for a set bit and +1.0 for a clear one (the sign is undone by the caller).
+__device__ __forceinline__ int8v unpack_fp4(uint32_t w)
+{
+    int8v b;
+    b[0] = (int)(((w << 3) & 0x88888888u) | 0x22222222u);
+    b[1] = (int)(((w << 2) & 0x88888888u) | 0x22222222u);
+    b[2] = (int)(((w << 1) & 0x88888888u) | 0x22222222u);
+    b[3] = (int)((w & 0x88888888u) | 0x22222222u);
+    b[4] = b[5] = b[6] = b[7] = 0;
+    return b;
+}
+
+// A operand of (segment, word t) for this lane, from a limb block in LDS.
+__device__ __forceinline__ int8v load_a(const uint8_t *blk, int lo, int hi)
+{
+    const u4v a0 = *reinterpret_cast<const u4v *>(blk + lo);
+    const u4v a1 = *reinterpret_cast<const u4v *>(blk + hi);
+    int8v a;
+    a[0] = a0.x; a[1] = a0.y; a[2] = a0.z; a[3] = a0.w;
+    a[4] = a1.x; a[5] = a1.y; a[6] = a1.z; a[7] = a1.w;
+    return a;
+}
+
+template <int T>
+__device__ __forceinline__ float4v mma(const int8v &a, uint32_t w, int scA, float4v c)
+{
+    return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a, unpack_fp4(w), c, 0, 4, T, scA, 0, 127);
+}
+
+// Lane offsets of the A operand inside a limb block: rows m = 4G + r of the MFMA are
+// (group G, limb r) and are nonzero only in K-block G; lane (m, g) reads its 16-byte halves
+// from row m or from the zero bytes.
+__device__ __forceinline__ void a_offsets(int lane, int &lo, int &hi)
+{
+    const int m = lane & 15, g = lane >> 4, G = m >> 2;
+    lo = (G == (g >> 1)) ? m * 32 + 16 * (g & 1) : kZero;
+    hi = (G == 2 + (g >> 1)) ? m * 32 + 16 * (g & 1) : kZero;
+}
+
+// Limbs of 16 activations (one half h of a 32-element block) into a limb block.
+// p0, p1: the 16 fp16 values; `mx` must already be the max |x| over the whole 32-block.
+// blk: the block of (segment, word t); G: the block's MFMA K-block; scbyte: E8M0 bytes of
+// rows 4G..4G+3 for word t (stride 4 bytes), written by the h == 0 half.
+// Element j of a block row pairs with weight bit pi(j) = 4*(j%8) + j/8 (unpack_fp4 order):
+// activation i of the half sits at byte j = 8*(i%4) + 4h + i/4.
+__device__ __forceinline__ void convert16(const u4v p0, const u4v p1, float mx, uint8_t *blk, int G, int h,
+                                          uint8_t *scbyte)
+{
+    const uint32_t hw[8] = {p0.x, p0.y, p0.z, p0.w, p1.x, p1.y, p1.z, p1.w};
+    float u[16];
+#pragma unroll
+    for (int i = 0; i < 16; ++i) u[i] = h2f((uint16_t)(hw[i >> 1] >> (16 * (i & 1))));
+    const int e0 = mx > 0.f ? __builtin_amdgcn_frexp_expf(mx) - 1 : 0;   // 2^e0 <= mx
+    const float mul = __builtin_ldexpf(1.0f, 7 - e0);
+#pragma unroll
+    for (int i = 0; i < 16; ++i) u[i] *= mul;        // |u| < 256, exact
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+        int d[4];
+#pragma unroll
+        for (int c = 0; c < 4; ++c) {
+            int v = __builtin_amdgcn_cvt_pk_fp8_f32(u[c], u[4 + c], 0, false);
+            d[c] = __builtin_amdgcn_cvt_pk_fp8_f32(u[8 + c], u[12 + c], v, true);
+            *reinterpret_cast<int *>(blk + (4 * G + r) * 32 + (2 * c + h) * 4) = d[c];
+        }
+        if (h == 0) scbyte[r * 4] = (uint8_t)(127 + e0 - 7 - 4 * r);
+        if (r < 3) {
+#pragma unroll
+            for (int c = 0; c < 4; ++c) {
+                u[c] = (u[c] - __builtin_amdgcn_cvt_f32_fp8(d[c], 0)) * 16.f;
+                u[4 + c] = (u[4 + c] - __builtin_amdgcn_cvt_f32_fp8(d[c], 1)) * 16.f;
+                u[8 + c] = (u[8 + c] - __builtin_amdgcn_cvt_f32_fp8(d[c], 2)) * 16.f;
+                u[12 + c] = (u[12 + c] - __builtin_amdgcn_cvt_f32_fp8(d[c], 3)) * 16.f;
+            }
+        }
+    }
+}
+
+// max |x| over 16 fp16 values
+__device__ __forceinline__ float absmax16(const u4v p0, const u4v p1)
+{
+    const uint32_t hw[8] = {p0.x, p0.y, p0.z, p0.w, p1.x, p1.y, p1.z, p1.w};
+    float mx = 0.f;
+#pragma unroll
+    for (int i = 0; i < 16; ++i) mx = fmaxf(mx, fabsf(h2f((uint16_t)(hw[i >> 1] >> (16 * (i & 1))))));
+    return mx;
+}
+
+// Sum over the four lanes n, n+16, n+32, n+48 (every lane gets its column's total).
+__device__ __forceinline__ float sum_groups(float v)
+{
+    const int iv = __builtin_bit_cast(int, v);
+    const auto a = __builtin_amdgcn_permlane32_swap(iv, iv, false, false);
+    v = __builtin_bit_cast(float, (int)a[0]) + __builtin_bit_cast(float, (int)a[1]);
+    const int iw = __builtin_bit_cast(int, v);
+    const auto b = __builtin_amdgcn_permlane16_swap(iw, iw, false, false);
+    return __builtin_bit_cast(float, (int)b[0]) + __builtin_bit_cast(float, (int)b[1]);
+}
+
+}  // namespace mx
+}  // namespace bin1

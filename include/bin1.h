@@ -50,6 +50,7 @@
 #ifndef BIN1_H
 #define BIN1_H
 
+#include <stddef.h>
 #include <stdint.h>
 
 #ifdef __cplusplus
@@ -118,6 +119,57 @@ int bin1_xor_patch_apply(uint32_t *Wbits, const int32_t *rowlist, int nrows,
 int bin1_xor_patch_apply_multi(uint32_t *const *Wtab, const int32_t *Ktab, const int32_t *Ntab,
                                int nmat, const int32_t *entries, int nentries,
                                int32_t *bad_rows, void *stream);
+
+/* ------------------------------------------------------------------------------------
+ * Decode-step chain: a sequence of dependent stages in ONE persistent launch.
+ * Stage s = `count` (1..4) products that read the same activations x_s (fp16 [K_s]), M = 1;
+ * stage s+1 starts only after every output of stage s is written (the batch-1 decode order:
+ * q/k/v, o, gate/up, down per layer, then lm_head).  Launch and synchronisation latency, not
+ * weight bandwidth, bound batch-1 decode on datacenter GPUs ["Bonsai 27B" page, section
+ * "Low-bit kernels for hybrid attention"]; the chain keeps one workgroup per CU resident for
+ * the whole step, streams the next stage's weights while a stage waits, and orders stages
+ * with device-scope release/acquire flags in the workspace.
+ * Requirements: K_s % 256 == 0 and K_s <= 20480; the GPU has at least 256 compute units; the
+ * products follow bin1_gemv's layouts.  An output may be (and usually is) a later stage's x, but
+ * must not overlap its own stage's x, any Wbits or scales of the chain, or another output of
+ * its stage.
+ * The workspace (device memory, caller-owned, bin1_chain_workspace_bytes(nstages) bytes,
+ * 256-byte aligned) holds the stage table, the flags and a run counter; it must not be shared
+ * by two chains running at the same time.  Runs never need it cleared again (flags only
+ * grow), so one prepared chain can be captured into a HIP graph and replayed.  A stage wait
+ * is bounded (about seconds); if it gives up, that run's results are invalid and
+ * bin1_chain_status reports it (the flag stays set until the chain is prepared again).  */
+typedef struct bin1_stage {
+    const void *x;                 /* device fp16 [K] */
+    int K;
+    int count;                     /* 1..4 */
+    const uint32_t *Wbits[4];      /* device, [N[i]][K/32] */
+    const void *scales[4];         /* device fp16 [N[i]][K/128] */
+    void *y[4];                    /* device fp16 [N[i]] */
+    int N[4];
+} bin1_stage;
+
+typedef struct bin1_chain_plan {   /* filled by bin1_chain_prepare; plain host struct */
+    void *workspace;
+    int nstages;
+    int spmax;                     /* ceil(max_s ceil(K_s / 1024) / 4): selects the kernel variant */
+    int max_tiles;                 /* most row tiles one workgroup owns in any stage */
+    int spin_limit;                /* polls per stage wait before giving up; 0 (set by prepare) =
+                                      the default of about seconds; the caller may lower it */
+} bin1_chain_plan;
+
+size_t bin1_chain_workspace_bytes(int nstages);
+
+/* Validate the stages and write the stage table into `workspace` (synchronous host->device
+ * copies; not for use inside graph capture).  Fills *plan. */
+int bin1_chain_prepare(const bin1_stage *stages, int nstages, void *workspace, size_t workspace_bytes,
+                       bin1_chain_plan *plan);
+
+/* Enqueue one run of a prepared chain on `stream`.  Capturable. */
+int bin1_gemv_chain(const bin1_chain_plan *plan, void *stream);
+
+/* Synchronously read the workspace: *runs = completed runs, *error = 1 if a wait gave up. */
+int bin1_chain_status(const bin1_chain_plan *plan, int *runs, int *error);
 
 /* Static description of a status code. */
 const char *bin1_status_string(int status);

@@ -82,6 +82,20 @@ def test_group_validation(L):
     assert L.bin1_gemv_group(FAKE, 2, W, S, Y, n, 1, 128, None) == -4
 
 
+def test_chain_validation(L):
+    from bit_packed_sign_amd import binding
+    assert L.bin1_chain_workspace_bytes(0) == 0
+    assert L.bin1_chain_workspace_bytes(3) > 3 * 256 * 4
+    plan = binding._Plan()
+    assert L.bin1_chain_prepare(None, 1, FAKE, 1 << 20, ctypes.byref(plan)) == -1
+    st = (binding._Stage * 1)()
+    assert L.bin1_chain_prepare(ctypes.cast(st, ctypes.c_void_p), 0, FAKE, 1 << 20, ctypes.byref(plan)) == -2
+    assert L.bin1_chain_prepare(ctypes.cast(st, ctypes.c_void_p), 1, FAKE, 16, ctypes.byref(plan)) == -2
+    assert L.bin1_chain_prepare(ctypes.cast(st, ctypes.c_void_p), 1, FAKE + 16, 1 << 20, ctypes.byref(plan)) == -3
+    assert L.bin1_gemv_chain(None, None) == -1
+    assert L.bin1_gemv_chain(ctypes.byref(binding._Plan()), None) == -1
+
+
 def test_pm1_and_patch_validation(L):
     assert L.bin1_gemv_pm1(None, FAKE, FAKE, 1, 128, 1, None) == -1
     assert L.bin1_gemv_pm1(FAKE, FAKE * 2, FAKE * 3, 1, 96, 1, None) == -2
