@@ -158,7 +158,6 @@ int bin1_chain_prepare(const bin1_stage *stages, int nstages, void *workspace, s
                         return fail(BIN1_ERR_ALIAS, "stage %d output %d overlaps stage %d matrix %d", s, i, t, j);
                 }
         }
-    const int R = bin1::chain_rows_per_tile(spmax) / 16;
     std::vector<bin1::ChainStage> table(nstages);
     int max_tiles = 0;
     for (int s = 0; s < nstages; ++s) {
@@ -168,21 +167,27 @@ int bin1_chain_prepare(const bin1_stage *stages, int nstages, void *workspace, s
         c.x = static_cast<const uint16_t *>(g.x);
         c.K = g.K;
         c.count = g.count;
-        int tiles = 0;
+        c.rt = bin1::chain_unit_tiles(spmax, g.K);
+        const int urows = 16 * c.rt;
+        int units = 0;
         for (int i = 0; i < g.count; ++i) {
             c.W[i] = g.Wbits[i];
             c.S[i] = static_cast<const uint16_t *>(g.scales[i]);
             c.y[i] = static_cast<uint16_t *>(g.y[i]);
             c.N[i] = g.N[i];
-            tiles += (g.N[i] + 16 * R - 1) / (16 * R);
-            c.tile_end[i] = tiles;
+            units += (g.N[i] + urows - 1) / urows;
+            c.unit_end[i] = units;
         }
-        c.ntiles = tiles;
-        const int per = (tiles + bin1::kChainWgs - 1) / bin1::kChainWgs;
-        if (per > max_tiles) max_tiles = per;
+        c.nunits = units;
+        for (int t = 0; t < nstages && !c.x_written; ++t)
+            for (int j = 0; j < stages[t].count; ++j)
+                if (overlap(g.x, (size_t)g.K * 2, stages[t].y[j], (size_t)stages[t].N[j] * 2)) c.x_written = 1;
+        const int tiles = (units + bin1::kChainWgs - 1) / bin1::kChainWgs * c.rt;   // workgroup 0 has the most
+        if (tiles > max_tiles) max_tiles = tiles;
     }
-    if (max_tiles * 64 * R * 4 > 64 * 1024)
-        return fail(BIN1_ERR_SHAPE, "a stage has too many rows for one chain (%d tiles per workgroup)", max_tiles);
+    if (bin1::chain_lds_bytes(spmax, nstages, max_tiles) == 0)
+        return fail(BIN1_ERR_SHAPE, "the chain does not fit in on-chip memory (%d stages, %d row tiles per "
+                    "workgroup in its largest stage)", nstages, max_tiles);
     bin1::ChainHeader hdr;
     memset(&hdr, 0, sizeof hdr);
     hdr.nstages = nstages;

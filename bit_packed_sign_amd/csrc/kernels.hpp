@@ -32,19 +32,28 @@ struct ChainHeader {
                       // so every later wait can only end through its spin limit
     int pad[9];
 };
+// One stage as the kernel sees it.  Work is split into units of `rt` row tiles (16 rows each)
+// of one matrix; unit_end[] is cumulative over the stage's matrices.
 struct ChainStage {
     const uint16_t *x;
     const uint32_t *W[kMaxMats];
     const uint16_t *S[kMaxMats];
     uint16_t *y[kMaxMats];
     int N[kMaxMats];
-    int tile_end[kMaxMats];
+    int unit_end[kMaxMats];
     int count;
     int K;
-    int ntiles;
+    int nunits;
+    int rt;
+    int x_written;    // some stage of the chain writes x: read it device-coherently
     int pad;
 };
-int chain_rows_per_tile(int spmax);
+// Pairs (1024-wide K slices) each of the 4 waves takes for a stage of width K.
+__host__ __device__ inline int chain_pairs_per_wave(int K) { return ((K + 1023) / 1024 + 3) / 4; }
+// Row tiles per unit: the kernel's register slot holds spmax (row tile, pair) blocks.
+__host__ __device__ inline int chain_unit_tiles(int spmax, int K) { return spmax / chain_pairs_per_wave(K); }
+// Dynamic LDS of the chain kernel, or 0 if it does not fit in one workgroup's LDS.
+size_t chain_lds_bytes(int spmax, int nstages, int max_tiles);
 hipError_t launch_gemv_chain(ChainHeader *hdr, int *done, const ChainStage *table, int nst, int spmax,
                              int max_tiles, long spin_limit, hipStream_t st);
 
