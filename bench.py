@@ -6,9 +6,15 @@
 Headline step: one batch-1 decode pass of the 8B-class model's GEMVs -- 36 layers of
 q 4096x4096, k/v 4096x1024, o 4096x4096, gate/up 4096x12288, down 12288x4096, then
 lm_head 4096x151936: 253 products in 145 dependent stages (q/k/v and gate/up each share
-one activation vector and run as one launch), every stage reading its own fp16 activation
-vector (norms/attention omitted), all weights and activations resident in HBM.  The step
-is captured once into a HIP graph and replayed; K replays are timed between HIP events.
+one activation vector), every stage reading its own fp16 activation vector (norms/attention
+omitted), all weights and activations resident in HBM.  Two complete implementations of the
+dependent step are timed on the same tensors:
+  graph  -- one decode launch per stage (same-input products fused), captured once into a HIP
+            graph and replayed;
+  chain  -- the whole step as one persistent launch (bin1_gemv_chain): stage s+1 reads its x
+            only after every output of stage s is visible device-wide.
+K steps of each are timed between HIP events after W warm-up steps; the faster one is the
+headline (named in config.workload) and the other is reported under extra.step_paths.
 
 Metric: weight-GB/s = bytes of packed bits + fp16 scales per step (1,064,263,680 B)
 divided by the step time; implied tokens/s = 1 / step time.
@@ -44,7 +50,7 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-extra", action="store_true")
     ap.add_argument("--only", default=None,
-                    help="run one workload alone (for profiling): step8b, lmhead, single, mlp16, "
+                    help="run one workload alone (for profiling): step8b, chain8b, lmhead, single, mlp16, "
                          "prefill, step27b, pm1, copy")
     return ap.parse_args()
 
@@ -155,6 +161,61 @@ class Step:
         return tot / reps
 
 
+class ChainStep:
+    """The same stages as one persistent chain launch per step."""
+
+    def __init__(self, step):
+        import bit_packed_sign_amd as b1
+        self.step = step
+        self.plan = b1.ChainPlan([(x, Ws, Ss, ys) for x, Ws, Ss, ys, _ in step.stages])
+
+    def timed(self, steps, warmup):
+        import torch
+        for _ in range(warmup):
+            self.plan.run()
+        torch.cuda.synchronize()
+        e0, e1 = events()
+        st = torch.cuda.current_stream()
+        e0.record(st)
+        for _ in range(steps):
+            self.plan.run()
+        e1.record(st)
+        torch.cuda.synchronize()
+        runs, err = self.plan.status()
+        if err:
+            raise RuntimeError("the chain reported a stage wait that gave up")
+        return e0.elapsed_time(e1) / steps
+
+
+def kernel_source_sha(*names):
+    """Hash of the kernel sources a stored counter summary was taken with."""
+    import hashlib
+    h = hashlib.sha256()
+    for n in names:
+        with open(os.path.join(ROOT, "bit_packed_sign_amd", "csrc", n), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def stored_traffic(kernel_key, sources, bytes_per_launch):
+    """HBM traffic per launch from the committed rocprofv3 counter summary of `kernel_key`
+    (FETCH_SIZE / WRITE_SIZE scaled by a plain copy of known size), or None when the summary
+    is missing or the kernel sources changed since it was taken."""
+    path = os.path.join(ROOT, "profiles", "traffic.json")
+    try:
+        with open(path) as f:
+            rec = json.load(f)[kernel_key]
+    except (OSError, KeyError, ValueError):
+        return None
+    if rec.get("source_sha") != kernel_source_sha(*sources):
+        return None
+    return {"fetch_bytes_per_launch": rec["fetch_bytes_per_launch"],
+            "write_bytes_per_launch": rec["write_bytes_per_launch"],
+            "over_algorithmic": round((rec["fetch_bytes_per_launch"] + rec["write_bytes_per_launch"]) /
+                                      bytes_per_launch, 3),
+            "copy_scale": rec["copy_scale"], "source": "profiles/traffic.json"}
+
+
 def cpu_baseline(wl):
     """The fp64 oracle over every output of the whole 8B decode step, on the host cores."""
     from bit_packed_sign_amd import synth
@@ -211,13 +272,18 @@ def extra_single(dev):
             "note": "eager launches back to back: each time includes the launch gap"}
 
 
-def extra_step(wl, dev, steps, label):
+def extra_step(wl, dev, steps, label, chain=False):
     st = Step(wl, dev)
     st.capture()
     ms = st.timed(max(5, steps // 2), 2)
     out = {"workload": label, "ms_per_step": round(ms, 4),
            "gbs": round(wl.weight_bytes / ms / 1e6, 1), "tok_s": round(1e3 / ms, 1),
-           "pct_hbm_peak": round(100 * wl.weight_bytes / ms / 1e6 / HBM_PEAK_GBS, 2)}
+           "pct_hbm_peak": round(100 * wl.weight_bytes / ms / 1e6 / HBM_PEAK_GBS, 2), "path": "graph"}
+    if chain:
+        c = ChainStep(st)
+        msc = c.timed(max(5, steps // 2), 2)
+        out["chain"] = {"ms_per_step": round(msc, 4), "gbs": round(wl.weight_bytes / msc / 1e6, 1)}
+        del c
     return st, out
 
 
@@ -286,30 +352,57 @@ def main():
         return
 
     wl = synth.decode_8b()
+    wbytes = wl.weight_bytes
     step = Step(wl, dev)
     step.capture()
-    ms = step.timed(args.steps, args.warmup)
-    wbytes = wl.weight_bytes
-    gbs = wbytes / (ms * 1e-3) / 1e9
-    log(f"[bench] step {ms * 1e3:.1f} us, {gbs:.0f} GB/s, {1e3 / ms:.0f} tok/s")
+    ms_graph = step.timed(args.steps, args.warmup)
+    log(f"[bench] graph step {ms_graph * 1e3:.1f} us, {wbytes / ms_graph / 1e6:.0f} GB/s")
+    chain = ChainStep(step)
+    ms_chain = chain.timed(args.steps, args.warmup)
+    log(f"[bench] chain step {ms_chain * 1e3:.1f} us, {wbytes / ms_chain / 1e6:.0f} GB/s")
 
-    # dominant kernel: the decode GEMV kernel (one launch per stage); per-launch HIP events
+    # eager per-launch HIP events (on the launch stream) give each stage's share; in the replayed
+    # graph the launches run back to back, so the kernel's average duration there is the step
+    # time over the launches (rocprofv3 kernel traces of the same command agree)
     per = step.per_launch_ms()
-    kern_gbs = wbytes / (per.sum() * 1e-3) / 1e9
-    big = max(range(len(step.stages)), key=lambda i: step.stages[i][4])
-    log(f"[bench] kernel-sum {per.sum() * 1e3:.1f} us over {len(per)} launches -> {kern_gbs:.0f} GB/s; "
-        f"largest launch {per[big] * 1e3:.1f} us -> {step.stages[big][4] / (per[big] * 1e-3) / 1e9:.0f} GB/s")
-    roof = {"bound": "hbm", "achieved": round(kern_gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-            "frac": round(kern_gbs / HBM_PEAK_GBS, 4), "traffic": None,
-            "kernel": "gemv_mx_kernel, all 145 launches of the 8B step (algorithmic bytes / summed launch time)",
-            "bytes_per_launch": round(wbytes / len(per), 1), "avg_launch_us": round(float(per.mean() * 1e3), 3),
-            "largest_launch": {"stage": "lm_head 4096x151936", "bytes": step.stages[big][4],
-                               "us": round(float(per[big] * 1e3), 2),
-                               "gbs": round(step.stages[big][4] / (per[big] * 1e-3) / 1e9, 1)}}
-    del step
+    nl = len(step.stages)
+    big = max(range(nl), key=lambda i: step.stages[i][4])
+    paths = {
+        "graph": {"ms_per_step": round(ms_graph, 5), "gbs": round(wbytes / ms_graph / 1e6, 1),
+                  "tok_s": round(1e3 / ms_graph, 1),
+                  "launches": nl, "avg_launch_us_in_graph": round(ms_graph * 1e3 / nl, 3),
+                  "eager_launch_sum_us": round(float(per.sum() * 1e3), 1),
+                  "largest_launch_eager": {"stage": "lm_head 4096x151936", "bytes": step.stages[big][4],
+                                           "us": round(float(per[big] * 1e3), 2),
+                                           "gbs": round(step.stages[big][4] / (per[big] * 1e-3) / 1e9, 1)}},
+        "chain": {"ms_per_step": round(ms_chain, 5), "gbs": round(wbytes / ms_chain / 1e6, 1),
+                  "tok_s": round(1e3 / ms_chain, 1)},
+    }
+    if ms_chain <= ms_graph:
+        head, ms = "chain", ms_chain
+        achieved = wbytes / (ms_chain * 1e-3) / 1e9
+        roof = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                "frac": round(achieved / HBM_PEAK_GBS, 4),
+                "traffic": stored_traffic("gemv_chain_kernel", ["gemv_chain.hip", "mx_common.hpp"], wbytes),
+                "kernel": "gemv_chain_kernel (one launch per step)",
+                "bytes_per_launch": wbytes, "avg_launch_us": round(ms_chain * 1e3, 2),
+                "timing": "HIP events around the timed launches (back to back on one stream)"}
+    else:
+        head, ms = "graph", ms_graph
+        achieved = wbytes / (ms_graph * 1e-3) / 1e9
+        roof = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                "frac": round(achieved / HBM_PEAK_GBS, 4),
+                "traffic": stored_traffic("gemv_mx_kernel", ["gemv_mx.hip", "mx_common.hpp"], wbytes / nl),
+                "kernel": "gemv_mx_kernel, all 145 launches of the 8B step",
+                "bytes_per_launch": round(wbytes / nl, 1), "avg_launch_us": round(ms_graph * 1e3 / nl, 3),
+                "timing": "HIP events around the timed graph replays on the replay stream; launches run "
+                          "back to back, so the average launch is the step time over 145 launches"}
+    gbs = wbytes / (ms * 1e-3) / 1e9
+    log(f"[bench] headline {head}: {ms * 1e3:.1f} us, {gbs:.0f} GB/s, {1e3 / ms:.0f} tok/s")
+    del chain, step
     torch.cuda.empty_cache()
 
-    extra = {}
+    extra = {"step_paths": paths}
     if not args.no_extra:
         t0 = time.time()
         extra["single_gemv"] = extra_single(dev)
@@ -323,7 +416,7 @@ def main():
         log(f"[bench] prefill: {extra['prefill']}")
         st, extra["decode_27b"] = extra_step(synth.decode_27b(), dev, args.steps,
                                              "27B decode batch 1: 64 x (q/k/v/o 5120x5120, gate/up "
-                                             "5120x17408, down 17408x5120)")
+                                             "5120x17408, down 17408x5120)", chain=True)
         extra["decode_27b"].update(extra_patch27b(st, dev))
         log(f"[bench] 27b: {extra['decode_27b']}")
         del st
@@ -342,8 +435,10 @@ def main():
         "dtype": "f16", "data": "synthetic",
         "config": {"workload": "decode-8b-m1: 36 x (q 4096x4096, k/v 4096x1024, o 4096x4096, "
                                "gate/up 4096x12288, down 12288x4096) + lm_head 4096x151936, batch 1, "
-                               "253 GEMVs in 145 dependent stages (q/k/v and gate/up fused per stage), "
-                               "HIP-graph replay",
+                               "253 GEMVs in 145 dependent stages (q/k/v and gate/up fused per stage); "
+                               + ("one persistent chain launch per step" if head == "chain" else
+                                  "one launch per stage, HIP-graph replay"),
+                   "step_path": head,
                    "weight_bytes_per_step": wbytes, "global_batch": 1, "parallelism": "none (1 GPU)"},
         "pct_hbm_peak": round(100 * gbs / HBM_PEAK_GBS, 2),
         "implied_tok_s": round(1e3 / ms, 1),
@@ -365,6 +460,10 @@ def run_only(args, dev):
         st.capture()
         ms = st.timed(args.steps, args.warmup)
         log(f"[bench] step8b {ms * 1e3:.1f} us")
+    elif name == "chain8b":
+        st = Step(synth.decode_8b(), dev)
+        ms = ChainStep(st).timed(args.steps, args.warmup)
+        log(f"[bench] chain8b {ms * 1e3:.1f} us")
     elif name == "lmhead":
         wl = synth.decode_8b()
         i = len(wl.gemvs) - 1
