@@ -287,27 +287,39 @@ void gemv_chain_kernel(ChainHeader *hdr, int *done, const ChainStage *table, int
             auto one = [&](CSlot<SP> &sl) {
                 advance(is, iu);                       // (is, iu) = last unit issued; look up the
                 const IssueAt nx = issue_at(is, iu);   // next one before the products run
+                // All blocks' MFMA chains advance together, word by word, so consecutive MFMAs
+                // are independent (one accumulator per chain) and the matrix pipe stays full.
+                // Branch-free: a block past the end of K has zero activations and zero scales
+                // (out-of-range loads), so it adds exactly 0, and straight-line code lets the
+                // compiler keep the other slot's loads in flight.
+                constexpr int NB = RT * NPW;
+                float4v c[NB][2];
+#pragma unroll
+                for (int b = 0; b < NB; ++b) c[b][0] = c[b][1] = float4v{0.f, 0.f, 0.f, 0.f};
+                auto word = [&](auto T_c) {
+                    constexpr int T = decltype(T_c)::value;
+#pragma unroll
+                    for (int b = 0; b < NB; ++b)
+#pragma unroll
+                        for (int h = 0; h < 2; ++h) {
+                            const int p = b % NPW;
+                            c[b][h] = mma<T>(A[p][h][T], sl.w[b][h][T], scA[p][h], c[b][h]);
+                        }
+                };
+                word(std::integral_constant<int, 0>{});
+                word(std::integral_constant<int, 1>{});
+                word(std::integral_constant<int, 2>{});
+                word(std::integral_constant<int, 3>{});
                 float acc[RT];
 #pragma unroll
                 for (int t = 0; t < RT; ++t) acc[t] = 0.f;
 #pragma unroll
-                // Branch-free: a block past the end of K has zero activations and zero scales
-                // (out-of-range loads), so it adds exactly 0, and straight-line code lets the
-                // compiler keep the other slot's loads in flight.
-                for (int b = 0; b < RT * NPW; ++b) {
-                    const int t = b / NPW, p = b % NPW;
+                for (int b = 0; b < NB; ++b) {
                     const uint32_t sv = sl.s[b];
                     const float s0 = h2f((uint16_t)(sv & 0xFFFFu)), s1 = h2f((uint16_t)(sv >> 16));
-#pragma unroll
-                    for (int h = 0; h < 2; ++h) {
-                        const u4v w = sl.w[b][h];
-                        float4v c = {0.f, 0.f, 0.f, 0.f};
-                        c = mma<0>(A[p][h][0], w.x, scA[p][h], c);
-                        c = mma<1>(A[p][h][1], w.y, scA[p][h], c);
-                        c = mma<2>(A[p][h][2], w.z, scA[p][h], c);
-                        c = mma<3>(A[p][h][3], w.w, scA[p][h], c);
-                        acc[t] = fmaf(-(h ? s1 : s0), (c[0] + c[1]) + (c[2] + c[3]), acc[t]);
-                    }
+                    // B held -w, so a group's partial is -(c0+c1+c2+c3)
+                    acc[b / NPW] = fmaf(-s0, (c[b][0][0] + c[b][0][1]) + (c[b][0][2] + c[b][0][3]), acc[b / NPW]);
+                    acc[b / NPW] = fmaf(-s1, (c[b][1][0] + c[b][1][1]) + (c[b][1][2] + c[b][1][3]), acc[b / NPW]);
                 }
                 issue(nx, sl);                         // refill this slot with that unit
 #pragma unroll
