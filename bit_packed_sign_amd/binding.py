@@ -128,7 +128,7 @@ def gemv(x: torch.Tensor, Wbits: torch.Tensor, scales: torch.Tensor, out: Option
 
 def gemv_group(x: torch.Tensor, Wbits: Sequence[torch.Tensor], scales: Sequence[torch.Tensor],
                outs: Optional[Sequence[torch.Tensor]] = None):
-    """Products of several matrices with the same activations x (e.g. q/k/v), one launch at M=1.
+    """Products of several matrices with the same activations x (e.g. q/k/v), one launch for M <= 16.
     Returns the list of outputs y_i [M][N_i]."""
     _need(x, "x", (torch.float16,), 2)
     count = len(Wbits)

@@ -302,6 +302,18 @@ int bin1_gemv_group(const void *x, int count, const uint32_t *const *Wbits,
         return launched(bin1::launch_gemv_mx(static_cast<const uint16_t *>(x), set, K, st),
                         "bin1_gemv_group");
     }
+    if (M >= 2 && M <= 16) {                              // small batch: one launch as well
+        bin1::MxSet set{};
+        for (int i = 0; i < count; ++i) {
+            set.W[i] = Wbits[i];
+            set.S[i] = static_cast<const uint16_t *>(scales[i]);
+            set.y[i] = static_cast<uint16_t *>(y[i]);
+            set.N[i] = N[i];
+        }
+        set.count = count;
+        return launched(bin1::launch_gemv_smallm(static_cast<const uint16_t *>(x), set, M, K, st),
+                        "bin1_gemv_group");
+    }
     for (int i = 0; i < count; ++i) {
         hipError_t e = bin1::launch_gemv(static_cast<const uint16_t *>(x), Wbits[i],
                                          static_cast<const uint16_t *>(scales[i]),

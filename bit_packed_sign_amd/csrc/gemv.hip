@@ -70,7 +70,12 @@ hipError_t launch_gemv(const uint16_t *x, const uint32_t *W, const uint16_t *S, 
         set.count = 1;
         return launch_gemv_mx(x, set, K, st);
     }
-    if (M >= 2) return launch_gemv_smallm(x, W, S, y, M, K, N, st);
+    if (M >= 2) {
+        MxSet set{};
+        set.W[0] = W; set.S[0] = S; set.y[0] = y; set.N[0] = N;
+        set.count = 1;
+        return launch_gemv_smallm(x, set, M, K, st);
+    }
     dim3 grid((N + 3) / 4), block(256);
     if (M == 1)
         hipLaunchKernelGGL(gemv_select_kernel<1>, grid, block, 0, st, x, W, S, y, M, K, N);

@@ -2,14 +2,24 @@
 //
 // y[m][n] = sum_k s[n][k/128] * w(n,k) * x[m][k] ["Bonsai 27B" page, section "Binary weight
 // format", eq. b_eff], fused decode with fp32 accumulation ["Bonsai 27B" page, section
-// "Low-bit kernels for hybrid attention"].
+// "Low-bit kernels for hybrid attention"].  With M tokens each weight serves M products, so
+// the expansion of a sign costs 1/M per product.
 //
-// With M tokens each weight byte serves M products, so the per-weight expansion cost is
-// amortised over the batch.  The tokens are the 16 A rows of v_mfma_f32_16x16x32_f16 (x is
-// fp16 already, so A is exact; rows past M are zero).  The weight operand is built directly
-// as fp16 +-|s| pairs: a pair takes one shift and one bit-field insert of the sign bit into
-// |s| (the sign of a negative scale is folded into the word first), so the group scale is
-// applied inside the product and the MFMA accumulates straight across groups.
+// v_mfma_f32_16x16x32_f16: the tokens are the 16 A rows (x is fp16 already, so A is exact;
+// rows past M are zero) and 16 weight rows are the B columns.  Lane (n, b) of a wave owns
+// ONE scale group of row n -- group 4*wave + b of the current 4096-wide K chunk -- so a tile
+// costs each lane one 16-byte load and one scale load, and the group scale goes straight into
+// the B operand as fp16 +-|s| (a negative scale is folded into the sign bits).
+//
+// k order inside an MFMA: for MFMA t = 4j + q of a group (word j, quarter q), lane (n, b)'s
+// B pair p holds the signs of bits 4q + p and 4q + p + 16 of word j -- one shift and one
+// and-or per fp16 pair -- and its A pair p holds x at the same two positions.
+//
+// x goes through LDS: the workgroup copies each 4096-wide K chunk of the 16 token rows
+// (128 KB) with contiguous 16-byte loads, all in flight at once; each wave then reads and
+// interleaves its A operands once per chunk and reuses them for every tile of the batch.
+// Read straight from memory, every A load would touch 64 cache lines.  The merge table
+// reuses the same LDS once the batch's last chunk is done.
 #include "common.hpp"
 #include "kernels.hpp"
 
@@ -28,143 +38,222 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t rsrc(const void *p, unsigned b
     return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(p), (short)0, (int)bytes, kRsrcFlags);
 }
 
-// fp16 +-|s| pairs for the 8 weights of byte `b` of word `nw` (nw: sign bit 1 = negative
-// product).  Pair j holds the weights of bits 2j (low half) and 2j+1 (high half) of the byte,
-// matching A's halves x[8b + 2j], x[8b + 2j + 1].  |s| has clear sign bits, so each pair is
-// one shift and one and-or.
-__device__ __forceinline__ half8 expand_byte(uint32_t nw, int b, uint32_t s2abs)
+constexpr int kWaves = 8;                            // waves per workgroup
+constexpr int kChunkGroups = 4 * kWaves;             // scale groups per K chunk (4096 k)
+constexpr int kChunkK = 128 * kChunkGroups;
+constexpr int kXRow = kChunkK + 8;                   // LDS row stride of the staged chunk (halves)
+constexpr int kXBytes = 16 * kXRow * 2;              // 16 token rows
+static_assert(kChunkK == 8 * 64 * kWaves && kWaves == 8, "one 16-byte load per thread per token row");
+
+// out dword p = (lo[p], hi[p]) for the 8 fp16 of lo and hi
+__device__ __forceinline__ void interleave(const u4v lo, const u4v hi, half8 &o0, half8 &o1)
 {
-    const uint32_t by = (nw >> (8 * b)) & 0xFFu;
-    const uint32_t tt = by | ((by >> 1) << 16);     // high copy pre-shifted by one bit
-    uint32_t p[4];
-#pragma unroll
-    for (int j = 0; j < 4; ++j) p[j] = ((tt << (15 - 2 * j)) & 0x80008000u) | s2abs;
-    return __builtin_bit_cast(half8, u4v{p[0], p[1], p[2], p[3]});
+    const u4v a{__builtin_amdgcn_perm(hi.x, lo.x, 0x05040100u), __builtin_amdgcn_perm(hi.x, lo.x, 0x07060302u),
+                __builtin_amdgcn_perm(hi.y, lo.y, 0x05040100u), __builtin_amdgcn_perm(hi.y, lo.y, 0x07060302u)};
+    const u4v b{__builtin_amdgcn_perm(hi.z, lo.z, 0x05040100u), __builtin_amdgcn_perm(hi.z, lo.z, 0x07060302u),
+                __builtin_amdgcn_perm(hi.w, lo.w, 0x05040100u), __builtin_amdgcn_perm(hi.w, lo.w, 0x07060302u)};
+    o0 = __builtin_bit_cast(half8, a);
+    o1 = __builtin_bit_cast(half8, b);
 }
 
-constexpr int kWaves = 8;                            // waves per workgroup
-constexpr int kChunkWords = 128;                     // 4096 weights per K chunk
-constexpr int kWPW = kChunkWords / kWaves;           // words per wave in a chunk
-constexpr int kGPW = kWPW / 4;                       // scale groups per wave in a chunk
-
-// Work: a workgroup of 8 waves takes batches of up to TB 16-row tiles (grid-stride); for each
-// batch it walks K in 4096-wide chunks.  In a chunk, wave w covers words [16w, 16w+16): its A
-// operands (16 tokens x 512 k) are loaded into registers once per (batch, chunk) and reused
-// by every tile of the batch.  Weights stream through a ring of P (chunk, tile) units.  The
-// waves' partial tiles are merged through LDS at the end of each batch.
-template <int P, int TB>
-__global__ __launch_bounds__(64 * kWaves) __attribute__((amdgpu_waves_per_eu(2, 2)))
-void gemv_smallm_kernel(const uint16_t *__restrict__ x, const uint32_t *__restrict__ W,
-                        const uint16_t *__restrict__ S, uint16_t *__restrict__ y, int M, int K, int N,
-                        int ntiles)
+// B operand of quarter Q: pair p = (+-|s| for bit 4Q + p, for bit 4Q + p + 16) of nw, bit 1 of
+// nw meaning a negative product.
+template <int Q>
+__device__ __forceinline__ half8 expand_q(uint32_t nw, uint32_t s2abs)
 {
-    __shared__ __attribute__((aligned(16))) float red[TB * 256 * kWaves];   // [tile][16 rows][16 tok][waves]
+    const u4v d{((nw << (15 - 4 * Q)) & 0x80008000u) | s2abs, ((nw << (14 - 4 * Q)) & 0x80008000u) | s2abs,
+                ((nw << (13 - 4 * Q)) & 0x80008000u) | s2abs, ((nw << (12 - 4 * Q)) & 0x80008000u) | s2abs};
+    return __builtin_bit_cast(half8, d);
+}
+
+struct SmSlot {
+    u4v w;          // this lane's group: 4 words of row n
+    uint32_t s;     // its fp16 scale
+};
+
+struct SmTile {     // one tile of the workgroup, resolved once
+    const uint32_t *W;
+    const uint16_t *S;
+    uint16_t *y;
+    int row0, N;    // N = 0: no tile (its loads return zeros, nothing is stored)
+};
+
+// Work: workgroup g takes tiles g, g + G, ... (at most TB of them); for these it walks K in
+// 4096-wide chunks.  Slot [d][t] holds tile t's group for chunk c = D*j + d, so D chunks of
+// every tile are in flight; a wave's A operands are built once per chunk, and the next chunk
+// of x is already loading (into registers) while the current one is used.  The waves' partial
+// tiles are merged through LDS at the end.  Tile slots past the workgroup's tiles compute on
+// zeros and are never stored.
+template <int TB, int D>
+__global__ __launch_bounds__(64 * kWaves) __attribute__((amdgpu_waves_per_eu(2, 2)))
+void gemv_smallm_kernel(const uint16_t *__restrict__ x, MxSet set, int M, int K, int ntiles)
+{
+    extern __shared__ __attribute__((aligned(16))) uint16_t xs[];   // staged chunk [16][kXRow]
+    float *red = reinterpret_cast<float *>(xs);                     // then [tile][wave][lane][4]
     const int lane = threadIdx.x & 63;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int n = lane & 15, b = lane >> 4;
     const int wpr = K >> 5, spr = K >> 7;
-    const int nchunk = (wpr + kChunkWords - 1) / kChunkWords;
-    const int my_tiles = blockIdx.x < ntiles ? (ntiles - 1 - blockIdx.x) / gridDim.x + 1 : 0;
-
+    const int nchunk = (spr + kChunkGroups - 1) / kChunkGroups;
+    const int G = gridDim.x;
+    const int nb = __builtin_amdgcn_readfirstlane(blockIdx.x < ntiles ? (ntiles - 1 - blockIdx.x) / G + 1 : 0);  // <= TB
     const __amdgpu_buffer_rsrc_t rx = rsrc(x, (unsigned)M * (unsigned)K * 2u);
-    const __amdgpu_buffer_rsrc_t rW = rsrc(W, (unsigned)N * (unsigned)wpr * 4u);
-    const __amdgpu_buffer_rsrc_t rS = rsrc(S, (unsigned)N * (unsigned)spr * 2u);
 
-    u4v wb[P][kGPW];
-    uint16_t sb[P][kGPW];
-    // unit u of a batch = (chunk u / nb, tile u % nb); units past the batch load nothing
-    auto issue = [&](int tb0, int nb, int u, u4v (&w)[kGPW], uint16_t (&s)[kGPW]) {
-        const int c = u / nb, i = u - c * nb;
-        const int row = (blockIdx.x + (tb0 + i) * gridDim.x) * 16 + n;
-        const bool rok = c < nchunk && row < N;
+    // lane t resolves tile slot t (matrix, first row) with vector selects; the results are
+    // then read into scalar registers, so every wave holds them at the cost of a few readlanes
+    SmTile tl[TB];
+    {
+        const int tile = blockIdx.x + lane * G;
+        const int m1 = set.count > 1 && tile >= set.tile_end[0], m2 = set.count > 2 && tile >= set.tile_end[1],
+                  m3 = set.count > 3 && tile >= set.tile_end[2];
+        auto sel = [&](auto a0, auto a1, auto a2, auto a3) { return m3 ? a3 : m2 ? a2 : m1 ? a1 : a0; };
+        const int row0 = (tile - sel(0, set.tile_end[0], set.tile_end[1], set.tile_end[2])) * 16;
+        const int N = lane < nb ? sel(set.N[0], set.N[1], set.N[2], set.N[3]) : 0;
+        const unsigned long long W = (unsigned long long)sel(set.W[0], set.W[1], set.W[2], set.W[3]);
+        const unsigned long long S = (unsigned long long)sel(set.S[0], set.S[1], set.S[2], set.S[3]);
+        const unsigned long long Y = (unsigned long long)sel(set.y[0], set.y[1], set.y[2], set.y[3]);
+        auto rl = [](unsigned long long v, int t) {       // readlane gives an int: no sign extension
+            const unsigned lo = (unsigned)__builtin_amdgcn_readlane((unsigned)v, t);
+            const unsigned hi = (unsigned)__builtin_amdgcn_readlane((unsigned)(v >> 32), t);
+            return ((unsigned long long)hi << 32) | lo;
+        };
 #pragma unroll
-        for (int q = 0; q < kGPW; ++q) {
-            const int grp = (c * kChunkWords + wave * kWPW) / 4 + q;
-            const bool ok = rok && grp < spr;
-            w[q] = __builtin_amdgcn_raw_buffer_load_b128(rW, ok ? ((unsigned)row * wpr + 4u * grp) * 4u : kOob,
-                                                        0, kNT);
-            s[q] = __builtin_amdgcn_raw_buffer_load_b16(rS, ok ? ((unsigned)row * spr + grp) * 2u : kOob, 0, 0);
-        }
+        for (int t = 0; t < TB; ++t)
+            tl[t] = SmTile{reinterpret_cast<const uint32_t *>(rl(W, t)), reinterpret_cast<const uint16_t *>(rl(S, t)),
+                           reinterpret_cast<uint16_t *>(rl(Y, t)), __builtin_amdgcn_readlane(row0, t),
+                           __builtin_amdgcn_readlane(N, t)};
+    }
+    SmSlot ring[D][TB];
+    // No selects here (the compiler turns them into branches that wait on loads in flight):
+    // rows at or past N fall outside the buffer range and load zeros, and a group past K (or a
+    // refill past the last chunk) reloads the row's last group, which meets x = 0.
+    auto issue = [&](const SmTile &T, int c, SmSlot &sl) {
+        const unsigned row = (unsigned)(T.row0 + n);
+        const unsigned gb = (unsigned)min(c * kChunkGroups + 4 * wave + b, spr - 1);
+        const __amdgpu_buffer_rsrc_t rW = rsrc(T.W, (unsigned)T.N * (unsigned)wpr * 4u);
+        const __amdgpu_buffer_rsrc_t rS = rsrc(T.S, (unsigned)T.N * (unsigned)spr * 2u);
+        sl.w = __builtin_amdgcn_raw_buffer_load_b128(rW, (row * (unsigned)wpr + 4u * gb) * 4u, 0, kNT);
+        sl.s = __builtin_amdgcn_raw_buffer_load_b16(rS, (row * (unsigned)spr + gb) * 2u, 0, 0);
     };
+#pragma unroll
+    for (int d = 0; d < D; ++d)
+#pragma unroll
+        for (int t = 0; t < TB; ++t) issue(tl[t], d, ring[d][t]);
+    // thread t's share of a chunk: 8 k of every token row; rows past M are outside the buffer
+    // range, and k past K starts from an out-of-range base, so both load zeros
+    u4v xr[16];
+    auto fetch_x = [&](int c) {
+        const unsigned kc = (unsigned)(c * kChunkK) + 8u * threadIdx.x;
+        const unsigned base = kc < (unsigned)K ? kc * 2u : kOob;
+#pragma unroll
+        for (int m = 0; m < 16; ++m)
+            xr[m] = __builtin_amdgcn_raw_buffer_load_b128(rx, base + (unsigned)m * (unsigned)K * 2u, 0, 0);
+    };
+    fetch_x(0);
 
-    for (int tb0 = 0; tb0 < my_tiles; tb0 += TB) {
-        const int nb = my_tiles - tb0 < TB ? my_tiles - tb0 : TB;     // tiles in this batch
-        const int nunits = nchunk * nb;
+    float4v acc[TB];
 #pragma unroll
-        for (int p = 0; p < P; ++p) issue(tb0, nb, p, wb[p], sb[p]);
-        float4v acc[TB];
+    for (int t = 0; t < TB; ++t) acc[t] = float4v{0.f, 0.f, 0.f, 0.f};
+    half8 A[16];
+    for (int c0 = 0; c0 < nchunk; c0 += D) {
 #pragma unroll
-        for (int i = 0; i < TB; ++i) acc[i] = float4v{0.f, 0.f, 0.f, 0.f};
-        half8 A[kWPW];
-        for (int u0 = 0; u0 < nunits; u0 += P) {
+        for (int d = 0; d < D; ++d) {
+            const int c = c0 + d;
+            if (c >= nchunk) break;                   // uniform
+            // new chunk: stage x, start loading the next one, build this wave's A
+            if (c > 0) __syncthreads();               // every wave has its A of the last chunk
 #pragma unroll
-            for (int p = 0; p < P; ++p) {
-                const int u = u0 + p;
-                if (u >= nunits) break;               // uniform
-                const int c = u / nb, i = u - c * nb;
-                if (i == 0) {                         // new chunk: this wave's A operands
+            for (int m = 0; m < 16; ++m) *reinterpret_cast<u4v *>(xs + m * kXRow + 8 * threadIdx.x) = xr[m];
+            if (nchunk > 1) fetch_x(c + 1);           // uniform
+            __syncthreads();
+            const uint16_t *xa = xs + n * kXRow + 128 * (4 * wave + b);
 #pragma unroll
-                    for (int k = 0; k < kWPW; ++k) {
-                        const int j = c * kChunkWords + wave * kWPW + k;   // word index
-                        const bool ok = n < M && j < wpr;
-                        const u4v v = __builtin_amdgcn_raw_buffer_load_b128(
-                            rx, ok ? ((unsigned)n * K + 32u * j + 8u * b) * 2u : kOob, 0, 0);
-                        A[k] = __builtin_bit_cast(half8, v);
-                    }
+            for (int j = 0; j < 4; ++j) {
+                const u4v l0 = *reinterpret_cast<const u4v *>(xa + 32 * j);
+                const u4v l1 = *reinterpret_cast<const u4v *>(xa + 32 * j + 8);
+                const u4v h0 = *reinterpret_cast<const u4v *>(xa + 32 * j + 16);
+                const u4v h1 = *reinterpret_cast<const u4v *>(xa + 32 * j + 24);
+                interleave(l0, h0, A[4 * j + 0], A[4 * j + 1]);
+                interleave(l1, h1, A[4 * j + 2], A[4 * j + 3]);
+            }
+#pragma unroll
+            for (int t = 0; t < TB; ++t) {
+                SmSlot &sl = ring[d][t];
+                const uint32_t sbits = sl.s & 0xFFFFu;
+                const uint32_t s2abs = (sbits & 0x7FFFu) * 0x00010001u;
+                const uint32_t flip = (sbits & 0x8000u) ? 0u : 0xFFFFFFFFu;   // bit 1: negative product
+                const u4v w = sl.w;
+#pragma unroll
+                for (int j = 0; j < 4; ++j) {
+                    const uint32_t nw = w[j] ^ flip;
+                    acc[t] = __builtin_amdgcn_mfma_f32_16x16x32_f16(A[4 * j + 0], expand_q<0>(nw, s2abs), acc[t], 0, 0, 0);
+                    acc[t] = __builtin_amdgcn_mfma_f32_16x16x32_f16(A[4 * j + 1], expand_q<1>(nw, s2abs), acc[t], 0, 0, 0);
+                    acc[t] = __builtin_amdgcn_mfma_f32_16x16x32_f16(A[4 * j + 2], expand_q<2>(nw, s2abs), acc[t], 0, 0, 0);
+                    acc[t] = __builtin_amdgcn_mfma_f32_16x16x32_f16(A[4 * j + 3], expand_q<3>(nw, s2abs), acc[t], 0, 0, 0);
                 }
-                float4v a = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-                for (int q = 0; q < kGPW; ++q) {
-                    const uint32_t sbits = sb[p][q];
-                    const uint32_t sabs = sbits & 0x7FFFu;
-                    const uint32_t s2abs = sabs | (sabs << 16);
-                    const uint32_t flip = (sbits & 0x8000u) ? 0u : 0xFFFFFFFFu;   // nw = w ^ flip
-                    const u4v w = wb[p][q];
-                    a = __builtin_amdgcn_mfma_f32_16x16x32_f16(A[4 * q + 0], expand_byte(w.x ^ flip, b, s2abs), a, 0, 0, 0);
-                    a = __builtin_amdgcn_mfma_f32_16x16x32_f16(A[4 * q + 1], expand_byte(w.y ^ flip, b, s2abs), a, 0, 0, 0);
-                    a = __builtin_amdgcn_mfma_f32_16x16x32_f16(A[4 * q + 2], expand_byte(w.z ^ flip, b, s2abs), a, 0, 0, 0);
-                    a = __builtin_amdgcn_mfma_f32_16x16x32_f16(A[4 * q + 3], expand_byte(w.w ^ flip, b, s2abs), a, 0, 0, 0);
-                }
-                issue(tb0, nb, u + P, wb[p], sb[p]);
-#pragma unroll
-                for (int t = 0; t < TB; ++t)
-                    if (t == i) acc[t] += a;
+                if (nchunk > D) issue(tl[t], c + D, sl);   // uniform
             }
         }
-        // merge the four waves' K-slices; D layout: lane (n, b) holds tokens 4b..4b+3 of row n
-        for (int t = 0; t < nb; ++t)
+    }
+    // merge the waves' K-slices.  D layout: lane (n, b) holds tokens 4b..4b+3 of row n.  Each
+    // wave stores its tiles whole (conflict-free 16-byte stores); reader q of a tile takes
+    // row (q >> 2) & 15, token 4 (q >> 6) + (q & 3), so a wave's reads hit 64 distinct banks
+    // and its fp16 stores form 32-byte runs.
+    __syncthreads();                                  // the staged x is dead from here
 #pragma unroll
-            for (int r = 0; r < 4; ++r) red[((t * 16 + n) * 16 + 4 * b + r) * kWaves + wave] = acc[t][r];
-        __syncthreads();
-        for (int e = threadIdx.x; e < nb * 256; e += 64 * kWaves) {
-            const int t = e >> 8, rr = (e >> 4) & 15, m = e & 15;
-            const int row = (blockIdx.x + (tb0 + t) * gridDim.x) * 16 + rr;
-            const float4v p0 = *reinterpret_cast<const float4v *>(red + (size_t)e * kWaves);
-            const float4v p1 = *reinterpret_cast<const float4v *>(red + (size_t)e * kWaves + 4);
-            const float tot = ((p0[0] + p0[1]) + (p0[2] + p0[3])) + ((p1[0] + p1[1]) + (p1[2] + p1[3]));
-            if (m < M && row < N) y[(size_t)m * N + row] = f2h_rne(tot);
-        }
-        __syncthreads();
+    for (int t = 0; t < TB; ++t)
+        *reinterpret_cast<float4v *>(red + ((t * kWaves + wave) * 64 + lane) * 4) = acc[t];
+    __syncthreads();
+    const int q = threadIdx.x & 255, rr = (q >> 2) & 15, m = 4 * (q >> 6) + (q & 3);
+#pragma unroll
+    for (int t0 = 0; t0 < TB; t0 += 2) {
+        const int t = t0 + (threadIdx.x >> 8);
+        if (t >= TB) break;                           // uniform per wave
+        const float *src = red + (t * kWaves * 64 + rr + 16 * (q >> 6)) * 4 + (q & 3);
+        float v[kWaves];
+#pragma unroll
+        for (int w = 0; w < kWaves; ++w) v[w] = src[w * 256];
+        const float tot = ((v[0] + v[1]) + (v[2] + v[3])) + ((v[4] + v[5]) + (v[6] + v[7]));
+        const SmTile &T = (threadIdx.x >> 8) ? tl[t0 + 1 < TB ? t0 + 1 : t0] : tl[t0];
+        const int row = T.row0 + rr;
+        if (m < M && row < T.N) T.y[(size_t)m * T.N + row] = f2h_rne(tot);
     }
 }
 
-template <int P, int TB>
-hipError_t launch_sm(const uint16_t *x, const uint32_t *W, const uint16_t *S, uint16_t *y, int M, int K,
-                     int N, hipStream_t st)
+template <int TB, int D>
+hipError_t launch_sm(const uint16_t *x, const MxSet &set, int M, int K, int tiles, hipStream_t st)
 {
-    const int tiles = (N + 15) / 16;
-    const int grid = tiles < 256 ? tiles : 256;
-    hipLaunchKernelGGL((gemv_smallm_kernel<P, TB>), dim3(grid), dim3(64 * kWaves), 0, st, x, W, S, y, M, K, N,
+    static_assert(TB * 256 * kWaves * 4 <= kXBytes, "merge table fits the staging area");
+    static const hipError_t attr = hipFuncSetAttribute(reinterpret_cast<const void *>(&gemv_smallm_kernel<TB, D>),
+                                                       hipFuncAttributeMaxDynamicSharedMemorySize, kXBytes);
+    if (attr != hipSuccess) return attr;
+    const int grid = (tiles + TB - 1) / TB;
+    hipLaunchKernelGGL((gemv_smallm_kernel<TB, D>), dim3(grid), dim3(64 * kWaves), kXBytes, st, x, set, M, K,
                        tiles);
     return hipGetLastError();
 }
 
 }  // namespace
 
-hipError_t launch_gemv_smallm(const uint16_t *x, const uint32_t *W, const uint16_t *S, uint16_t *y, int M,
-                              int K, int N, hipStream_t st)
+hipError_t launch_gemv_smallm(const uint16_t *x, const MxSet &set0, int M, int K, hipStream_t st)
 {
-    return launch_sm<3, 4>(x, W, S, y, M, K, N, st);
+    MxSet set = set0;
+    int tiles = 0;
+    for (int i = 0; i < set.count; ++i) {
+        tiles += (set.N[i] + 15) / 16;
+        set.tile_end[i] = tiles;
+    }
+    // TB tiles per workgroup: as few as fill the 256 CUs in one round, at most 6 (the grid
+    // grows past 256 beyond that); with several K chunks, more chunks per tile are in flight
+    const int per = (tiles + 255) / 256, nchunk = (K + kChunkK - 1) / kChunkK;
+    if (nchunk == 1) {
+        if (per <= 2) return launch_sm<2, 1>(x, set, M, K, tiles, st);
+        if (per <= 4) return launch_sm<4, 1>(x, set, M, K, tiles, st);
+        return launch_sm<6, 1>(x, set, M, K, tiles, st);
+    }
+    if (per <= 1) return launch_sm<1, 4>(x, set, M, K, tiles, st);
+    if (per <= 2) return launch_sm<2, 3>(x, set, M, K, tiles, st);
+    return launch_sm<4, 2>(x, set, M, K, tiles, st);
 }
 
 }  // namespace bin1

@@ -64,8 +64,8 @@ hipError_t launch_gemv_mx(const uint16_t *x, const MxSet &set, int K, hipStream_
 hipError_t launch_gemv(const uint16_t *x, const uint32_t *W, const uint16_t *S, uint16_t *y,
                        int M, int K, int N, hipStream_t st);
 // Small-batch product (2 <= M <= 16) on fp16 MFMA with the tokens as the A rows.
-hipError_t launch_gemv_smallm(const uint16_t *x, const uint32_t *W, const uint16_t *S, uint16_t *y, int M,
-                              int K, int N, hipStream_t st);
+// 2 <= M <= 16 tokens, 1..4 products sharing x (tile_end filled in by the launcher).
+hipError_t launch_gemv_smallm(const uint16_t *x, const MxSet &set, int M, int K, hipStream_t st);
 hipError_t launch_prefill(const uint16_t *x, const uint32_t *W, const uint16_t *S, uint16_t *y,
                           int M, int K, int N, hipStream_t st);
 hipError_t launch_pm1(const uint32_t *A, const uint32_t *W, int32_t *y, int M, int K, int N,

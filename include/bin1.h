@@ -78,7 +78,7 @@ int bin1_gemv(const void *x, const uint32_t *Wbits, const void *scales, void *y,
 
 /* Same-input fusion: `count` (1..4) products that read the same activations x [M][K]
  * (such as the q/k/v or gate/up projections of one layer), enqueued as one launch when
- * M == 1.  Wbits, scales, y and N are HOST arrays of `count` entries; entry i describes
+ * M <= 16.  Wbits, scales, y and N are HOST arrays of `count` entries; entry i describes
  * matrix i exactly as in bin1_gemv (Wbits[i] [N[i]][K/32], scales[i] [N[i]][K/128],
  * y[i] [M][N[i]]).  Every y[i] must be disjoint from every input and from the other
  * outputs.  Results equal `count` separate bin1_gemv calls. */

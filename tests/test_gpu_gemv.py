@@ -116,7 +116,9 @@ def test_output_is_fully_overwritten_and_out_argument(orc, dev):
 
 @pytest.mark.parametrize("M,K,Ns", [(1, 4096, (4096, 1024, 1024)), (1, 4096, (12288, 12288)),
                                     (1, 5120, (5120, 5120, 5120)), (1, 384, (7, 33, 100, 16)),
-                                    (1, 17408, (5120,)), (2, 512, (64, 65))])
+                                    (1, 17408, (5120,)), (2, 512, (64, 65)),
+                                    (16, 4096, (12288, 12288)), (5, 384, (7, 33, 100, 16)),
+                                    (16, 4352, (300, 1000, 17)), (9, 12288, (4096, 1500))])
 def test_gemv_group_matches_oracle(orc, dev, M, K, Ns):
     """Same-input fusion (q/k/v, gate/up): one launch, each output checked against the oracle."""
     r = synth.rng_for(0, synth.WL_TEST, 7000 + K + sum(Ns) + M)
@@ -132,6 +134,20 @@ def test_gemv_group_matches_oracle(orc, dev, M, K, Ns):
         rows = sample_rows(r, N, k=128) if N > 2048 else np.arange(N)
         ref, nrm = orc.gemv_rows(x, W, S, rows)
         assert norm_err(y.float().cpu().numpy()[:, rows], ref, nrm) <= TOL
+
+
+@pytest.mark.parametrize("M", [1, 3, 16])
+def test_gemv_group_equals_separate_calls(dev, M):
+    """One grouped launch gives bit-identical outputs to one call per matrix."""
+    r = synth.rng_for(0, synth.WL_TEST, 7300 + M)
+    K, Ns = 4352, (300, 1000, 17, 2048)
+    x = synth.activations(r, M, K)
+    xd = dev_tensors(dev, x)[0]
+    Wd = [dev_tensors(dev, W=synth.sign_words(r, n, K))[0] for n in Ns]
+    Sd = [dev_tensors(dev, S=synth.group_scales(r, n, K))[0] for n in Ns]
+    outs = b1.gemv_group(xd, Wd, Sd)
+    for W, S, y in zip(Wd, Sd, outs):
+        assert torch.equal(b1.gemv(xd, W, S), y)
 
 
 def test_gemv_repeated_calls_are_deterministic(dev):
