@@ -76,6 +76,10 @@ int check_product_host(const void *x, const void *W, const void *S, const void *
         return fail(BIN1_ERR_ALIGN, "x, Wbits, scales and y must be 16-byte aligned");
     const size_t xb = (size_t)M * K * 2, wb = (size_t)N * (K / 8), sb = (size_t)N * (K / 128) * 2,
                  yb = (size_t)M * N * 2;
+    // the kernels address rows with 24-bit products and buffers with 32-bit offsets
+    if (N >= (1 << 24) - 64 || xb >= (1ull << 31) || wb >= (1ull << 31) || yb >= (1ull << 31))
+        return fail(BIN1_ERR_SHAPE, "need N < 2^24 - 64 and x, Wbits, y each under 2 GiB (got M=%d K=%d N=%d)", M,
+                    K, N);
     if (overlap(y, yb, x, xb) || overlap(y, yb, W, wb) || overlap(y, yb, S, sb))
         return fail(BIN1_ERR_ALIAS, "y overlaps an input");
     return BIN1_OK;

@@ -92,15 +92,38 @@ __device__ __forceinline__ void limbs_build(int K, uint8_t *lds, const XLoad<XT>
     }
 }
 
-// Locate tile `tile` (16*R rows) of the matrix set: matrix index and first row.
+// The workgroup's tile table, one tile per lane: lane i describes the workgroup's i-th tile
+// (16*R rows) -- its matrix's weights, scales, output and row count, and its first row --
+// computed with vector selects once per kernel.  Uniform reads (readlane with a scalar lane
+// index) put a tile's entry in scalar registers; indexing the kernel argument by a computed
+// matrix index instead costs a scalar-memory round trip per tile.
+struct TileTab {
+    unsigned long long W, S, y;
+    int row0, N;
+};
+
 template <int R>
-__device__ __forceinline__ void locate(const MxSet &set, int tile, int &mi, int &row0)
+__device__ __forceinline__ TileTab tile_tab(const MxSet &set, int tile)
 {
-    mi = 0;
-#pragma unroll
-    for (int i = 0; i < kMaxMats - 1; ++i)
-        if (i + 1 < set.count && tile >= set.tile_end[i]) mi = i + 1;
-    row0 = (tile - (mi ? set.tile_end[mi - 1] : 0)) * 16 * R;
+    const int m1 = set.count > 1 && tile >= set.tile_end[0], m2 = set.count > 2 && tile >= set.tile_end[1],
+              m3 = set.count > 3 && tile >= set.tile_end[2];
+    auto sel = [&](auto a0, auto a1, auto a2, auto a3) { return m3 ? a3 : m2 ? a2 : m1 ? a1 : a0; };
+    TileTab t;
+    t.row0 = (tile - sel(0, set.tile_end[0], set.tile_end[1], set.tile_end[2])) * 16 * R;
+    t.N = sel(set.N[0], set.N[1], set.N[2], set.N[3]);
+    t.W = (unsigned long long)sel(set.W[0], set.W[1], set.W[2], set.W[3]);
+    t.S = (unsigned long long)sel(set.S[0], set.S[1], set.S[2], set.S[3]);
+    t.y = (unsigned long long)sel(set.y[0], set.y[1], set.y[2], set.y[3]);
+    return t;
+}
+
+__device__ __forceinline__ int lane_of(int v, int l) { return __builtin_amdgcn_readlane(v, l); }
+
+__device__ __forceinline__ unsigned long long lane_of(unsigned long long v, int l)
+{
+    const unsigned lo = (unsigned)__builtin_amdgcn_readlane((unsigned)v, l);      // int result:
+    const unsigned hi = (unsigned)__builtin_amdgcn_readlane((unsigned)(v >> 32), l);   // no sign extension
+    return ((unsigned long long)hi << 32) | lo;
 }
 
 // One ring slot: for each 16-row block r and each of the wave's pairs, 32 bytes of weights
@@ -123,29 +146,35 @@ void gemv_mx_kernel(const uint16_t *__restrict__ x, MxSet set, int K, int ntiles
     const int n = lane & 15, g = lane >> 4;
     const int npair = (K + 1023) >> 10, nseg = 2 * npair;
     const int wpr = K >> 5, spr = K >> 7;
-    const int my_tiles = blockIdx.x < ntiles ? (ntiles - 1 - blockIdx.x) / gridDim.x + 1 : 0;
+    const int my_tiles = __builtin_amdgcn_readfirstlane(
+        blockIdx.x < ntiles ? (ntiles - 1 - blockIdx.x) / gridDim.x + 1 : 0);   // <= 64
+    const TileTab tab = tile_tab<R>(set, blockIdx.x + lane * gridDim.x);
 
     Slot<SP, R> ring[P];
 
     // Ring slot fill for the workgroup's it-th tile.  Slots past the last tile, rows past N
     // and groups past K get out-of-range offsets: zero data and zero scales, no traffic.
+    // Row offsets use 24-bit multiplies (rows < 2^24): a full 32-bit multiply-add becomes a
+    // 64-bit one whose unused high input may sit in a register a load is still filling, and
+    // the compiler then waits for every load in flight.
     auto issue = [&](int it, Slot<SP, R> &sl) {
         const bool live = it < my_tiles;
-        int mi, row0;
-        locate<R>(set, live ? blockIdx.x + it * gridDim.x : 0, mi, row0);
-        const int N = set.N[mi];
-        const __amdgpu_buffer_rsrc_t rW = rsrc(set.W[mi], (unsigned)N * (unsigned)wpr * 4u);
-        const __amdgpu_buffer_rsrc_t rS = rsrc(set.S[mi], (unsigned)N * (unsigned)spr * 2u);
+        const int L = it & 63;
+        const int row0 = lane_of(tab.row0, L), N = live ? lane_of(tab.N, L) : 0;
+        const __amdgpu_buffer_rsrc_t rW =
+            rsrc(reinterpret_cast<const void *>(lane_of(tab.W, L)), (unsigned)N * (unsigned)wpr * 4u);
+        const __amdgpu_buffer_rsrc_t rS =
+            rsrc(reinterpret_cast<const void *>(lane_of(tab.S, L)), (unsigned)N * (unsigned)spr * 2u);
 #pragma unroll
         for (int r = 0; r < R; ++r) {
             const int row = row0 + 16 * r + n;
-            const bool rok = live && row < N;
+            const bool rok = row < N;
 #pragma unroll
             for (int q = 0; q < SP; ++q) {
                 const int gam = 8 * (wave + 4 * q) + 2 * g;     // this lane's first group
                 const bool ok0 = rok && gam < spr, ok1 = rok && gam + 1 < spr;
-                const unsigned ow = ((unsigned)row * wpr + 4u * gam) * 4u;
-                const unsigned os = ((unsigned)row * spr + gam) * 2u;
+                const unsigned ow = (__umul24((unsigned)row, (unsigned)wpr) + 4u * gam) * 4u;
+                const unsigned os = (__umul24((unsigned)row, (unsigned)spr) + gam) * 2u;
                 sl.w[r][q][0] = __builtin_amdgcn_raw_buffer_load_b128(rW, ok0 ? ow : kOob, 0, kNT);
                 sl.w[r][q][1] = __builtin_amdgcn_raw_buffer_load_b128(rW, ok1 ? ow + 16u : kOob, 0, kNT);
                 if (ODD) {
@@ -239,12 +268,12 @@ done:
     // Merge: thread t finishes rows t, t+256, ... of the workgroup's tiles in order.
     for (int e = tid; e < my_tiles * 16 * R; e += 256) {
         const int it = e / (16 * R), j = e - it * (16 * R);
-        int mi, row0;
-        locate<R>(set, blockIdx.x + it * gridDim.x, mi, row0);
-        const int row = row0 + j;
+        const int row = __shfl(tab.row0, it, kWave) + j, N = __shfl(tab.N, it, kWave);
+        const unsigned long long yp = ((unsigned long long)(unsigned)__shfl((unsigned)(tab.y >> 32), it, kWave) << 32) |
+                                      (unsigned)__shfl((unsigned)tab.y, it, kWave);
         const float4v pr4 = *reinterpret_cast<const float4v *>(red + e * 4);
         const float tot = (pr4[0] + pr4[1]) + (pr4[2] + pr4[3]);
-        if (row < set.N[mi]) set.y[mi][row] = f2h_rne(tot);
+        if (row < N) reinterpret_cast<uint16_t *>(yp)[row] = f2h_rne(tot);
     }
 }
 
@@ -259,6 +288,7 @@ constexpr size_t shm_bytes(int K, int rows_per_wg)
 template <int SP, int P, int R, bool ODD>
 hipError_t launch_mx(const uint16_t *x, const MxSet &set0, int K, hipStream_t st)
 {
+    static_assert(kMaxTileRows / (16 * R) <= 64, "a workgroup's tiles fit the one-per-lane tile table");
     static const hipError_t attr = hipFuncSetAttribute(
         reinterpret_cast<const void *>(&gemv_mx_kernel<SP, P, R, ODD>),
         hipFuncAttributeMaxDynamicSharedMemorySize, (int)shm_bytes(kMaxPairs * 1024, kMaxTileRows));

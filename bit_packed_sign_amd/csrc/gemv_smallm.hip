@@ -83,7 +83,9 @@ struct SmTile {     // one tile of the workgroup, resolved once
 // every tile are in flight; a wave's A operands are built once per chunk, and the next chunk
 // of x is already loading (into registers) while the current one is used.  The waves' partial
 // tiles are merged through LDS at the end.  Tile slots past the workgroup's tiles compute on
-// zeros and are never stored.
+// zeros and are never stored.  D = 0 is the one-chunk case (K <= 4096): no prefetch, no
+// refills.  Loads are never issued under a branch (the compiler would then wait for every
+// load in flight where the paths meet).
 template <int TB, int D>
 __global__ __launch_bounds__(64 * kWaves) __attribute__((amdgpu_waves_per_eu(2, 2)))
 void gemv_smallm_kernel(const uint16_t *__restrict__ x, MxSet set, int M, int K, int ntiles)
@@ -123,22 +125,22 @@ void gemv_smallm_kernel(const uint16_t *__restrict__ x, MxSet set, int M, int K,
                            reinterpret_cast<uint16_t *>(rl(Y, t)), __builtin_amdgcn_readlane(row0, t),
                            __builtin_amdgcn_readlane(N, t)};
     }
-    SmSlot ring[D][TB];
+    constexpr int DS = D > 0 ? D : 1;
+    SmSlot ring[DS][TB];
     // No selects here (the compiler turns them into branches that wait on loads in flight):
     // rows at or past N fall outside the buffer range and load zeros, and a group past K (or a
     // refill past the last chunk) reloads the row's last group, which meets x = 0.
     auto issue = [&](const SmTile &T, int c, SmSlot &sl) {
         const unsigned row = (unsigned)(T.row0 + n);
         const unsigned gb = (unsigned)min(c * kChunkGroups + 4 * wave + b, spr - 1);
-        const __amdgpu_buffer_rsrc_t rW = rsrc(T.W, (unsigned)T.N * (unsigned)wpr * 4u);
-        const __amdgpu_buffer_rsrc_t rS = rsrc(T.S, (unsigned)T.N * (unsigned)spr * 2u);
-        sl.w = __builtin_amdgcn_raw_buffer_load_b128(rW, (row * (unsigned)wpr + 4u * gb) * 4u, 0, kNT);
-        sl.s = __builtin_amdgcn_raw_buffer_load_b16(rS, (row * (unsigned)spr + gb) * 2u, 0, 0);
+        const unsigned live = c < nchunk ? (unsigned)T.N : 0u;       // past the last chunk: no range
+        const __amdgpu_buffer_rsrc_t rW = rsrc(T.W, live * (unsigned)wpr * 4u);
+        const __amdgpu_buffer_rsrc_t rS = rsrc(T.S, live * (unsigned)spr * 2u);
+        // 24-bit row products (rows < 2^24): a full 32-bit multiply-add becomes a 64-bit one
+        // whose unused high input can alias a register a load is filling (a needless wait)
+        sl.w = __builtin_amdgcn_raw_buffer_load_b128(rW, (__umul24(row, (unsigned)wpr) + 4u * gb) * 4u, 0, kNT);
+        sl.s = __builtin_amdgcn_raw_buffer_load_b16(rS, (__umul24(row, (unsigned)spr) + gb) * 2u, 0, 0);
     };
-#pragma unroll
-    for (int d = 0; d < D; ++d)
-#pragma unroll
-        for (int t = 0; t < TB; ++t) issue(tl[t], d, ring[d][t]);
     // thread t's share of a chunk: 8 k of every token row; rows past M are outside the buffer
     // range, and k past K starts from an out-of-range base, so both load zeros
     u4v xr[16];
@@ -149,23 +151,35 @@ void gemv_smallm_kernel(const uint16_t *__restrict__ x, MxSet set, int M, int K,
         for (int m = 0; m < 16; ++m)
             xr[m] = __builtin_amdgcn_raw_buffer_load_b128(rx, base + (unsigned)m * (unsigned)K * 2u, 0, 0);
     };
-    fetch_x(0);
+    fetch_x(0);                                       // first: staging it waits on nothing else
+#pragma unroll
+    for (int d = 0; d < DS; ++d)
+#pragma unroll
+        for (int t = 0; t < TB; ++t) issue(tl[t], d, ring[d][t]);
 
     float4v acc[TB];
 #pragma unroll
     for (int t = 0; t < TB; ++t) acc[t] = float4v{0.f, 0.f, 0.f, 0.f};
+    // stage chunk c's x (in xr) into LDS and start loading chunk c + 1 (past K: zeros, no
+    // traffic).  Staging comes last in a chunk, so its wait is for loads issued before that
+    // chunk's refills.
+    auto stage = [&](int c) {
+#pragma unroll
+        for (int m = 0; m < 16; ++m) *reinterpret_cast<u4v *>(xs + m * kXRow + 8 * threadIdx.x) = xr[m];
+        if (D > 0) fetch_x(c + 1);
+        __syncthreads();
+    };
+    stage(0);
     half8 A[16];
-    for (int c0 = 0; c0 < nchunk; c0 += D) {
+    // D = 0 has exactly one chunk: a literal trip count of one, so that nothing of the tile
+    // loop (the sign expansions) is hoisted out of it and kept live for every tile at once
+    const int nloop = D > 0 ? nchunk : 1;
+    for (int c0 = 0; c0 < nloop; c0 += DS) {
 #pragma unroll
-        for (int d = 0; d < D; ++d) {
+        for (int d = 0; d < DS; ++d) {
             const int c = c0 + d;
-            if (c >= nchunk) break;                   // uniform
-            // new chunk: stage x, start loading the next one, build this wave's A
-            if (c > 0) __syncthreads();               // every wave has its A of the last chunk
-#pragma unroll
-            for (int m = 0; m < 16; ++m) *reinterpret_cast<u4v *>(xs + m * kXRow + 8 * threadIdx.x) = xr[m];
-            if (nchunk > 1) fetch_x(c + 1);           // uniform
-            __syncthreads();
+            if (c >= nloop) break;                    // uniform
+            // this wave's A operands for chunk c
             const uint16_t *xa = xs + n * kXRow + 128 * (4 * wave + b);
 #pragma unroll
             for (int j = 0; j < 4; ++j) {
@@ -191,7 +205,12 @@ void gemv_smallm_kernel(const uint16_t *__restrict__ x, MxSet set, int M, int K,
                     acc[t] = __builtin_amdgcn_mfma_f32_16x16x32_f16(A[4 * j + 2], expand_q<2>(nw, s2abs), acc[t], 0, 0, 0);
                     acc[t] = __builtin_amdgcn_mfma_f32_16x16x32_f16(A[4 * j + 3], expand_q<3>(nw, s2abs), acc[t], 0, 0, 0);
                 }
-                if (nchunk > D) issue(tl[t], c + D, sl);   // uniform
+                if (D > 0) issue(tl[t], c + D, sl);       // past the last chunk: no traffic
+                __builtin_amdgcn_sched_barrier(0);        // tiles one after another: bounded registers
+            }
+            if (D > 0) {                              // compile-time
+                __syncthreads();                      // every wave has its A of chunk c
+                stage(c + 1);
             }
         }
     }
@@ -247,9 +266,9 @@ hipError_t launch_gemv_smallm(const uint16_t *x, const MxSet &set0, int M, int K
     // grows past 256 beyond that); with several K chunks, more chunks per tile are in flight
     const int per = (tiles + 255) / 256, nchunk = (K + kChunkK - 1) / kChunkK;
     if (nchunk == 1) {
-        if (per <= 2) return launch_sm<2, 1>(x, set, M, K, tiles, st);
-        if (per <= 4) return launch_sm<4, 1>(x, set, M, K, tiles, st);
-        return launch_sm<6, 1>(x, set, M, K, tiles, st);
+        if (per <= 2) return launch_sm<2, 0>(x, set, M, K, tiles, st);
+        if (per <= 4) return launch_sm<4, 0>(x, set, M, K, tiles, st);
+        return launch_sm<6, 0>(x, set, M, K, tiles, st);
     }
     if (per <= 1) return launch_sm<1, 4>(x, set, M, K, tiles, st);
     if (per <= 2) return launch_sm<2, 3>(x, set, M, K, tiles, st);

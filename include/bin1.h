@@ -41,7 +41,8 @@
  *  - Validation happens before anything is enqueued; on any error nothing is enqueued
  *    and the outputs are untouched.
  *  - Requirements: M >= 1, N >= 1, K >= 128, K % 128 == 0; x, Wbits, scales, y, Abits
- *    16-byte aligned; y must not overlap any input.
+ *    16-byte aligned; y must not overlap any input.  Products also need N < 2^24 - 64
+ *    and x, Wbits and y each under 2 GiB (else BIN1_ERR_SHAPE).
  *  - Device-side faults surface at the caller's next synchronisation, as with any
  *    HIP kernel.  BIN1_ERR_LAUNCH carries the HIP error text in bin1_last_error().
  *  - The library is stateless apart from a thread-local error string: calls are

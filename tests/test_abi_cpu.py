@@ -63,6 +63,9 @@ def test_product_validation(L, fn):
     assert f(FAKE, FAKE, FAKE, FAKE * 2, 1, 100, 1, None) == -2
     assert f(FAKE, FAKE, FAKE, FAKE * 2, 1, 0, 1, None) == -2
     assert f(FAKE, FAKE, FAKE, FAKE * 2, 1, 128, 0, None) == -2
+    assert f(FAKE, FAKE, FAKE, FAKE * 2, 1, 128, 1 << 24, None) == -2            # rows past 24-bit
+    assert f(FAKE, FAKE, FAKE, FAKE * 2, 1, 1 << 20, 1 << 14, None) == -2        # Wbits of 2 GiB
+    assert b"2 GiB" in L.bin1_last_error()
     assert f(FAKE + 2, FAKE * 3, FAKE * 4, FAKE * 5, 1, 128, 1, None) == -3
     # y overlapping x (x occupies M*K*2 bytes from FAKE)
     assert f(FAKE, FAKE * 8, FAKE * 9, FAKE + 128, 1, 128, 1, None) == -4
