@@ -22,6 +22,16 @@ __device__ __forceinline__ uint16_t f2h_rne(float f) {
     return __builtin_bit_cast(uint16_t, v);
 }
 
+// a * b for a, b < 2^24, as one v_mul_u32_u24.  Written as an instruction because the
+// compiler fuses a plain (masked) 24-bit product with a following add into a 64-bit
+// multiply-add, whose unused high input it may place in a register that a buffer load is
+// still filling; the wait-count pass then drains every load in flight at that point.
+__device__ __forceinline__ unsigned mul24(unsigned a, unsigned b) {
+    unsigned r;
+    asm("v_mul_u32_u24 %0, %1, %2" : "=v"(r) : "v"(a), "v"(b));
+    return r;
+}
+
 // Sum over the 64 lanes of a wave (butterfly; every lane ends with the total).
 __device__ __forceinline__ float wave_sum(float v) {
 #pragma unroll

@@ -181,8 +181,9 @@ void gemv_chain_kernel(ChainHeader *hdr, int *done, const ChainStage *table, int
             const int row = d.row0 + 16 * t + n;
             const int gam = 8 * (wave + 4 * p) + 2 * g;
             const bool ok = d.live && t < d.rt && row < d.N && gam < spr;   // K % 256 == 0: gam+1 valid
-            const unsigned ow = ((unsigned)row * wpr + 4u * gam) * 4u;
-            const unsigned os = ((unsigned)row * spr + gam) * 2u;
+            // mul24 row products (rows < 2^24) keep the wait counts exact
+            const unsigned ow = (mul24((unsigned)row, (unsigned)wpr) + 4u * gam) * 4u;
+            const unsigned os = (mul24((unsigned)row, (unsigned)spr) + gam) * 2u;
             sl.w[b][0] = __builtin_amdgcn_raw_buffer_load_b128(rW, ok ? ow : kOob, 0, kNT);
             sl.w[b][1] = __builtin_amdgcn_raw_buffer_load_b128(rW, ok ? ow + 16u : kOob, 0, kNT);
             sl.s[b] = __builtin_amdgcn_raw_buffer_load_b32(rS, ok ? os : kOob, 0, 0);

@@ -154,9 +154,7 @@ void gemv_mx_kernel(const uint16_t *__restrict__ x, MxSet set, int K, int ntiles
 
     // Ring slot fill for the workgroup's it-th tile.  Slots past the last tile, rows past N
     // and groups past K get out-of-range offsets: zero data and zero scales, no traffic.
-    // Row offsets use 24-bit multiplies (rows < 2^24): a full 32-bit multiply-add becomes a
-    // 64-bit one whose unused high input may sit in a register a load is still filling, and
-    // the compiler then waits for every load in flight.
+    // Row offsets use mul24 (rows < 2^24), which keeps the wait counts exact.
     auto issue = [&](int it, Slot<SP, R> &sl) {
         const bool live = it < my_tiles;
         const int L = it & 63;
@@ -173,8 +171,8 @@ void gemv_mx_kernel(const uint16_t *__restrict__ x, MxSet set, int K, int ntiles
             for (int q = 0; q < SP; ++q) {
                 const int gam = 8 * (wave + 4 * q) + 2 * g;     // this lane's first group
                 const bool ok0 = rok && gam < spr, ok1 = rok && gam + 1 < spr;
-                const unsigned ow = (__umul24((unsigned)row, (unsigned)wpr) + 4u * gam) * 4u;
-                const unsigned os = (__umul24((unsigned)row, (unsigned)spr) + gam) * 2u;
+                const unsigned ow = (mul24((unsigned)row, (unsigned)wpr) + 4u * gam) * 4u;
+                const unsigned os = (mul24((unsigned)row, (unsigned)spr) + gam) * 2u;
                 sl.w[r][q][0] = __builtin_amdgcn_raw_buffer_load_b128(rW, ok0 ? ow : kOob, 0, kNT);
                 sl.w[r][q][1] = __builtin_amdgcn_raw_buffer_load_b128(rW, ok1 ? ow + 16u : kOob, 0, kNT);
                 if (ODD) {

@@ -136,10 +136,9 @@ void gemv_smallm_kernel(const uint16_t *__restrict__ x, MxSet set, int M, int K,
         const unsigned live = c < nchunk ? (unsigned)T.N : 0u;       // past the last chunk: no range
         const __amdgpu_buffer_rsrc_t rW = rsrc(T.W, live * (unsigned)wpr * 4u);
         const __amdgpu_buffer_rsrc_t rS = rsrc(T.S, live * (unsigned)spr * 2u);
-        // 24-bit row products (rows < 2^24): a full 32-bit multiply-add becomes a 64-bit one
-        // whose unused high input can alias a register a load is filling (a needless wait)
-        sl.w = __builtin_amdgcn_raw_buffer_load_b128(rW, (__umul24(row, (unsigned)wpr) + 4u * gb) * 4u, 0, kNT);
-        sl.s = __builtin_amdgcn_raw_buffer_load_b16(rS, (__umul24(row, (unsigned)spr) + gb) * 2u, 0, 0);
+        // mul24 row products (rows < 2^24) keep the wait counts exact
+        sl.w = __builtin_amdgcn_raw_buffer_load_b128(rW, (mul24(row, (unsigned)wpr) + 4u * gb) * 4u, 0, kNT);
+        sl.s = __builtin_amdgcn_raw_buffer_load_b16(rS, (mul24(row, (unsigned)spr) + gb) * 2u, 0, 0);
     };
     // thread t's share of a chunk: 8 k of every token row; rows past M are outside the buffer
     // range, and k past K starts from an out-of-range base, so both load zeros
