@@ -51,14 +51,9 @@ struct XLoad {
 __device__ __forceinline__ int nseg_of(int K) { return 2 * ((K + 1023) >> 10); }
 
 template <int XT>
-__device__ __forceinline__ void limbs_init(int K, uint8_t *lds, const uint16_t *__restrict__ x, XLoad<XT> &xl)
+__device__ __forceinline__ void x_load(int K, const uint16_t *__restrict__ x, XLoad<XT> &xl)
 {
-    const int nseg = nseg_of(K);
-    uint32_t *sc = reinterpret_cast<uint32_t *>(lds + nseg * 4 * kBlk);
     const int tid = threadIdx.x;
-    u4v *a16 = reinterpret_cast<u4v *>(lds);
-    for (int i = tid; i < nseg * 4 * kBlk / 16; i += 256) a16[i] = u4v{0, 0, 0, 0};
-    for (int i = tid; i < nseg * 16; i += 256) sc[i] = 0x7F7F7F7Fu;
     const __amdgpu_buffer_rsrc_t rx = rsrc(x, (unsigned)K * 2u);
 #pragma unroll
     for (int q = 0; q < XT; ++q) {
@@ -66,6 +61,17 @@ __device__ __forceinline__ void limbs_init(int K, uint8_t *lds, const uint16_t *
         xl.v[q][0] = __builtin_amdgcn_raw_buffer_load_b128(rx, off, 0, 0);
         xl.v[q][1] = __builtin_amdgcn_raw_buffer_load_b128(rx, off + 16u, 0, 0);
     }
+}
+
+// Zero limbs and unit exponents (2^0) for the whole limb area, so blocks past K add nothing.
+__device__ __forceinline__ void limbs_fill(int K, uint8_t *lds)
+{
+    const int nseg = nseg_of(K);
+    uint32_t *sc = reinterpret_cast<uint32_t *>(lds + nseg * 4 * kBlk);
+    const int tid = threadIdx.x;
+    u4v *a16 = reinterpret_cast<u4v *>(lds);
+    for (int i = tid; i < nseg * 4 * kBlk / 16; i += 256) a16[i] = u4v{0, 0, 0, 0};
+    for (int i = tid; i < nseg * 16; i += 256) sc[i] = 0x7F7F7F7Fu;
 }
 
 template <int XT>
@@ -148,21 +154,15 @@ void gemv_mx_kernel(const uint16_t *__restrict__ x, MxSet set, int K, int ntiles
     const int wpr = K >> 5, spr = K >> 7;
     const int my_tiles = __builtin_amdgcn_readfirstlane(
         blockIdx.x < ntiles ? (ntiles - 1 - blockIdx.x) / gridDim.x + 1 : 0);   // <= 64
-    const TileTab tab = tile_tab<R>(set, blockIdx.x + lane * gridDim.x);
 
     Slot<SP, R> ring[P];
 
     // Ring slot fill for the workgroup's it-th tile.  Slots past the last tile, rows past N
     // and groups past K get out-of-range offsets: zero data and zero scales, no traffic.
     // Row offsets use mul24 (rows < 2^24), which keeps the wait counts exact.
-    auto issue = [&](int it, Slot<SP, R> &sl) {
-        const bool live = it < my_tiles;
-        const int L = it & 63;
-        const int row0 = lane_of(tab.row0, L), N = live ? lane_of(tab.N, L) : 0;
-        const __amdgpu_buffer_rsrc_t rW =
-            rsrc(reinterpret_cast<const void *>(lane_of(tab.W, L)), (unsigned)N * (unsigned)wpr * 4u);
-        const __amdgpu_buffer_rsrc_t rS =
-            rsrc(reinterpret_cast<const void *>(lane_of(tab.S, L)), (unsigned)N * (unsigned)spr * 2u);
+    auto issue_t = [&](int row0, int N, unsigned long long Wp, unsigned long long Sp, Slot<SP, R> &sl) {
+        const __amdgpu_buffer_rsrc_t rW = rsrc(reinterpret_cast<const void *>(Wp), (unsigned)N * (unsigned)wpr * 4u);
+        const __amdgpu_buffer_rsrc_t rS = rsrc(reinterpret_cast<const void *>(Sp), (unsigned)N * (unsigned)spr * 2u);
 #pragma unroll
         for (int r = 0; r < R; ++r) {
             const int row = row0 + 16 * r + n;
@@ -184,12 +184,26 @@ void gemv_mx_kernel(const uint16_t *__restrict__ x, MxSet set, int K, int ntiles
             }
         }
     };
+    // the workgroup's it-th tile from the lane table (slots past the last tile load nothing)
+    auto issue = [&](const TileTab &tab, int it, Slot<SP, R> &sl) {
+        const int L = it & 63;
+        issue_t(lane_of(tab.row0, L), it < my_tiles ? lane_of(tab.N, L) : 0, lane_of(tab.W, L), lane_of(tab.S, L), sl);
+    };
 
+    // Entry: the x loads, then the first tile's weights straight from the kernel argument
+    // (most launches give a workgroup one tile, whose weight latency is then the critical
+    // path), and only then the LDS fill and the lane table for the other ring slots.
     constexpr int XT = SP;                           // activation tasks per thread (K <= 4096*SP)
     XLoad<XT> xl;
-    limbs_init<XT>(K, lds, x, xl);
+    x_load<XT>(K, x, xl);
+    {
+        const TileTab t0 = tile_tab<R>(set, blockIdx.x);          // uniform
+        issue_t(t0.row0, my_tiles > 0 ? t0.N : 0, t0.W, t0.S, ring[0]);
+    }
+    limbs_fill(K, lds);
+    const TileTab tab = tile_tab<R>(set, blockIdx.x + lane * gridDim.x);
 #pragma unroll
-    for (int p = 0; p < P; ++p) issue(p, ring[p]);
+    for (int p = 1; p < P; ++p) issue(tab, p, ring[p]);
     __syncthreads();                                  // zero-filled limb area visible
     limbs_build<XT>(K, lds, xl);
     __syncthreads();                                  // limbs visible
@@ -252,7 +266,7 @@ void gemv_mx_kernel(const uint16_t *__restrict__ x, MxSet set, int K, int ntiles
                     }
                 }
             }
-            issue(it + P, ring[p]);
+            issue(tab, it + P, ring[p]);
             float *rb = red + it * (64 * R);          // [tile][16R rows][4 waves]
 #pragma unroll
             for (int r = 0; r < R; ++r) {
@@ -312,10 +326,15 @@ template <bool ODD>
 hipError_t dispatch_mx(const uint16_t *x, const MxSet &set, int K, hipStream_t st)
 {
     const int SP = (((K + 1023) >> 10) + 3) / 4;        // pairs per wave
+    // One tile per workgroup (the grid covers all tiles): a one-slot ring, so that no dead
+    // slots are filled on the way to the first tile.
+    int tiles = 0;
+    for (int i = 0; i < set.count; ++i) tiles += (set.N[i] + 31) / 32;
+    const bool one = tiles <= (SP <= 2 ? 2 * 256 : 256);
     switch (SP) {
-    case 1: return launch_mx<1, 3, 2, ODD>(x, set, K, st);
-    case 2: return launch_mx<2, 2, 2, ODD>(x, set, K, st);
-    case 3: return launch_mx<3, 2, 2, ODD>(x, set, K, st);
+    case 1: return one ? launch_mx<1, 1, 2, ODD>(x, set, K, st) : launch_mx<1, 3, 2, ODD>(x, set, K, st);
+    case 2: return one ? launch_mx<2, 1, 2, ODD>(x, set, K, st) : launch_mx<2, 2, 2, ODD>(x, set, K, st);
+    case 3: return one ? launch_mx<3, 1, 2, ODD>(x, set, K, st) : launch_mx<3, 2, 2, ODD>(x, set, K, st);
     case 4: return launch_mx<4, 1, 2, ODD>(x, set, K, st);
     default: return launch_mx<5, 1, 2, ODD>(x, set, K, st);
     }
