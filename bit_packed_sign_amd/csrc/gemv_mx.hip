@@ -300,7 +300,7 @@ constexpr size_t shm_bytes(int K, int rows_per_wg)
 template <int SP, int P, int R, bool ODD>
 hipError_t launch_mx(const uint16_t *x, const MxSet &set0, int K, hipStream_t st)
 {
-    static_assert(kMaxTileRows / (16 * R) <= 64, "a workgroup's tiles fit the one-per-lane tile table");
+    static_assert(P == 1 || kMaxTileRows / (16 * R) <= 64, "a workgroup's tiles fit the one-per-lane tile table");
     static const hipError_t attr = hipFuncSetAttribute(
         reinterpret_cast<const void *>(&gemv_mx_kernel<SP, P, R, ODD>),
         hipFuncAttributeMaxDynamicSharedMemorySize, (int)shm_bytes(kMaxPairs * 1024, kMaxTileRows));
@@ -314,6 +314,7 @@ hipError_t launch_mx(const uint16_t *x, const MxSet &set0, int K, hipStream_t st
     // Resident workgroups per CU follow the register budget (A operands dominate it); the
     // grid grows past that only when a workgroup's rows would overflow the merge table.
     const int cap = SP <= 2 ? 2 * 256 : 256;
+    if (kMaxTileRows / (16 * R) > 64 && tiles > cap) return hipErrorInvalidValue;   // one tile per workgroup only
     const int need = (tiles + kMaxTileRows / (16 * R) - 1) / (kMaxTileRows / (16 * R));
     const int grid = tiles < cap ? tiles : (need > cap ? need : cap);
     const int rows_per_wg = (tiles + grid - 1) / grid * 16 * R;
@@ -327,14 +328,23 @@ hipError_t dispatch_mx(const uint16_t *x, const MxSet &set, int K, hipStream_t s
 {
     const int SP = (((K + 1023) >> 10) + 3) / 4;        // pairs per wave
     // One tile per workgroup (the grid covers all tiles): a one-slot ring, so that no dead
-    // slots are filled on the way to the first tile.
-    int tiles = 0;
-    for (int i = 0; i < set.count; ++i) tiles += (set.N[i] + 31) / 32;
-    const bool one = tiles <= (SP <= 2 ? 2 * 256 : 256);
+    // slots are filled on the way to the first tile.  Such launches are latency-bound (one
+    // wave per SIMD), so 16-row tiles are used where they still fit one per workgroup: half
+    // the work per workgroup, and co-resident workgroups hide each other's latency.
+    int t16 = 0, t32 = 0;
+    for (int i = 0; i < set.count; ++i) {
+        t16 += (set.N[i] + 15) / 16;
+        t32 += (set.N[i] + 31) / 32;
+    }
+    const int cap = SP <= 2 ? 2 * 256 : 256;
+    const bool one16 = t16 <= cap, one = t32 <= cap;
     switch (SP) {
-    case 1: return one ? launch_mx<1, 1, 2, ODD>(x, set, K, st) : launch_mx<1, 3, 2, ODD>(x, set, K, st);
-    case 2: return one ? launch_mx<2, 1, 2, ODD>(x, set, K, st) : launch_mx<2, 2, 2, ODD>(x, set, K, st);
-    case 3: return one ? launch_mx<3, 1, 2, ODD>(x, set, K, st) : launch_mx<3, 2, 2, ODD>(x, set, K, st);
+    case 1: return one16 ? launch_mx<1, 1, 1, ODD>(x, set, K, st)
+                 : one   ? launch_mx<1, 1, 2, ODD>(x, set, K, st) : launch_mx<1, 3, 2, ODD>(x, set, K, st);
+    case 2: return one16 ? launch_mx<2, 1, 1, ODD>(x, set, K, st)
+                 : one   ? launch_mx<2, 1, 2, ODD>(x, set, K, st) : launch_mx<2, 2, 2, ODD>(x, set, K, st);
+    case 3: return one16 ? launch_mx<3, 1, 1, ODD>(x, set, K, st)
+                 : one   ? launch_mx<3, 1, 2, ODD>(x, set, K, st) : launch_mx<3, 2, 2, ODD>(x, set, K, st);
     case 4: return launch_mx<4, 1, 2, ODD>(x, set, K, st);
     default: return launch_mx<5, 1, 2, ODD>(x, set, K, st);
     }
