@@ -63,15 +63,19 @@ __device__ __forceinline__ void x_load(int K, const uint16_t *__restrict__ x, XL
     }
 }
 
-// Zero limbs and unit exponents (2^0) for the whole limb area, so blocks past K add nothing.
+// What limbs_build leaves unwritten: the zero bytes of every block, and, when K is not a
+// multiple of 1024, the last pair's two segments in full (zero limbs, unit exponents 2^0),
+// so that groups past K add nothing.  Every row of a segment inside K is written by the build.
 __device__ __forceinline__ void limbs_fill(int K, uint8_t *lds)
 {
     const int nseg = nseg_of(K);
+    const int full = ((K >> 7) & 7) ? nseg - 2 : nseg;     // segments the build covers
     uint32_t *sc = reinterpret_cast<uint32_t *>(lds + nseg * 4 * kBlk);
     const int tid = threadIdx.x;
-    u4v *a16 = reinterpret_cast<u4v *>(lds);
-    for (int i = tid; i < nseg * 4 * kBlk / 16; i += 256) a16[i] = u4v{0, 0, 0, 0};
-    for (int i = tid; i < nseg * 16; i += 256) sc[i] = 0x7F7F7F7Fu;
+    for (int i = tid; i < nseg * 4; i += 256) *reinterpret_cast<u4v *>(lds + i * kBlk + kZero) = u4v{0, 0, 0, 0};
+    u4v *tail = reinterpret_cast<u4v *>(lds + full * 4 * kBlk);
+    for (int i = tid; i < (nseg - full) * 4 * kBlk / 16; i += 256) tail[i] = u4v{0, 0, 0, 0};
+    for (int i = tid; i < (nseg - full) * 16; i += 256) sc[full * 16 + i] = 0x7F7F7F7Fu;
 }
 
 template <int XT>

@@ -97,25 +97,33 @@ __device__ __forceinline__ void convert16(const u4v p0, const u4v p1, float mx, 
         }
         if (h == 0) scbyte[r * 4] = (uint8_t)(127 + e0 - 7 - 4 * r);
         if (r < 3) {
+            // next limb's input: 16 (u - q), q = the fp8 value just stored.  u - q is exact
+            // (q is u rounded to 4 significant bits) and so are 16 u and 16 q, so the single
+            // fma 16 u - 16 q rounds nothing.
 #pragma unroll
             for (int c = 0; c < 4; ++c) {
-                u[c] = (u[c] - __builtin_amdgcn_cvt_f32_fp8(d[c], 0)) * 16.f;
-                u[4 + c] = (u[4 + c] - __builtin_amdgcn_cvt_f32_fp8(d[c], 1)) * 16.f;
-                u[8 + c] = (u[8 + c] - __builtin_amdgcn_cvt_f32_fp8(d[c], 2)) * 16.f;
-                u[12 + c] = (u[12 + c] - __builtin_amdgcn_cvt_f32_fp8(d[c], 3)) * 16.f;
+                u[c] = fmaf(u[c], 16.f, -16.f * __builtin_amdgcn_cvt_f32_fp8(d[c], 0));
+                u[4 + c] = fmaf(u[4 + c], 16.f, -16.f * __builtin_amdgcn_cvt_f32_fp8(d[c], 1));
+                u[8 + c] = fmaf(u[8 + c], 16.f, -16.f * __builtin_amdgcn_cvt_f32_fp8(d[c], 2));
+                u[12 + c] = fmaf(u[12 + c], 16.f, -16.f * __builtin_amdgcn_cvt_f32_fp8(d[c], 3));
             }
         }
     }
 }
 
-// max |x| over 16 fp16 values
+// max |x| over 16 fp16 values (packed fp16 max: exact, and a quarter of the scalar ops)
+typedef _Float16 h2v __attribute__((ext_vector_type(2)));
 __device__ __forceinline__ float absmax16(const u4v p0, const u4v p1)
 {
     const uint32_t hw[8] = {p0.x, p0.y, p0.z, p0.w, p1.x, p1.y, p1.z, p1.w};
-    float mx = 0.f;
+    h2v m[8];
 #pragma unroll
-    for (int i = 0; i < 16; ++i) mx = fmaxf(mx, fabsf(h2f((uint16_t)(hw[i >> 1] >> (16 * (i & 1))))));
-    return mx;
+    for (int i = 0; i < 8; ++i) m[i] = __builtin_elementwise_abs(__builtin_bit_cast(h2v, hw[i]));
+#pragma unroll
+    for (int w = 4; w >= 1; w >>= 1)
+#pragma unroll
+        for (int i = 0; i < w; ++i) m[i] = __builtin_elementwise_max(m[i], m[i + w]);
+    return fmaxf((float)m[0].x, (float)m[0].y);
 }
 
 // Sum over the four lanes n, n+16, n+32, n+48 (every lane gets its column's total).
