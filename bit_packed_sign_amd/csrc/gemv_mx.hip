@@ -304,7 +304,6 @@ constexpr size_t shm_bytes(int K, int rows_per_wg)
 template <int SP, int P, int R, bool ODD>
 hipError_t launch_mx(const uint16_t *x, const MxSet &set0, int K, hipStream_t st)
 {
-    static_assert(P == 1 || kMaxTileRows / (16 * R) <= 64, "a workgroup's tiles fit the one-per-lane tile table");
     static const hipError_t attr = hipFuncSetAttribute(
         reinterpret_cast<const void *>(&gemv_mx_kernel<SP, P, R, ODD>),
         hipFuncAttributeMaxDynamicSharedMemorySize, (int)shm_bytes(kMaxPairs * 1024, kMaxTileRows));
@@ -318,8 +317,9 @@ hipError_t launch_mx(const uint16_t *x, const MxSet &set0, int K, hipStream_t st
     // Resident workgroups per CU follow the register budget (A operands dominate it); the
     // grid grows past that only when a workgroup's rows would overflow the merge table.
     const int cap = SP <= 2 ? 2 * 256 : 256;
-    if (kMaxTileRows / (16 * R) > 64 && tiles > cap) return hipErrorInvalidValue;   // one tile per workgroup only
-    const int need = (tiles + kMaxTileRows / (16 * R) - 1) / (kMaxTileRows / (16 * R));
+    // tiles per workgroup: at most what the merge table holds and the one-per-lane tile table
+    constexpr int kMaxT = kMaxTileRows / (16 * R) < 64 ? kMaxTileRows / (16 * R) : 64;
+    const int need = (tiles + kMaxT - 1) / kMaxT;
     const int grid = tiles < cap ? tiles : (need > cap ? need : cap);
     const int rows_per_wg = (tiles + grid - 1) / grid * 16 * R;
     hipLaunchKernelGGL((gemv_mx_kernel<SP, P, R, ODD>), dim3(grid), dim3(256), shm_bytes(K, rows_per_wg),
@@ -340,13 +340,17 @@ hipError_t dispatch_mx(const uint16_t *x, const MxSet &set, int K, hipStream_t s
         t16 += (set.N[i] + 15) / 16;
         t32 += (set.N[i] + 31) / 32;
     }
+    // Up to three 16-row tiles per workgroup still beat 32-row tiles (even shares, shorter
+    // dependent chains); past that the larger tile wins.
     const int cap = SP <= 2 ? 2 * 256 : 256;
-    const bool one16 = t16 <= cap, one = t32 <= cap;
+    const bool one16 = t16 <= cap, one = t32 <= cap, few16 = t16 <= 3 * cap;
     switch (SP) {
     case 1: return one16 ? launch_mx<1, 1, 1, ODD>(x, set, K, st)
-                 : one   ? launch_mx<1, 1, 2, ODD>(x, set, K, st) : launch_mx<1, 3, 2, ODD>(x, set, K, st);
+                 : one   ? launch_mx<1, 1, 2, ODD>(x, set, K, st)
+                 : few16 ? launch_mx<1, 3, 1, ODD>(x, set, K, st) : launch_mx<1, 3, 2, ODD>(x, set, K, st);
     case 2: return one16 ? launch_mx<2, 1, 1, ODD>(x, set, K, st)
-                 : one   ? launch_mx<2, 1, 2, ODD>(x, set, K, st) : launch_mx<2, 2, 2, ODD>(x, set, K, st);
+                 : one   ? launch_mx<2, 1, 2, ODD>(x, set, K, st)
+                 : few16 ? launch_mx<2, 2, 1, ODD>(x, set, K, st) : launch_mx<2, 2, 2, ODD>(x, set, K, st);
     case 3: return one16 ? launch_mx<3, 1, 1, ODD>(x, set, K, st)
                  : one   ? launch_mx<3, 1, 2, ODD>(x, set, K, st) : launch_mx<3, 2, 2, ODD>(x, set, K, st);
     case 4: return launch_mx<4, 1, 2, ODD>(x, set, K, st);
