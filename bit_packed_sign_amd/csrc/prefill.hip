@@ -14,7 +14,8 @@
 //  * Activations go through LDS (two buffers, one barrier per step): the next step's 16-byte
 //    chunks are prefetched into registers and stored while the MFMAs read the current buffer.
 //  * Weights never touch LDS: every wave expands the bits of its own 96 columns straight into
-//    B-operand registers.  Within each 32-wide word the k order is permuted -- fp16 pair p of
+//    B-operand registers, one 16-wide substep ahead of the MFMAs that use them, so a
+//    substep's MFMAs wait on nothing computed in it.  Within each 32-wide word the k order is permuted -- fp16 pair p of
 //    a lane's operand holds bits b and b + 16 -- so one shift and one bit-field insert make
 //    two +-|s| values (a negative scale is folded into the sign bits first).  The activation
 //    rows are stored in LDS under the same permutation (a byte permute per dword while
@@ -199,28 +200,33 @@ void prefill_kernel(const uint16_t *__restrict__ x, const uint32_t *__restrict__
         half8v a[2][FI];
 #pragma unroll
         for (int i = 0; i < FI; ++i) a[0][i] = *reinterpret_cast<const half8v *>(as + 32 * i * LDK);
+        // B operands one substep ahead: a substep's MFMAs depend on nothing computed in it, so
+        // the next substep's sign expansion, A reads and staging run in their shadow
+        half8v b[2][FJ];
+#pragma unroll
+        for (int j = 0; j < FJ; ++j) b[0][j] = expand_pairs<0>(nw[j][0], s2[j]);
 #pragma unroll
         for (int sub = 0; sub < 8; ++sub) {           // 16 k per MFMA: word sub / 2, half sub % 2
-            const int wd = sub >> 1, c = sub & 1;
+            const int c = sub & 1;
+#pragma unroll
+            for (int i = 0; i < FI; ++i)
+#pragma unroll
+                for (int j = 0; j < FJ; ++j)
+                    acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(a[c][i], b[c][j], acc[i][j], 0, 0, 0);
             if (sub < 7) {
+                const int wd1 = (sub + 1) >> 1;
 #pragma unroll
                 for (int i = 0; i < FI; ++i)
                     a[c ^ 1][i] = *reinterpret_cast<const half8v *>(as + 32 * i * LDK + 16 * (sub + 1));
+#pragma unroll
+                for (int j = 0; j < FJ; ++j)
+                    b[c ^ 1][j] = ((sub + 1) & 1) ? expand_pairs<8>(nw[j][wd1], s2[j]) : expand_pairs<0>(nw[j][wd1], s2[j]);
             }
 #pragma unroll
             for (int i = sub; i < kAUnits; i += 8) {
                 store_a1(nxt, i, ra[i]);
                 load_a1(ks + 2, i, ra[i]);
             }
-            half8v b[FJ];
-#pragma unroll
-            for (int j = 0; j < FJ; ++j)
-                b[j] = (sub & 1) ? expand_pairs<8>(nw[j][wd], s2[j]) : expand_pairs<0>(nw[j][wd], s2[j]);
-#pragma unroll
-            for (int i = 0; i < FI; ++i)
-#pragma unroll
-                for (int j = 0; j < FJ; ++j)
-                    acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(a[c][i], b[j], acc[i][j], 0, 0, 0);
             __builtin_amdgcn_sched_barrier(0);
         }
         __syncthreads();
