@@ -1,6 +1,6 @@
 /*
  * bin1_oracle.c -- plain, slow, fp64 CPU oracle for the 1-bit sign GEMV, the
- * +-1 popcount product and the XOR row patch.
+ * +-1 popcount product, the XOR row and bit patches and the scale ranking of rows.
  *
  * TEST INFRASTRUCTURE ONLY.  Nothing on the product path may link or call this
  * file; only the tests, the smoke check and the benchmark's CPU-baseline leg do.
@@ -35,6 +35,7 @@
  *   y, nrm double    [M][N]
  */
 #include <math.h>
+#include <stdlib.h>
 #include <stdint.h>
 #include <omp.h>
 
@@ -128,6 +129,59 @@ int64_t oracle_xor_patch(uint32_t *W, int64_t K, int64_t N,
             W[r * wpr + j] ^= 0xFFFFFFFFu;
     }
     return bad;
+}
+
+/* Bit-granular XOR patch over a set of matrices ("LocalLLaMA ... XOR patch 'Bankai'",
+ * sections on the experiments -- random flips of single bits of the MLP weights -- and on
+ * why XOR patches need true binary codes): entry i = (matrix id, row, k) flips the sign bit
+ * of weight k of that row.  Entries are applied one after another, so a bit listed an even
+ * number of times is unchanged and the same list applied twice restores every matrix.
+ * Entries with id outside [0, nmat), row outside [0, N_id), k outside [0, K_id), or a K_id
+ * that is not a positive multiple of 128 are skipped and counted; the count is returned.
+ * Wtab holds host pointers to the matrices ([N_id][K_id/32] uint32 each). */
+int64_t oracle_xor_bits(uint32_t *const *Wtab, const int64_t *Ktab, const int64_t *Ntab,
+                        int64_t nmat, const int32_t *entries, int64_t nentries)
+{
+    int64_t bad = 0;
+    for (int64_t i = 0; i < nentries; ++i) {
+        const int64_t id = entries[3 * i], r = entries[3 * i + 1], k = entries[3 * i + 2];
+        if (id < 0 || id >= nmat) { ++bad; continue; }
+        const int64_t K = Ktab[id], N = Ntab[id];
+        if (K <= 0 || K % 128 != 0 || r < 0 || r >= N || k < 0 || k >= K) { ++bad; continue; }
+        Wtab[id][r * (K / 32) + k / 32] ^= (uint32_t)1u << (k % 32);
+    }
+    return bad;
+}
+
+/* Scale-ranked rows (the Bankai page's scale-factor targeting, experiments section): the
+ * score of row n is the sum over its groups of |S[n][g]|, taken exactly as an integer in
+ * units of 2^-24, the spacing of the smallest fp16 subnormal:
+ *   |s| = frac * 2^-24 for exponent 0, (1024 + frac) * 2^(expo - 25) otherwise,
+ * so |s| * 2^24 = frac or (1024 + frac) << (expo - 1) (for exponent 31, inf/NaN, the same
+ * formula is used; it exceeds every finite value).  order receives the rows by score,
+ * largest first, equal scores by ascending row. */
+static const int64_t *rank_score;
+static int rank_cmp(const void *a, const void *b)
+{
+    const int32_t i = *(const int32_t *)a, j = *(const int32_t *)b;
+    if (rank_score[i] != rank_score[j]) return rank_score[i] > rank_score[j] ? -1 : 1;
+    return i < j ? -1 : (i > j);
+}
+
+void oracle_rank_rows(const uint16_t *S, int64_t N, int64_t groups, int64_t *score, int32_t *order)
+{
+    for (int64_t n = 0; n < N; ++n) {
+        int64_t acc = 0;
+        for (int64_t g = 0; g < groups; ++g) {
+            const uint16_t h = S[n * groups + g];
+            const int64_t expo = (h >> 10) & 0x1f, frac = h & 0x3ff;
+            acc += expo == 0 ? frac : ((1024 + frac) << (expo - 1));
+        }
+        score[n] = acc;
+        order[n] = (int32_t)n;
+    }
+    rank_score = score;
+    qsort(order, (size_t)N, sizeof(int32_t), rank_cmp);
 }
 
 int oracle_max_threads(void) { return omp_get_max_threads(); }

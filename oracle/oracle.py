@@ -36,6 +36,10 @@ def lib():
             L.oracle_pm1.restype = None
             L.oracle_xor_patch.argtypes = [_p, _i64, _i64, _p, _i64]
             L.oracle_xor_patch.restype = _i64
+            L.oracle_xor_bits.argtypes = [_p, _p, _p, _i64, _p, _i64]
+            L.oracle_xor_bits.restype = _i64
+            L.oracle_rank_rows.argtypes = [_p, _i64, _i64, _p, _p]
+            L.oracle_rank_rows.restype = None
             L.oracle_max_threads.restype = ctypes.c_int
             L.oracle_set_threads.argtypes = [ctypes.c_int]
             _lib = L
@@ -93,6 +97,29 @@ def xor_patch(W: np.ndarray, rows, K: int) -> tuple:
     rows = np.ascontiguousarray(np.asarray(rows, dtype=np.int32))
     bad = lib().oracle_xor_patch(_ptr(out), K, out.shape[0], _ptr(rows), rows.size)
     return out, int(bad)
+
+
+def xor_bits(mats, entries) -> tuple:
+    """Bit-granular patch: mats is a list of uint32 [N_i][K_i/32] arrays, entries int32 [n][3]
+    of (matrix id, row, k).  Returns (patched copies, number of entries skipped)."""
+    outs = [np.array(m, dtype=np.uint32, copy=True, order="C") for m in mats]
+    ptrs = (ctypes.c_void_p * len(outs))(*[o.ctypes.data for o in outs])
+    K = np.array([o.shape[1] * 32 for o in outs], np.int64)
+    N = np.array([o.shape[0] for o in outs], np.int64)
+    e = np.ascontiguousarray(np.asarray(entries, dtype=np.int32).reshape(-1, 3))
+    bad = lib().oracle_xor_bits(ptrs, _ptr(K), _ptr(N), len(outs), _ptr(e), e.shape[0])
+    return outs, int(bad)
+
+
+def rank_rows(S: np.ndarray) -> tuple:
+    """Exact scale ranking: S fp16 [N][G].  Returns (score int64 [N] in units of 2^-24,
+    order int32 [N]: rows by score descending, ties by ascending row)."""
+    S = np.ascontiguousarray(S, dtype=np.float16)
+    N, G = S.shape
+    score = np.empty(N, np.int64)
+    order = np.empty(N, np.int32)
+    lib().oracle_rank_rows(_ptr(S), N, G, _ptr(score), _ptr(order))
+    return score, order
 
 
 def max_threads() -> int:

@@ -313,3 +313,147 @@ def test_pins_accept_the_oracle(orc):
                                      "dropped_last_term", "transposed_output"])
 def test_planted_mistakes_are_caught(variant):
     assert not _pins_pass(_planted(variant))
+
+
+# ---------------------------------------------------------------- bit patch (Bankai experiments)
+def _bits_pins_pass(xor_bits, gemv):
+    """Pins of the bit-granular patch, as a predicate over any implementation."""
+    ok = True
+    r = _rng(90)
+    mats = [synth.sign_words(r, 40, 256), synth.sign_words(r, 7, 384)]
+    # one flip of weight (row, k) changes output row `row` by -2 s w x_k and nothing else
+    # (the rank-one closed form, checked through the pinned dequantise-and-dot)
+    x = synth.activations(r, 2, 256)
+    S = synth.group_scales(r, 40, 256)
+    for row, k in [(0, 0), (5, 31), (5, 32), (39, 255), (17, 128)]:
+        P, bad = xor_bits(mats, np.array([[0, row, k]], np.int32))
+        y0, _ = gemv(x, mats[0], S)
+        y1, _ = gemv(x, P[0], S)
+        w = 1.0 if (int(mats[0][row, k // 32]) >> (k % 32)) & 1 else -1.0
+        delta = -2.0 * float(S[row, k // 128]) * w * x[:, k].astype(np.float64)
+        expect = y0.copy()
+        expect[:, row] += delta
+        ok &= bad == 0 and bool(np.allclose(y1, expect, rtol=0, atol=1e-9))
+        ok &= bool(np.array_equal(P[1], mats[1]))
+    # every bit of a row listed == the row patch of that row
+    row = 3
+    full = np.array([[1, row, k] for k in range(384)], np.int32)
+    P, _ = xor_bits(mats, full)
+    expect = mats[1].copy()
+    expect[row] = np.bitwise_not(mats[1][row])
+    ok &= bool(np.array_equal(P[1], expect))
+    # a multiset of flips: duplicates cancel in pairs, order is irrelevant, and the same list
+    # applied twice restores both matrices
+    e = np.array([[0, 1, 2], [1, 6, 383], [0, 1, 2], [0, 1, 2], [1, 0, 0]], np.int32)
+    P, _ = xor_bits(mats, e)
+    expect0 = mats[0].copy()
+    expect0[1, 0] ^= np.uint32(1 << 2)
+    expect1 = mats[1].copy()
+    expect1[6, 11] ^= np.uint32(1 << 31)
+    expect1[0, 0] ^= np.uint32(1)
+    ok &= bool(np.array_equal(P[0], expect0)) and bool(np.array_equal(P[1], expect1))
+    P2, _ = xor_bits(P, e[::-1])
+    ok &= bool(np.array_equal(P2[0], mats[0])) and bool(np.array_equal(P2[1], mats[1]))
+    # out-of-range entries are skipped and counted
+    bad_e = np.array([[2, 0, 0], [-1, 0, 0], [0, 40, 0], [0, -1, 0], [0, 0, 256], [1, 0, -1], [1, 6, 0]],
+                     np.int32)
+    P, bad = xor_bits(mats, bad_e)
+    expect1 = mats[1].copy()
+    expect1[6, 0] ^= np.uint32(1)
+    ok &= bad == 6 and bool(np.array_equal(P[0], mats[0])) and bool(np.array_equal(P[1], expect1))
+    return ok
+
+
+def _planted_bits(variant):
+    def xor_bits(mats, entries):
+        outs = [np.array(m, copy=True) for m in mats]
+        bad = 0
+        for mid, row, k in np.asarray(entries).reshape(-1, 3):
+            if not (0 <= mid < len(outs)) or not (0 <= row < outs[mid].shape[0]) or \
+                    not (0 <= k < outs[mid].shape[1] * 32):
+                bad += 1
+                continue
+            if variant == "msb_first":
+                outs[mid][row, k // 32] ^= np.uint32(1 << (31 - k % 32))
+            elif variant == "set_not_flip":
+                outs[mid][row, k // 32] |= np.uint32(1 << (k % 32))
+            elif variant == "row_major_swapped":
+                kk = k % (outs[mid].shape[0] * 32)
+                outs[mid][kk // 32 % outs[mid].shape[0], (row * 32 + k % 32) // 32 % outs[mid].shape[1]] ^= \
+                    np.uint32(1 << (k % 32))
+            else:
+                outs[mid][row, k // 32] ^= np.uint32(1 << (k % 32))
+        if variant == "uncounted":
+            bad = 0
+        return outs, bad
+    return xor_bits
+
+
+def test_bit_patch_pins_accept_the_oracle(orc):
+    assert _bits_pins_pass(orc.xor_bits, orc.gemv)
+
+
+@pytest.mark.parametrize("variant", ["msb_first", "set_not_flip", "row_major_swapped", "uncounted"])
+def test_bit_patch_planted_mistakes_are_caught(orc, variant):
+    assert not _bits_pins_pass(_planted_bits(variant), orc.gemv)
+
+
+# ---------------------------------------------------------------- scale ranking of rows
+def _rank_pins_pass(rank_rows, half_to_double):
+    ok = True
+    r = _rng(95)
+    S = synth.group_scales(r, 300, 1024)                 # 8 groups per row
+    S[7] = S[3]                                          # exact ties, resolved by row index
+    S[250] = S[3]
+    S[11, :] = np.float16(0.0)
+    S[12, 0] = np.float16(-0.0)                          # sign ignored
+    S[12, 1:] = S[11, 1:]
+    S[13] = -S[5]                                        # magnitude only: same score as row 5
+    S[20, 0] = np.float16(np.ldexp(1.0, -24))            # subnormals and the largest finite value
+    S[21, 0] = np.float16(65504.0)
+    score, order = rank_rows(S)
+    # the score is sum |s| * 2^24, with |s| from the pinned fp16 decode
+    for n in range(S.shape[0]):
+        ref = sum(abs(half_to_double(int(h))) for h in S[n].view(np.uint16)) * 2.0 ** 24
+        ok &= float(score[n]) == ref
+    # the order is the comparison sort (score descending, row ascending), brute force
+    ranked = sorted(range(S.shape[0]), key=lambda n: (-int(score[n]), n))
+    ok &= bool(np.array_equal(order, np.array(ranked, np.int32)))
+    ok &= list(order[list(order).index(3):list(order).index(3) + 2]) == [3, 7]
+    ok &= int(order[0]) == 21
+    # hand-worked example: rows of two groups
+    S2 = np.array([[1.0, 2.0], [-3.0, 0.0], [0.5, 2.5], [0.0, 0.0]], np.float16)
+    sc2, or2 = rank_rows(S2)
+    ok &= list(sc2) == [3 << 24, 3 << 24, 3 << 24, 0] and list(or2) == [0, 1, 2, 3]
+    S3 = np.array([[0.25, 0.0], [1.0, 1.0], [0.0, 0.5]], np.float16)
+    sc3, or3 = rank_rows(S3)
+    ok &= list(sc3) == [1 << 22, 1 << 25, 1 << 23] and list(or3) == [1, 2, 0]
+    return ok
+
+
+def _planted_rank(variant):
+    def rank_rows(S):
+        s = S.astype(np.float64)
+        if variant == "signed_sum":
+            sc = (s.sum(axis=1) * 2.0 ** 24).astype(np.int64)
+        elif variant == "max_not_sum":
+            sc = (np.abs(s).max(axis=1) * 2.0 ** 24).astype(np.int64)
+        else:
+            sc = (np.abs(s).sum(axis=1) * 2.0 ** 24).astype(np.int64)
+        if variant == "ascending":
+            order = sorted(range(len(sc)), key=lambda n: (int(sc[n]), n))
+        elif variant == "ties_reversed":
+            order = sorted(range(len(sc)), key=lambda n: (-int(sc[n]), -n))
+        else:
+            order = sorted(range(len(sc)), key=lambda n: (-int(sc[n]), n))
+        return sc, np.array(order, np.int32)
+    return rank_rows
+
+
+def test_rank_pins_accept_the_oracle(orc):
+    assert _rank_pins_pass(orc.rank_rows, orc.half_to_double)
+
+
+@pytest.mark.parametrize("variant", ["signed_sum", "max_not_sum", "ascending", "ties_reversed"])
+def test_rank_planted_mistakes_are_caught(orc, variant):
+    assert not _rank_pins_pass(_planted_rank(variant), orc.half_to_double)
