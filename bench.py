@@ -51,7 +51,7 @@ def parse():
     ap.add_argument("--no-extra", action="store_true")
     ap.add_argument("--only", default=None,
                     help="run one workload alone (for profiling): step8b, chain8b, lmhead, single, mlp16, "
-                         "prefill, step27b, pm1, copy")
+                         "prefill, step27b, pm1, bits, copy")
     return ap.parse_args()
 
 
@@ -305,6 +305,33 @@ def extra_patch27b(st, dev):
     return {"patch_2000_rows_us": round(ms * 1e3, 2), "patch_bytes_read_and_written": int(2 * row_bytes)}
 
 
+def extra_bits_8b(st, dev):
+    """500K random single-bit flips over the 108 MLP matrices of the 8B batch-16 workload (the
+    Bankai robustness experiment's data movement), one launch; each timed call flips them again."""
+    import bit_packed_sign_amd as b1
+    import torch
+    from bit_packed_sign_amd import synth
+    mlp = []
+    for l in range(36):                       # stages per layer: gate|up, down
+        gu = st.stages[2 * l][1]
+        dn = st.stages[2 * l + 1][1]
+        mlp += [gu[0], gu[1], dn[0]]
+    table = b1.PatchTable(mlp)
+    ent = torch.from_numpy(synth.bit_flip_entries(0, [(m.shape[0], m.shape[1] * 32) for m in mlp],
+                                                  500_000)).to(dev)
+    ms = time_fn(lambda: b1.xor_bits_apply(table, ent), reps=50)
+    return {"bit_flips_500k_us": round(ms * 1e3, 2), "flips_per_s": round(500_000 / (ms * 1e-3), 0)}
+
+
+def extra_rank27b(st, dev):
+    """Scale ranking of the rows of one 27B gate matrix (17408 x 5120), exact."""
+    import bit_packed_sign_amd as b1
+    S = st.stages[2][2][0]                    # layer 0: gate|up stage, gate scales
+    score, order = b1.rank_rows_by_scale(S)
+    ms = time_fn(lambda: b1.rank_rows_by_scale(S, score, order), reps=20)
+    return {"rank_rows_17408x5120_us": round(ms * 1e3, 1)}
+
+
 def extra_prefill(dev):
     import torch
     import bit_packed_sign_amd as b1
@@ -409,6 +436,7 @@ def main():
         log(f"[bench] single GEMV: {extra['single_gemv']}")
         st, extra["mlp_8b_m16"] = extra_step(synth.mlp_8b_m16(), dev, args.steps,
                                              "8B MLP batch 16: 36 x (gate/up 4096x12288, down 12288x4096)")
+        extra["mlp_8b_m16"].update(extra_bits_8b(st, dev))
         log(f"[bench] mlp m16: {extra['mlp_8b_m16']}")
         del st
         torch.cuda.empty_cache()
@@ -418,6 +446,7 @@ def main():
                                              "27B decode batch 1: 64 x (q/k/v/o 5120x5120, gate/up "
                                              "5120x17408, down 17408x5120)", chain=True)
         extra["decode_27b"].update(extra_patch27b(st, dev))
+        extra["decode_27b"].update(extra_rank27b(st, dev))
         log(f"[bench] 27b: {extra['decode_27b']}")
         del st
         torch.cuda.empty_cache()
@@ -479,11 +508,14 @@ def run_only(args, dev):
     elif name == "mlp16":
         st, o = extra_step(synth.mlp_8b_m16(), dev, args.steps, "mlp16")
         log(f"[bench] {o}")
+    elif name == "bits":
+        st, _ = extra_step(synth.mlp_8b_m16(), dev, 2, "mlp16")
+        log(f"[bench] {extra_bits_8b(st, dev)}")
     elif name == "prefill":
         log(f"[bench] {extra_prefill(dev)}")
     elif name == "step27b":
         st, o = extra_step(synth.decode_27b(), dev, args.steps, "27b")
-        log(f"[bench] {o} patch {extra_patch27b(st, dev)}")
+        log(f"[bench] {o} patch {extra_patch27b(st, dev)} rank {extra_rank27b(st, dev)}")
     elif name == "pm1":
         log(f"[bench] {extra_pm1(dev)}")
     elif name == "copy":

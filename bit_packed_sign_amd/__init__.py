@@ -4,4 +4,4 @@ The computation lives in libbin1.so (C ABI: include/bin1.h, HIP kernels in csrc/
 functions below are its thin torch binding.  ``synth`` holds the seeded input generators.
 """
 from .binding import (Bin1Error, ChainPlan, PatchTable, gemm_prefill, gemv, gemv_group, gemv_pm1, lib,  # noqa: F401
-                      xor_patch_apply, xor_patch_apply_multi)
+                      rank_rows_by_scale, xor_bits_apply, xor_patch_apply, xor_patch_apply_multi)

@@ -31,6 +31,8 @@ _SIGS = {
     "bin1_gemv_pm1": [_p, _p, _p, _i, _i, _i, _p],
     "bin1_xor_patch_apply": [_p, _p, _i, _i, _i, _p, _p],
     "bin1_xor_patch_apply_multi": [_p, _p, _p, _i, _p, _i, _p, _p],
+    "bin1_xor_bits_apply": [_p, _p, _p, _i, _p, _i, _p, _p],
+    "bin1_rank_rows_by_scale": [_p, _i, _i, _p, _p, _p],
     "bin1_chain_workspace_bytes": [_i],
     "bin1_chain_prepare": [_p, _i, _p, ctypes.c_size_t, _p],
     "bin1_gemv_chain": [_p, _p],
@@ -243,6 +245,43 @@ def xor_patch_apply_multi(table: PatchTable, entries: torch.Tensor, bad_rows: Op
         _check("bin1_xor_patch_apply_multi", lib().bin1_xor_patch_apply_multi(
             table.ptrs.data_ptr(), table.K.data_ptr(), table.N.data_ptr(), len(table),
             entries.data_ptr(), entries.shape[0], bp or None, _stream(table.ptrs)))
+
+
+def xor_bits_apply(table: PatchTable, entries: torch.Tensor, bad: Optional[torch.Tensor] = None) -> None:
+    """Bit-granular patch in one launch.  ``entries``: device int32 [n][3] of (matrix id, row, k);
+    records may repeat (flips are XORs: an even count cancels)."""
+    _need(entries, "entries", (torch.int32,), 2)
+    if entries.shape[1] != 3:
+        raise ValueError("entries must be [n][3]")
+    bp = 0
+    if bad is not None:
+        _need(bad, "bad", (torch.int32,), 1)
+        bp = bad.data_ptr()
+    dev = table.ptrs.device
+    with torch.cuda.device(dev):
+        _check("bin1_xor_bits_apply", lib().bin1_xor_bits_apply(
+            table.ptrs.data_ptr(), table.K.data_ptr(), table.N.data_ptr(), len(table),
+            entries.data_ptr(), entries.shape[0], bp or None, _stream(table.ptrs)))
+
+
+def rank_rows_by_scale(scales: torch.Tensor, score: Optional[torch.Tensor] = None,
+                       order: Optional[torch.Tensor] = None):
+    """Rows of a matrix by the exact sum of |scale| (units of 2^-24), largest first, ties by
+    row.  ``scales``: device fp16 [N][K/128].  Returns (score int64 [N], order int32 [N])."""
+    _need(scales, "scales", (torch.float16,), 2)
+    N, G = scales.shape
+    if score is None:
+        score = torch.empty(N, dtype=torch.int64, device=scales.device)
+    if order is None:
+        order = torch.empty(N, dtype=torch.int32, device=scales.device)
+    _need(score, "score", (torch.int64,), 1)
+    _need(order, "order", (torch.int32,), 1)
+    if score.shape[0] != N or order.shape[0] != N:
+        raise ValueError("score and order must have N entries")
+    with torch.cuda.device(scales.device):
+        _check("bin1_rank_rows_by_scale", lib().bin1_rank_rows_by_scale(
+            scales.data_ptr(), N, G * 128, score.data_ptr(), order.data_ptr(), _stream(scales)))
+    return score, order
 
 
 class ChainPlan:

@@ -404,4 +404,45 @@ int bin1_xor_patch_apply_multi(uint32_t *const *Wtab, const int32_t *Ktab, const
                     "bin1_xor_patch_apply_multi");
 }
 
+int bin1_xor_bits_apply(uint32_t *const *Wtab, const int32_t *Ktab, const int32_t *Ntab, int nmat,
+                        const int32_t *entries, int nentries, int32_t *bad, void *stream)
+{
+    if (nentries < 0 || nmat < 1)
+        return fail(BIN1_ERR_SHAPE, "need nentries>=0 and nmat>=1 (got %d, %d)", nentries, nmat);
+    if (nentries == 0) return ok();
+    if (!Wtab || !Ktab || !Ntab || !entries)
+        return fail(BIN1_ERR_NULL, "Wtab, Ktab, Ntab and entries must be non-NULL");
+    if (reinterpret_cast<uintptr_t>(Wtab) & 7u || reinterpret_cast<uintptr_t>(Ktab) & 3u ||
+        reinterpret_cast<uintptr_t>(Ntab) & 3u || reinterpret_cast<uintptr_t>(entries) & 3u ||
+        reinterpret_cast<uintptr_t>(bad) & 3u)
+        return fail(BIN1_ERR_ALIGN, "tables must be naturally aligned");
+    int st;
+    if ((st = check_device(Wtab, "Wtab")) || (st = check_device(Ktab, "Ktab")) ||
+        (st = check_device(Ntab, "Ntab")) || (st = check_device(entries, "entries")) ||
+        (bad && (st = check_device(bad, "bad"))))
+        return st;
+    return launched(bin1::launch_xor_bits(Wtab, Ktab, Ntab, nmat, entries, nentries, bad,
+                                          static_cast<hipStream_t>(stream)),
+                    "bin1_xor_bits_apply");
+}
+
+int bin1_rank_rows_by_scale(const void *scales, int N, int K, int64_t *score, int32_t *order, void *stream)
+{
+    if (!scales || !score || !order) return fail(BIN1_ERR_NULL, "scales, score and order must be non-NULL");
+    if (N < 1 || N > (1 << 20) || K < 128 || K % 128 != 0)
+        return fail(BIN1_ERR_SHAPE, "need 1 <= N <= 2^20, K >= 128, K %% 128 == 0 (got N=%d K=%d)", N, K);
+    if (!aligned16(scales) || reinterpret_cast<uintptr_t>(score) & 7u || reinterpret_cast<uintptr_t>(order) & 3u)
+        return fail(BIN1_ERR_ALIGN, "scales must be 16-byte aligned, score 8-byte, order 4-byte");
+    const size_t sb = (size_t)N * (K / 128) * 2, cb = (size_t)N * 8, ob = (size_t)N * 4;
+    if (overlap(score, cb, scales, sb) || overlap(order, ob, scales, sb) || overlap(order, ob, score, cb))
+        return fail(BIN1_ERR_ALIAS, "scales, score and order must not overlap");
+    int st;
+    if ((st = check_device(scales, "scales")) || (st = check_device(score, "score")) ||
+        (st = check_device(order, "order")))
+        return st;
+    return launched(bin1::launch_rank_rows(static_cast<const uint16_t *>(scales), N, K, score, order,
+                                           static_cast<hipStream_t>(stream)),
+                    "bin1_rank_rows_by_scale");
+}
+
 }  // extern "C"

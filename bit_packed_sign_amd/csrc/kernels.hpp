@@ -70,6 +70,9 @@ hipError_t launch_prefill(const uint16_t *x, const uint32_t *W, const uint16_t *
                           int M, int K, int N, hipStream_t st);
 hipError_t launch_pm1(const uint32_t *A, const uint32_t *W, int32_t *y, int M, int K, int N,
                       hipStream_t st);
+hipError_t launch_xor_bits(uint32_t *const *Wtab, const int32_t *Ktab, const int32_t *Ntab, int nmat,
+                           const int32_t *entries, int n, int32_t *bad, hipStream_t st);
+hipError_t launch_rank_rows(const uint16_t *S, int N, int K, int64_t *score, int32_t *order, hipStream_t st);
 hipError_t launch_xor_patch(uint32_t *W, const int32_t *rows, int nrows, int K, int N,
                             int32_t *bad, hipStream_t st);
 hipError_t launch_xor_patch_multi(uint32_t *const *Wtab, const int32_t *Ktab, const int32_t *Ntab,

@@ -199,3 +199,24 @@ def patch_entries_27b(seed: int = 0, count: int = 2000) -> np.ndarray:
     flat = rng_for(seed, WL_DECODE_27B, 20_000).choice(int(offs[-1]), size=count, replace=False)
     mid = np.searchsorted(offs, flat, side="right") - 1
     return np.stack([mid, flat - offs[mid]], axis=1).astype(np.int32)
+
+
+def mlp_mats_8b() -> List[Tuple[int, str, int, int]]:
+    """(layer, projection, N, K) of every MLP matrix of the 8B workload (36 x gate, up, down)."""
+    out = []
+    for l in range(36):
+        out += [(l, "gate", 12288, 4096), (l, "up", 12288, 4096), (l, "down", 4096, 12288)]
+    return out
+
+
+def bit_flip_entries(seed: int, shapes: List[Tuple[int, int]], count: int, workload: int = WL_TEST,
+                     tensor: int = 21_000) -> np.ndarray:
+    """int32 [count][3] = (matrix id, row, k): `count` weights drawn uniformly (with replacement,
+    as independent random flips are) from all weights of the matrices of `shapes` [(N, K), ...]."""
+    sizes = np.array([n * k for (n, k) in shapes], dtype=np.int64)
+    offs = np.concatenate([[0], np.cumsum(sizes)])
+    flat = rng_for(seed, workload, tensor).integers(0, int(offs[-1]), size=count, dtype=np.int64)
+    mid = np.searchsorted(offs, flat, side="right") - 1
+    local = flat - offs[mid]
+    Ks = np.array([k for (_, k) in shapes], dtype=np.int64)[mid]
+    return np.stack([mid, local // Ks, local % Ks], axis=1).astype(np.int32)

@@ -121,6 +121,29 @@ int bin1_xor_patch_apply_multi(uint32_t *const *Wtab, const int32_t *Ktab, const
                                int nmat, const int32_t *entries, int nentries,
                                int32_t *bad_rows, void *stream);
 
+/* Bit-granular XOR patch over many matrices in one launch ["LocalLLaMA ... XOR patch
+ * 'Bankai'", experiments section: random flips of single bits of the MLP weights, e.g.
+ * 500K of them].  Wtab, Ktab, Ntab describe the matrices as in bin1_xor_patch_apply_multi;
+ * entries (device int32[nentries][3]) holds (matrix id, row, k) records, each flipping the
+ * sign bit of weight k of that row (y[:, row] changes by -2 s w x_k).  Records may repeat:
+ * flips are atomic XORs, so the result is independent of order, a bit listed an even number
+ * of times is unchanged, and the same list applied again removes the patch.  Records with a
+ * matrix id outside [0, nmat), a row outside [0, N_id), k outside [0, K_id), a K_id that is
+ * not a positive multiple of 128, or a misaligned matrix are skipped and counted into *bad
+ * (device int32*, may be NULL; the caller zeroes it).  nentries == 0 is a no-op.  Order it
+ * on the stream of the products that read the weights. */
+int bin1_xor_bits_apply(uint32_t *const *Wtab, const int32_t *Ktab, const int32_t *Ntab, int nmat,
+                        const int32_t *entries, int nentries, int32_t *bad, void *stream);
+
+/* Scale ranking of rows, the mechanics of targeting patches by scale factors [same page,
+ * experiments section].  scales: device fp16 [N][K/128] (16-byte aligned).  Writes
+ * score (device int64[N]): the sum over the row's groups of |scale|, exactly, in units of
+ * 2^-24 (an inf/NaN scale counts as its magnitude bits would, (f + 2^10) << 30), and order
+ * (device int32[N]): the rows by score, largest first, equal scores by ascending row.
+ * Requires 1 <= N <= 2^20 (the ranking counts over all pairs), K >= 128, K % 128 == 0,
+ * and no overlap between scales, score and order. */
+int bin1_rank_rows_by_scale(const void *scales, int N, int K, int64_t *score, int32_t *order, void *stream);
+
 /* ------------------------------------------------------------------------------------
  * Decode-step chain: a sequence of dependent stages in ONE persistent launch.
  * Stage s = `count` (1..4) products that read the same activations x_s (fp16 [K_s]), M = 1;

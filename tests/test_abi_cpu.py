@@ -28,8 +28,8 @@ def L():
 def test_header_declares_the_entry_points():
     names = _declared()
     for fn in ["bin1_gemv", "bin1_gemv_group", "bin1_gemm_prefill", "bin1_gemv_pm1", "bin1_xor_patch_apply",
-               "bin1_xor_patch_apply_multi", "bin1_status_string", "bin1_last_error",
-               "bin1_abi_version"]:
+               "bin1_xor_patch_apply_multi", "bin1_xor_bits_apply", "bin1_rank_rows_by_scale",
+               "bin1_status_string", "bin1_last_error", "bin1_abi_version"]:
         assert fn in names
 
 
@@ -112,6 +112,24 @@ def test_pm1_and_patch_validation(L):
     assert L.bin1_xor_patch_apply_multi(None, None, None, 1, None, 0, None, None) == 0
     assert L.bin1_xor_patch_apply_multi(FAKE, FAKE, FAKE, 0, FAKE, 1, None, None) == -2
     assert L.bin1_xor_patch_apply_multi(None, FAKE, FAKE, 1, FAKE, 1, None, None) == -1
+
+
+def test_bit_patch_and_rank_validation(L):
+    # bit patch: empty list is a no-op, bad counts and tables are rejected before launch
+    assert L.bin1_xor_bits_apply(None, None, None, 1, None, 0, None, None) == 0
+    assert L.bin1_xor_bits_apply(FAKE, FAKE, FAKE, 0, FAKE, 1, None, None) == -2
+    assert L.bin1_xor_bits_apply(FAKE, FAKE, FAKE, 1, FAKE, -1, None, None) == -2
+    assert L.bin1_xor_bits_apply(None, FAKE, FAKE, 1, FAKE, 1, None, None) == -1
+    assert L.bin1_xor_bits_apply(FAKE + 4, FAKE, FAKE, 1, FAKE, 1, None, None) == -3
+    # rank: NULLs, shapes, alignment and overlap
+    assert L.bin1_rank_rows_by_scale(None, 1, 128, FAKE, FAKE * 2, None) == -1
+    assert L.bin1_rank_rows_by_scale(FAKE, 0, 128, FAKE * 2, FAKE * 3, None) == -2
+    assert L.bin1_rank_rows_by_scale(FAKE, (1 << 20) + 1, 128, FAKE * 2, FAKE * 3, None) == -2
+    assert L.bin1_rank_rows_by_scale(FAKE, 4, 96, FAKE * 2, FAKE * 3, None) == -2
+    assert L.bin1_rank_rows_by_scale(FAKE + 2, 4, 128, FAKE * 2, FAKE * 3, None) == -3
+    assert L.bin1_rank_rows_by_scale(FAKE, 4, 128, FAKE * 2 + 4, FAKE * 3, None) == -3
+    assert L.bin1_rank_rows_by_scale(FAKE, 4, 1024, FAKE + 8, FAKE * 3, None) == -4     # score over scales
+    assert L.bin1_rank_rows_by_scale(FAKE, 4, 128, FAKE * 2, FAKE * 2 + 16, None) == -4
 
 
 def test_binding_rejects_cpu_tensors():

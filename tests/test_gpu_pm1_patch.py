@@ -111,3 +111,66 @@ def test_multi_patch_bad_entries_counted(dev):
     expect = W.copy()
     expect[2] ^= np.uint32(0xFFFFFFFF)
     assert np.array_equal(got, expect) and int(bad.item()) == 4
+
+
+# ---------------------------------------------------------------- bit-granular patch
+def test_bit_patch_matches_oracle_with_duplicates_and_bad_entries(orc, dev):
+    r = synth.rng_for(0, synth.WL_TEST, 6400)
+    host = [synth.sign_words(r, 37, 128), synth.sign_words(r, 300, 4096), synth.sign_words(r, 5, 12288)]
+    devm = [_i32(h).to(dev) for h in host]
+    table = b1.PatchTable(devm)
+    ent = synth.bit_flip_entries(1, [(h.shape[0], h.shape[1] * 32) for h in host], 5000)
+    ent = np.concatenate([ent, ent[:700], ent[:300],                              # repeats
+                          np.array([[3, 0, 0], [-1, 0, 0], [0, 37, 0], [1, 0, 4096], [2, 4, -1]], np.int32)])
+    ed = torch.from_numpy(ent).to(dev)
+    bad = torch.zeros(1, dtype=torch.int32, device=dev)
+    b1.xor_bits_apply(table, ed, bad=bad)
+    expect, nbad = orc.xor_bits(host, ent)
+    torch.cuda.synchronize()
+    for mid, (e, d) in enumerate(zip(expect, devm)):
+        assert np.array_equal(d.cpu().numpy().view(np.uint32), e), mid
+    assert int(bad.item()) == nbad == 5
+    b1.xor_bits_apply(table, ed[torch.randperm(ed.shape[0], device=dev)])   # any order removes it
+    for h, d in zip(host, devm):
+        assert np.array_equal(d.cpu().numpy().view(np.uint32), h)
+
+
+def test_bit_patch_500k_random_flips_8b_mlp(orc, dev):
+    """500K random single-bit flips over all 108 MLP matrices of the 8B workload (the page's
+    robustness experiment, mechanics only), one launch; every matrix bit-exact, then removed."""
+    mats = synth.mlp_mats_8b()
+    r = synth.rng_for(0, synth.WL_TEST, 6500)
+    host = [synth.sign_words(r, n, k) for (_, _, n, k) in mats]
+    devm = [_i32(h).to(dev) for h in host]
+    table = b1.PatchTable(devm)
+    ent = synth.bit_flip_entries(0, [(n, k) for (_, _, n, k) in mats], 500_000)
+    ed = torch.from_numpy(ent).to(dev)
+    bad = torch.zeros(1, dtype=torch.int32, device=dev)
+    b1.xor_bits_apply(table, ed, bad=bad)
+    expect, nbad = orc.xor_bits(host, ent)
+    torch.cuda.synchronize()
+    assert nbad == 0 and int(bad.item()) == 0
+    for mid, (e, d) in enumerate(zip(expect, devm)):
+        assert np.array_equal(d.cpu().numpy().view(np.uint32), e), mid
+    b1.xor_bits_apply(table, ed)
+    for h, d in zip(host, devm):
+        assert np.array_equal(d.cpu().numpy().view(np.uint32), h)
+
+
+# ---------------------------------------------------------------- scale ranking of rows
+@pytest.mark.parametrize("N,K", [(1, 128), (300, 1024), (2500, 4096), (17408, 5120), (5120, 17408)])
+def test_rank_rows_matches_oracle(orc, dev, N, K):
+    r = synth.rng_for(0, synth.WL_TEST, 6600 + N)
+    S = synth.group_scales(r, N, K)
+    if N >= 300:
+        S[N - 1] = S[0]                                  # ties across LDS tiles of the ranking
+        S[N // 2] = -S[1]                                # sign ignored
+        S[5] = np.float16(0.0)
+        S[6, 0] = np.float16(np.ldexp(1.0, -24))
+        S[7, :] = np.float16(65504.0)
+    score_ref, order_ref = orc.rank_rows(S)
+    Sd = torch.from_numpy(S).to(dev)
+    score, order = b1.rank_rows_by_scale(Sd)
+    torch.cuda.synchronize()
+    assert np.array_equal(score.cpu().numpy(), score_ref)
+    assert np.array_equal(order.cpu().numpy(), order_ref)
