@@ -52,6 +52,14 @@ def sign_words(rng: np.random.Generator, N: int, K: int) -> np.ndarray:
     return rng.integers(0, 1 << 32, size=(N, (K + WORD_BITS - 1) // WORD_BITS), dtype=np.uint32)
 
 
+def ternary_words(rng: np.random.Generator, N: int, K: int) -> np.ndarray:
+    """uint32 [N][K/16]: 2-bit slots, LSB first, each weight drawn uniformly from {0, +1, -1}
+    as the codes 00, 01, 11 (code 10 is never drawn)."""
+    codes = np.array([0, 1, 3], np.uint32)[rng.integers(0, 3, size=(N, K), dtype=np.int64)]
+    shifts = (2 * np.arange(16, dtype=np.uint32))[None, None, :]
+    return np.bitwise_or.reduce(codes.reshape(N, K // 16, 16) << shifts, axis=2).astype(np.uint32)
+
+
 def group_scales(rng: np.random.Generator, N: int, K: int, group: int = GROUP) -> np.ndarray:
     """fp16 [N][K/group] = fp16(|N(0,1)| * 0.02)."""
     return (np.abs(rng.standard_normal((N, K // group))) * 0.02).astype(np.float16)

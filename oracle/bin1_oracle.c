@@ -92,6 +92,45 @@ void oracle_gemv(const uint16_t *x, const uint32_t *W, const uint16_t *S,
     }
 }
 
+/* Ternary weight of (n, k) from its 2-bit slot ("Bonsai 27B", section on the ternary weight
+ * format: t in {-1, 0, +1}, w = s_g * t, one fp16 scale per group of 128; the same page's
+ * deployment section: current kernels keep each ternary value in a 2-bit slot).  Reading:
+ * slot k % 16 of word k / 16, LSB first; within the slot, the low bit says nonzero and the
+ * high bit says negative (00 -> 0, 01 -> +1, 11 -> -1; 10, never written, reads as 0). */
+static inline double ternary_value(const uint32_t *row, int64_t k)
+{
+    const uint32_t code = (row[k / 16] >> (2 * (k % 16))) & 3u;
+    if (!(code & 1u)) return 0.0;
+    return (code & 2u) ? -1.0 : 1.0;
+}
+
+/* y[m][n]   = sum_k S[n][k/G] * t(n,k) * x[m][k]   (ascending k, fp64)
+ * nrm[m][n] = sum_k |S[n][k/G] * t(n,k) * x[m][k]| (parity normaliser: the terms the product
+ * actually adds).  T: uint32 [N][ceil(K/16)].  Either output pointer may be NULL. */
+void oracle_gemv_t2(const uint16_t *x, const uint32_t *T, const uint16_t *S,
+                    int64_t M, int64_t K, int64_t N, int64_t G, double *y, double *nrm)
+{
+    const int64_t wpr = (K + 15) / 16;
+    const int64_t spr = K / G;
+    #pragma omp parallel for schedule(dynamic, 16)
+    for (int64_t n = 0; n < N; ++n) {
+        const uint32_t *row = T + n * wpr;
+        const uint16_t *srow = S + n * spr;
+        for (int64_t m = 0; m < M; ++m) {
+            const uint16_t *xr = x + m * K;
+            double acc = 0.0, a = 0.0;
+            for (int64_t k = 0; k < K; ++k) {
+                double term = oracle_half_to_double(srow[k / G]) * ternary_value(row, k) *
+                              oracle_half_to_double(xr[k]);
+                acc += term;
+                a += fabs(term);
+            }
+            if (y) y[m * N + n] = acc;
+            if (nrm) nrm[m * N + n] = a;
+        }
+    }
+}
+
 /* +-1 activations and weights, both packed (bit 1 = +1):
  * y[m][n] = sum_k a(m,k) * w(n,k), exact in int64. */
 void oracle_pm1(const uint32_t *A, const uint32_t *W,

@@ -32,6 +32,8 @@ def lib():
             L.oracle_half_to_double.restype = ctypes.c_double
             L.oracle_gemv.argtypes = [_p, _p, _p, _i64, _i64, _i64, _i64, _p, _p]
             L.oracle_gemv.restype = None
+            L.oracle_gemv_t2.argtypes = [_p, _p, _p, _i64, _i64, _i64, _i64, _p, _p]
+            L.oracle_gemv_t2.restype = None
             L.oracle_pm1.argtypes = [_p, _p, _i64, _i64, _i64, _p]
             L.oracle_pm1.restype = None
             L.oracle_xor_patch.argtypes = [_p, _i64, _i64, _p, _i64]
@@ -79,6 +81,29 @@ def gemv_rows(x, W, S, rows, group: int = 128):
     """The oracle at selected output rows only: returns (y, nrm) of shape [M][len(rows)]."""
     rows = np.asarray(rows, dtype=np.int64)
     return gemv(x, W[rows], S[rows], group)
+
+
+def gemv_t2(x: np.ndarray, T: np.ndarray, S: np.ndarray, group: int = 128):
+    """fp64 ternary dequantise-and-dot.  x: fp16 [M][K]; T: uint32 [N][ceil(K/16)] of 2-bit
+    slots; S: fp16 [N][K/group].  Returns (y, nrm) float64 [M][N], nrm = sum_k |s*t*x|."""
+    x = np.ascontiguousarray(x, dtype=np.float16)
+    T = np.ascontiguousarray(T, dtype=np.uint32)
+    S = np.ascontiguousarray(S, dtype=np.float16)
+    M, K = x.shape
+    N = T.shape[0]
+    if K % group:
+        raise ValueError("K must be a multiple of the group size")
+    if T.shape[1] != (K + 15) // 16 or S.shape != (N, K // group):
+        raise ValueError("shape mismatch")
+    y = np.empty((M, N), np.float64)
+    nrm = np.empty((M, N), np.float64)
+    lib().oracle_gemv_t2(_ptr(x), _ptr(T), _ptr(S), M, K, N, group, _ptr(y), _ptr(nrm))
+    return y, nrm
+
+
+def gemv_t2_rows(x, T, S, rows, group: int = 128):
+    rows = np.asarray(rows, dtype=np.int64)
+    return gemv_t2(x, T[rows], S[rows], group)
 
 
 def pm1(A: np.ndarray, W: np.ndarray, K: int) -> np.ndarray:

@@ -457,3 +457,101 @@ def test_rank_pins_accept_the_oracle(orc):
 @pytest.mark.parametrize("variant", ["signed_sum", "max_not_sum", "ascending", "ties_reversed"])
 def test_rank_planted_mistakes_are_caught(orc, variant):
     assert not _rank_pins_pass(_planted_rank(variant), orc.half_to_double)
+
+
+# ---------------------------------------------------------------- ternary g128 in 2-bit slots
+def _binary_as_ternary(W, K):
+    """The 2-bit-slot words holding +1 (code 01) for every set sign bit and -1 (code 11) for
+    every clear one."""
+    bits = np.unpackbits(W.view(np.uint8).reshape(W.shape[0], -1), axis=1, bitorder="little")[:, :K]
+    codes = np.where(bits == 1, 1, 3).astype(np.uint32).reshape(W.shape[0], K // 16, 16)
+    return np.bitwise_or.reduce(codes << (2 * np.arange(16, dtype=np.uint32)), axis=2).astype(np.uint32)
+
+
+def _t2_pins_pass(gemv_t2, gemv):
+    ok = True
+    r = _rng(97)
+    M, K, N = 2, 512, 24
+    x = synth.activations(r, M, K)
+    S = synth.group_scales(r, N, K)
+    S[3] = -S[3]
+    W = synth.sign_words(r, N, K)
+    # with no zero codes, the ternary product is the binary product of the same signs, term for
+    # term (both ascending k, same products), so bit-identical
+    yt, nt = gemv_t2(x, _binary_as_ternary(W, K), S)
+    yb, nb = gemv(x, W, S)
+    ok &= bool(np.array_equal(yt, yb)) and bool(np.array_equal(nt, nb))
+    # all-zero codes, and the never-written code 10, add nothing
+    for code in (0, 2):
+        Tz = np.full((N, K // 16), sum(code << (2 * i) for i in range(16)), np.uint32)
+        yz, nz = gemv_t2(x, Tz, S)
+        ok &= bool(np.all(yz == 0.0)) and bool(np.all(nz == 0.0))
+    # one nonzero slot at k: y = t * s_{k/128} * x_k exactly (pins LSB-first 2-bit placement)
+    x64 = x.astype(np.float64)
+    for k, code, t in [(0, 1, 1.0), (1, 3, -1.0), (15, 1, 1.0), (16, 3, -1.0), (127, 1, 1.0), (128, 3, -1.0),
+                       (511, 1, 1.0)]:
+        T1 = np.zeros((N, K // 16), np.uint32)
+        T1[:, k // 16] = np.uint32(code << (2 * (k % 16)))
+        y1, _ = gemv_t2(x, T1, S)
+        expect = t * S[:, k // 128].astype(np.float64)[None, :] * x64[:, k:k + 1]
+        ok &= bool(np.array_equal(y1, expect))
+    # exhaustive: every ternary row of K = 8 (3^8 rows, groups of 4) against exact rationals
+    Kt, G = 8, 4
+    vals = np.array(np.meshgrid(*[[0, 1, -1]] * Kt, indexing="ij")).reshape(Kt, -1).T      # [6561][8]
+    codes = np.where(vals == 0, 0, np.where(vals > 0, 1, 3)).astype(np.uint32)
+    Te = np.bitwise_or.reduce(codes << (2 * np.arange(Kt, dtype=np.uint32)), axis=1).astype(np.uint32)[:, None]
+    xe = synth.activations(_rng(98), 1, Kt)
+    Se = synth.group_scales(_rng(99), vals.shape[0], Kt, group=G)
+    ye, _ = gemv_t2(xe, Te, Se, group=G)
+    xf = [Fraction(float(v)) for v in xe[0]]
+    for n in range(vals.shape[0]):
+        ref = sum(Fraction(float(Se[n, k // G])) * int(vals[n, k]) * xf[k] for k in range(Kt))
+        ok &= abs(Fraction(ye[0, n]) - ref) <= Fraction(2 ** -40) * (abs(ref) + 1)
+    return ok
+
+
+def _planted_t2(variant):
+    def gemv_t2(x, T, S, group=128):
+        M, K = x.shape
+        N = T.shape[0]
+        sh = 2 * np.arange(16, dtype=np.uint32)
+        if variant == "msb_first":
+            sh = sh[::-1]
+        codes = ((T[:, :, None] >> sh[None, None, :]) & 3).reshape(N, -1)[:, :K]
+        if variant == "sign_magnitude_swapped":
+            t = np.where(codes & 2, np.where(codes & 1, -1.0, 1.0), 0.0)
+        elif variant == "code10_is_minus_one":
+            t = np.where(codes == 1, 1.0, np.where(codes == 0, 0.0, -1.0))
+        else:
+            t = np.where(codes & 1, np.where(codes & 2, -1.0, 1.0), 0.0)
+        sd = np.repeat(S.astype(np.float64), group, axis=1)
+        if variant == "scale_off_by_one_group":
+            sd = np.roll(sd, group, axis=1)
+        terms = x.astype(np.float64)[:, None, :] * (sd * t)[None, :, :]
+        return terms.sum(axis=2), np.abs(terms).sum(axis=2)
+    return gemv_t2
+
+
+def test_ternary_pins_accept_the_oracle(orc):
+    assert _t2_pins_pass(orc.gemv_t2, orc.gemv)
+
+
+@pytest.mark.parametrize("variant", ["msb_first", "sign_magnitude_swapped", "code10_is_minus_one",
+                                     "scale_off_by_one_group"])
+def test_ternary_planted_mistakes_are_caught(orc, variant):
+    assert not _t2_pins_pass(_planted_t2(variant), orc.gemv)
+
+
+def test_ternary_byte_accounting_reproduces_page_figures():
+    figs = json.load(open(os.path.join(GOLDEN, "page_figures.json")))
+    bits = np.log2(3) + 16 / 128                                  # information content + scale
+    assert round(bits, 2) == figs["bits_per_weight_ternary"]["value"]
+    assert round(16 / figs["bits_per_weight_ternary"]["value"], 1) == figs["compression_vs_fp16_ternary"]["value"]
+    lm, vision, emb = figs["bonsai_27b_params_breakdown_b"]["value"]
+    assert round((lm + vision + emb) * figs["bits_per_weight_ternary"]["value"] / 8, 1) == \
+        figs["bonsai_27b_ternary_gb"]["value"]
+    # 2-bit slots: 2 + 16/128 bits per weight for the language model and embedding/head (the
+    # vision tower is stored at 4 bits separately), about the page's deployed 7.2 GB
+    slot_bits = 2 + 16 / 128
+    assert synth.ternary_words(_rng(1), 4, 256).nbytes * 8 / (4 * 256) == 2.0
+    assert abs((lm + emb) * slot_bits / 8 - figs["bonsai_27b_ternary_deployed_gb"]["value"]) < 0.1
