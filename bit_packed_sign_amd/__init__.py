@@ -3,5 +3,6 @@
 The computation lives in libbin1.so (C ABI: include/bin1.h, HIP kernels in csrc/); the
 functions below are its thin torch binding.  ``synth`` holds the seeded input generators.
 """
-from .binding import (Bin1Error, ChainPlan, PatchTable, gemm_prefill, gemv, gemv_group, gemv_pm1, lib,  # noqa: F401
+from .binding import (Bin1Error, ChainPlan, PatchTable, gemm_prefill, gemm_prefill_t2, gemv, gemv_group,  # noqa: F401
+                      gemv_pm1, gemv_t2, lib,
                       rank_rows_by_scale, xor_bits_apply, xor_patch_apply, xor_patch_apply_multi)

@@ -27,6 +27,8 @@ _i = ctypes.c_int
 _SIGS = {
     "bin1_gemv": [_p, _p, _p, _p, _i, _i, _i, _p],
     "bin1_gemm_prefill": [_p, _p, _p, _p, _i, _i, _i, _p],
+    "bin1_gemv_t2": [_p, _p, _p, _p, _i, _i, _i, _p],
+    "bin1_gemm_prefill_t2": [_p, _p, _p, _p, _i, _i, _i, _p],
     "bin1_gemv_group": [_p, _i, _p, _p, _p, _p, _i, _i, _p],
     "bin1_gemv_pm1": [_p, _p, _p, _i, _i, _i, _p],
     "bin1_xor_patch_apply": [_p, _p, _i, _i, _i, _p, _p],
@@ -103,13 +105,13 @@ def _need(t: torch.Tensor, name: str, dtypes, ndim: int):
 _BITS = (torch.int32, torch.uint32)
 
 
-def _product(fn: str, x, Wbits, scales, out):
+def _product(fn: str, x, Wbits, scales, out, per_word: int = 32):
     _need(x, "x", (torch.float16,), 2)
     _need(Wbits, "Wbits", _BITS, 2)
     _need(scales, "scales", (torch.float16,), 2)
     M, K = x.shape
     N = Wbits.shape[0]
-    if Wbits.shape[1] * 32 != K or tuple(scales.shape) != (N, K // 128):
+    if Wbits.shape[1] * per_word != K or tuple(scales.shape) != (N, K // 128):
         raise ValueError(f"shapes: x {tuple(x.shape)}, Wbits {tuple(Wbits.shape)}, scales {tuple(scales.shape)}")
     if out is None:
         out = torch.empty((M, N), dtype=torch.float16, device=x.device)
@@ -126,6 +128,17 @@ def _product(fn: str, x, Wbits, scales, out):
 def gemv(x: torch.Tensor, Wbits: torch.Tensor, scales: torch.Tensor, out: Optional[torch.Tensor] = None):
     """y[M][N] (fp16) = x[M][K] (fp16) times the 1-bit weights (Wbits [N][K/32], scales [N][K/128])."""
     return _product("bin1_gemv", x, Wbits, scales, out)
+
+
+def gemv_t2(x: torch.Tensor, Tbits: torch.Tensor, scales: torch.Tensor, out: Optional[torch.Tensor] = None):
+    """y[M][N] (fp16) = x[M][K] (fp16) times ternary weights in 2-bit slots (Tbits [N][K/16],
+    scales [N][K/128])."""
+    return _product("bin1_gemv_t2", x, Tbits, scales, out, per_word=16)
+
+
+def gemm_prefill_t2(x: torch.Tensor, Tbits: torch.Tensor, scales: torch.Tensor, out: Optional[torch.Tensor] = None):
+    """Ternary prefill product, tuned for M >= 256; same arguments as gemv_t2."""
+    return _product("bin1_gemm_prefill_t2", x, Tbits, scales, out, per_word=16)
 
 
 def gemv_group(x: torch.Tensor, Wbits: Sequence[torch.Tensor], scales: Sequence[torch.Tensor],

@@ -67,14 +67,16 @@ int launched(hipError_t e, const char *what)
 }
 
 // Shared validation of the (x, Wbits, scales, y, M, K, N) products: host-side checks first.
-int check_product_host(const void *x, const void *W, const void *S, const void *y, int M, int K, int N)
+// bits: bits per weight of W (1: signs, 2: ternary slots)
+int check_product_host(const void *x, const void *W, const void *S, const void *y, int M, int K, int N,
+                       int bits = 1)
 {
     if (!x || !W || !S || !y) return fail(BIN1_ERR_NULL, "x, Wbits, scales and y must be non-NULL");
     if (M < 1 || N < 1 || K < 128 || K % 128 != 0)
         return fail(BIN1_ERR_SHAPE, "need M>=1, N>=1, K>=128, K%%128==0 (got M=%d K=%d N=%d)", M, K, N);
     if (!aligned16(x) || !aligned16(W) || !aligned16(S) || !aligned16(y))
         return fail(BIN1_ERR_ALIGN, "x, Wbits, scales and y must be 16-byte aligned");
-    const size_t xb = (size_t)M * K * 2, wb = (size_t)N * (K / 8), sb = (size_t)N * (K / 128) * 2,
+    const size_t xb = (size_t)M * K * 2, wb = (size_t)N * (K / 8) * bits, sb = (size_t)N * (K / 128) * 2,
                  yb = (size_t)M * N * 2;
     // the kernels address rows with 24-bit products and buffers with 32-bit offsets
     if (N >= (1 << 24) - 64 || xb >= (1ull << 31) || wb >= (1ull << 31) || yb >= (1ull << 31))
@@ -94,9 +96,9 @@ int check_product_device(const void *x, const void *W, const void *S, const void
     return BIN1_OK;
 }
 
-int check_product(const void *x, const void *W, const void *S, const void *y, int M, int K, int N)
+int check_product(const void *x, const void *W, const void *S, const void *y, int M, int K, int N, int bits = 1)
 {
-    int st = check_product_host(x, W, S, y, M, K, N);
+    int st = check_product_host(x, W, S, y, M, K, N, bits);
     return st ? st : check_product_device(x, W, S, y);
 }
 
@@ -443,6 +445,38 @@ int bin1_rank_rows_by_scale(const void *scales, int N, int K, int64_t *score, in
     return launched(bin1::launch_rank_rows(static_cast<const uint16_t *>(scales), N, K, score, order,
                                            static_cast<hipStream_t>(stream)),
                     "bin1_rank_rows_by_scale");
+}
+
+int bin1_gemv_t2(const void *x, const uint32_t *Tbits, const void *scales, void *y, int M, int K, int N,
+                 void *stream)
+{
+    int st = check_product(x, Tbits, scales, y, M, K, N, 2);
+    if (st) return st;
+    const hipStream_t s = static_cast<hipStream_t>(stream);
+    if (M == 1 && K <= bin1::mx_max_k()) {
+        bin1::MxSet set{};
+        set.W[0] = Tbits;
+        set.S[0] = static_cast<const uint16_t *>(scales);
+        set.y[0] = static_cast<uint16_t *>(y);
+        set.N[0] = N;
+        set.count = 1;
+        return launched(bin1::launch_gemv_mx_t2(static_cast<const uint16_t *>(x), set, K, s), "bin1_gemv_t2");
+    }
+    return launched(bin1::launch_prefill_t2(static_cast<const uint16_t *>(x), Tbits,
+                                            static_cast<const uint16_t *>(scales), static_cast<uint16_t *>(y),
+                                            M, K, N, s),
+                    "bin1_gemv_t2");
+}
+
+int bin1_gemm_prefill_t2(const void *x, const uint32_t *Tbits, const void *scales, void *y, int M, int K, int N,
+                         void *stream)
+{
+    int st = check_product(x, Tbits, scales, y, M, K, N, 2);
+    if (st) return st;
+    return launched(bin1::launch_prefill_t2(static_cast<const uint16_t *>(x), Tbits,
+                                            static_cast<const uint16_t *>(scales), static_cast<uint16_t *>(y),
+                                            M, K, N, static_cast<hipStream_t>(stream)),
+                    "bin1_gemm_prefill_t2");
 }
 
 }  // extern "C"

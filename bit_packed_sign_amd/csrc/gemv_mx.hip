@@ -78,7 +78,7 @@ __device__ __forceinline__ void limbs_fill(int K, uint8_t *lds)
     for (int i = tid; i < (nseg - full) * 16; i += 256) sc[full * 16 + i] = 0x7F7F7F7Fu;
 }
 
-template <int XT>
+template <int XT, bool T2>
 __device__ __forceinline__ void limbs_build(int K, uint8_t *lds, const XLoad<XT> &xl)
 {
     const int nseg = nseg_of(K);
@@ -96,7 +96,7 @@ __device__ __forceinline__ void limbs_build(int K, uint8_t *lds, const XLoad<XT>
             const int beta = tau >> 1, h = tau & 1;
             const int gamma = beta >> 2, t = beta & 3;
             const int sigma = 2 * (gamma >> 3) + (gamma & 1), G = (gamma & 7) >> 1;
-            convert16(p0, p1, mx, lds + (sigma * 4 + t) * kBlk, G, h,
+            convert16<T2>(p0, p1, mx, lds + (sigma * 4 + t) * kBlk, G, h,
                       reinterpret_cast<uint8_t *>(sc) + (sigma * 16 + 4 * G) * 4 + t);
         }
     }
@@ -139,14 +139,14 @@ __device__ __forceinline__ unsigned long long lane_of(unsigned long long v, int 
 // One ring slot: for each 16-row block r and each of the wave's pairs, 32 bytes of weights
 // (groups gamma0, gamma0+1) and their two scales (one dword; or two halves when K/128 is odd,
 // where a dword load could straddle rows misaligned).
-template <int SP, int R>
+template <int SP, int R, bool T2>
 struct Slot {
-    u4v w[R][SP][2];
+    u4v w[R][SP][2][T2 ? 2 : 1];        // per group: 4 binary words, or 8 ternary words
     uint32_t s[R][SP];
     uint16_t s1[R][SP];
 };
 
-template <int SP, int P, int R, bool ODD>
+template <int SP, int P, int R, bool ODD, bool T2>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 4)))
 void gemv_mx_kernel(const uint16_t *__restrict__ x, MxSet set, int K, int ntiles)
 {
@@ -155,16 +155,17 @@ void gemv_mx_kernel(const uint16_t *__restrict__ x, MxSet set, int K, int ntiles
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);      // wave-uniform
     const int n = lane & 15, g = lane >> 4;
     const int npair = (K + 1023) >> 10, nseg = 2 * npair;
-    const int wpr = K >> 5, spr = K >> 7;
+    const int wpr = T2 ? K >> 4 : K >> 5, spr = K >> 7;   // words per row: 16 or 32 weights each
+    constexpr int kGW = T2 ? 8 : 4;                      // words per scale group
     const int my_tiles = __builtin_amdgcn_readfirstlane(
         blockIdx.x < ntiles ? (ntiles - 1 - blockIdx.x) / gridDim.x + 1 : 0);   // <= 64
 
-    Slot<SP, R> ring[P];
+    Slot<SP, R, T2> ring[P];
 
     // Ring slot fill for the workgroup's it-th tile.  Slots past the last tile, rows past N
     // and groups past K get out-of-range offsets: zero data and zero scales, no traffic.
     // Row offsets use mul24 (rows < 2^24), which keeps the wait counts exact.
-    auto issue_t = [&](int row0, int N, unsigned long long Wp, unsigned long long Sp, Slot<SP, R> &sl) {
+    auto issue_t = [&](int row0, int N, unsigned long long Wp, unsigned long long Sp, Slot<SP, R, T2> &sl) {
         const __amdgpu_buffer_rsrc_t rW = rsrc(reinterpret_cast<const void *>(Wp), (unsigned)N * (unsigned)wpr * 4u);
         const __amdgpu_buffer_rsrc_t rS = rsrc(reinterpret_cast<const void *>(Sp), (unsigned)N * (unsigned)spr * 2u);
 #pragma unroll
@@ -175,10 +176,14 @@ void gemv_mx_kernel(const uint16_t *__restrict__ x, MxSet set, int K, int ntiles
             for (int q = 0; q < SP; ++q) {
                 const int gam = 8 * (wave + 4 * q) + 2 * g;     // this lane's first group
                 const bool ok0 = rok && gam < spr, ok1 = rok && gam + 1 < spr;
-                const unsigned ow = (mul24((unsigned)row, (unsigned)wpr) + 4u * gam) * 4u;
+                const unsigned ow = (mul24((unsigned)row, (unsigned)wpr) + (unsigned)kGW * gam) * 4u;
                 const unsigned os = (mul24((unsigned)row, (unsigned)spr) + gam) * 2u;
-                sl.w[r][q][0] = __builtin_amdgcn_raw_buffer_load_b128(rW, ok0 ? ow : kOob, 0, kNT);
-                sl.w[r][q][1] = __builtin_amdgcn_raw_buffer_load_b128(rW, ok1 ? ow + 16u : kOob, 0, kNT);
+#pragma unroll
+                for (int v = 0; v < (T2 ? 2 : 1); ++v) {
+                    sl.w[r][q][0][v] = __builtin_amdgcn_raw_buffer_load_b128(rW, ok0 ? ow + 16u * v : kOob, 0, kNT);
+                    sl.w[r][q][1][v] =
+                        __builtin_amdgcn_raw_buffer_load_b128(rW, ok1 ? ow + 4u * kGW + 16u * v : kOob, 0, kNT);
+                }
                 if (ODD) {
                     sl.s[r][q] = __builtin_amdgcn_raw_buffer_load_b16(rS, ok0 ? os : kOob, 0, 0);
                     sl.s1[r][q] = __builtin_amdgcn_raw_buffer_load_b16(rS, ok1 ? os + 2u : kOob, 0, 0);
@@ -189,7 +194,7 @@ void gemv_mx_kernel(const uint16_t *__restrict__ x, MxSet set, int K, int ntiles
         }
     };
     // the workgroup's it-th tile from the lane table (slots past the last tile load nothing)
-    auto issue = [&](const TileTab &tab, int it, Slot<SP, R> &sl) {
+    auto issue = [&](const TileTab &tab, int it, Slot<SP, R, T2> &sl) {
         const int L = it & 63;
         issue_t(lane_of(tab.row0, L), it < my_tiles ? lane_of(tab.N, L) : 0, lane_of(tab.W, L), lane_of(tab.S, L), sl);
     };
@@ -209,7 +214,7 @@ void gemv_mx_kernel(const uint16_t *__restrict__ x, MxSet set, int K, int ntiles
 #pragma unroll
     for (int p = 1; p < P; ++p) issue(tab, p, ring[p]);
     __syncthreads();                                  // zero-filled limb area visible
-    limbs_build<XT>(K, lds, xl);
+    limbs_build<XT, T2>(K, lds, xl);
     __syncthreads();                                  // limbs visible
 
     const uint32_t *sc = reinterpret_cast<const uint32_t *>(lds + nseg * 4 * kBlk);
@@ -258,14 +263,24 @@ void gemv_mx_kernel(const uint16_t *__restrict__ x, MxSet set, int K, int ntiles
                                              : (gam + 1 < spr ? h2f((uint16_t)(sv >> 16)) : 0.f);
 #pragma unroll
                         for (int h = 0; h < 2; ++h) {
-                            const u4v w = ring[p].w[r][q][h];
                             float4v c = {0.f, 0.f, 0.f, 0.f};
-                            c = mma<0>(A[q][h][0], w.x, scA[q][h], c);
-                            c = mma<1>(A[q][h][1], w.y, scA[q][h], c);
-                            c = mma<2>(A[q][h][2], w.z, scA[q][h], c);
-                            c = mma<3>(A[q][h][3], w.w, scA[q][h], c);
-                            // B held -w, so the group's partial is -(c0+c1+c2+c3)
-                            acc[r] = fmaf(-(h ? s1 : s0), (c[0] + c[1]) + (c[2] + c[3]), acc[r]);
+                            if constexpr (T2) {
+                                // MFMA t takes the group's words 2t and 2t + 1 (32 weights)
+                                const u4v w0 = ring[p].w[r][q][h][0], w1 = ring[p].w[r][q][h][T2 ? 1 : 0];
+                                c = mma_b<0>(A[q][h][0], unpack_t2(w0.x, w0.y), scA[q][h], c);
+                                c = mma_b<1>(A[q][h][1], unpack_t2(w0.z, w0.w), scA[q][h], c);
+                                c = mma_b<2>(A[q][h][2], unpack_t2(w1.x, w1.y), scA[q][h], c);
+                                c = mma_b<3>(A[q][h][3], unpack_t2(w1.z, w1.w), scA[q][h], c);
+                                acc[r] = fmaf(h ? s1 : s0, (c[0] + c[1]) + (c[2] + c[3]), acc[r]);
+                            } else {
+                                const u4v w = ring[p].w[r][q][h][0];
+                                c = mma<0>(A[q][h][0], w.x, scA[q][h], c);
+                                c = mma<1>(A[q][h][1], w.y, scA[q][h], c);
+                                c = mma<2>(A[q][h][2], w.z, scA[q][h], c);
+                                c = mma<3>(A[q][h][3], w.w, scA[q][h], c);
+                                // B held -w, so the group's partial is -(c0+c1+c2+c3)
+                                acc[r] = fmaf(-(h ? s1 : s0), (c[0] + c[1]) + (c[2] + c[3]), acc[r]);
+                            }
                         }
                     }
                 }
@@ -301,11 +316,11 @@ constexpr size_t shm_bytes(int K, int rows_per_wg)
     return (size_t)(2 * ((K + 1023) >> 10)) * (4 * kBlk + 64) + (size_t)rows_per_wg * 4 * 4;
 }
 
-template <int SP, int P, int R, bool ODD>
+template <int SP, int P, int R, bool ODD, bool T2>
 hipError_t launch_mx(const uint16_t *x, const MxSet &set0, int K, hipStream_t st)
 {
     static const hipError_t attr = hipFuncSetAttribute(
-        reinterpret_cast<const void *>(&gemv_mx_kernel<SP, P, R, ODD>),
+        reinterpret_cast<const void *>(&gemv_mx_kernel<SP, P, R, ODD, T2>),
         hipFuncAttributeMaxDynamicSharedMemorySize, (int)shm_bytes(kMaxPairs * 1024, kMaxTileRows));
     if (attr != hipSuccess) return attr;
     MxSet set = set0;
@@ -322,12 +337,12 @@ hipError_t launch_mx(const uint16_t *x, const MxSet &set0, int K, hipStream_t st
     const int need = (tiles + kMaxT - 1) / kMaxT;
     const int grid = tiles < cap ? tiles : (need > cap ? need : cap);
     const int rows_per_wg = (tiles + grid - 1) / grid * 16 * R;
-    hipLaunchKernelGGL((gemv_mx_kernel<SP, P, R, ODD>), dim3(grid), dim3(256), shm_bytes(K, rows_per_wg),
+    hipLaunchKernelGGL((gemv_mx_kernel<SP, P, R, ODD, T2>), dim3(grid), dim3(256), shm_bytes(K, rows_per_wg),
                        st, x, set, K, tiles);
     return hipGetLastError();
 }
 
-template <bool ODD>
+template <bool ODD, bool T2>
 hipError_t dispatch_mx(const uint16_t *x, const MxSet &set, int K, hipStream_t st)
 {
     const int SP = (((K + 1023) >> 10) + 3) / 4;        // pairs per wave
@@ -345,16 +360,21 @@ hipError_t dispatch_mx(const uint16_t *x, const MxSet &set, int K, hipStream_t s
     const int cap = SP <= 2 ? 2 * 256 : 256;
     const bool one16 = t16 <= cap, one = t32 <= cap, few16 = t16 <= 3 * cap;
     switch (SP) {
-    case 1: return one16 ? launch_mx<1, 1, 1, ODD>(x, set, K, st)
-                 : one   ? launch_mx<1, 1, 2, ODD>(x, set, K, st)
-                 : few16 ? launch_mx<1, 3, 1, ODD>(x, set, K, st) : launch_mx<1, 3, 2, ODD>(x, set, K, st);
-    case 2: return one16 ? launch_mx<2, 1, 1, ODD>(x, set, K, st)
-                 : one   ? launch_mx<2, 1, 2, ODD>(x, set, K, st)
-                 : few16 ? launch_mx<2, 2, 1, ODD>(x, set, K, st) : launch_mx<2, 2, 2, ODD>(x, set, K, st);
-    case 3: return one16 ? launch_mx<3, 1, 1, ODD>(x, set, K, st)
-                 : one   ? launch_mx<3, 1, 2, ODD>(x, set, K, st) : launch_mx<3, 2, 2, ODD>(x, set, K, st);
-    case 4: return launch_mx<4, 1, 2, ODD>(x, set, K, st);
-    default: return launch_mx<5, 1, 2, ODD>(x, set, K, st);
+    case 1: return one16 ? launch_mx<1, 1, 1, ODD, T2>(x, set, K, st)
+                 : one   ? launch_mx<1, 1, 2, ODD, T2>(x, set, K, st)
+                 : few16 ? launch_mx<1, 3, 1, ODD, T2>(x, set, K, st) : launch_mx<1, 3, 2, ODD, T2>(x, set, K, st);
+    case 2: return one16 ? launch_mx<2, 1, 1, ODD, T2>(x, set, K, st)
+                 : one   ? launch_mx<2, 1, 2, ODD, T2>(x, set, K, st)
+                 : few16 ? launch_mx<2, 2, 1, ODD, T2>(x, set, K, st) : launch_mx<2, 2, 2, ODD, T2>(x, set, K, st);
+    case 3: return one16 ? launch_mx<3, 1, 1, ODD, T2>(x, set, K, st)
+                 : one   ? launch_mx<3, 1, 2, ODD, T2>(x, set, K, st) : launch_mx<3, 2, 2, ODD, T2>(x, set, K, st);
+    // (ternary rows are twice as many bytes: 16-row tiles keep the ring in registers)
+    case 4:
+        if constexpr (T2) return launch_mx<4, 1, 1, ODD, T2>(x, set, K, st);
+        else return launch_mx<4, 1, 2, ODD, T2>(x, set, K, st);
+    default:
+        if constexpr (T2) return launch_mx<5, 1, 1, ODD, T2>(x, set, K, st);
+        else return launch_mx<5, 1, 2, ODD, T2>(x, set, K, st);
     }
 }
 
@@ -364,7 +384,12 @@ int mx_max_k() { return kMaxPairs * 1024; }
 
 hipError_t launch_gemv_mx(const uint16_t *x, const MxSet &set, int K, hipStream_t st)
 {
-    return ((K >> 7) & 1) ? dispatch_mx<true>(x, set, K, st) : dispatch_mx<false>(x, set, K, st);
+    return ((K >> 7) & 1) ? dispatch_mx<true, false>(x, set, K, st) : dispatch_mx<false, false>(x, set, K, st);
+}
+
+hipError_t launch_gemv_mx_t2(const uint16_t *x, const MxSet &set, int K, hipStream_t st)
+{
+    return ((K >> 7) & 1) ? dispatch_mx<true, true>(x, set, K, st) : dispatch_mx<false, true>(x, set, K, st);
 }
 
 }  // namespace bin1

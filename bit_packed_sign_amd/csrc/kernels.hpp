@@ -60,6 +60,8 @@ hipError_t launch_gemv_chain(ChainHeader *hdr, int *done, const ChainStage *tabl
 // Largest K the block-scaled decode kernel takes (longer rows use the select kernel).
 int mx_max_k();
 hipError_t launch_gemv_mx(const uint16_t *x, const MxSet &set, int K, hipStream_t st);
+// The same product for ternary weights in 2-bit slots (W pointers of the set: uint32 [N][K/16]).
+hipError_t launch_gemv_mx_t2(const uint16_t *x, const MxSet &set, int K, hipStream_t st);
 
 hipError_t launch_gemv(const uint16_t *x, const uint32_t *W, const uint16_t *S, uint16_t *y,
                        int M, int K, int N, hipStream_t st);
@@ -68,6 +70,9 @@ hipError_t launch_gemv(const uint16_t *x, const uint32_t *W, const uint16_t *S, 
 hipError_t launch_gemv_smallm(const uint16_t *x, const MxSet &set, int M, int K, hipStream_t st);
 hipError_t launch_prefill(const uint16_t *x, const uint32_t *W, const uint16_t *S, uint16_t *y,
                           int M, int K, int N, hipStream_t st);
+// Ternary weights in 2-bit slots: T uint32 [N][K/16].
+hipError_t launch_prefill_t2(const uint16_t *x, const uint32_t *T, const uint16_t *S, uint16_t *y,
+                             int M, int K, int N, hipStream_t st);
 hipError_t launch_pm1(const uint32_t *A, const uint32_t *W, int32_t *y, int M, int K, int N,
                       hipStream_t st);
 hipError_t launch_xor_bits(uint32_t *const *Wtab, const int32_t *Ktab, const int32_t *Ntab, int nmat,

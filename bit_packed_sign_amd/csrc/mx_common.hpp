@@ -53,10 +53,32 @@ __device__ __forceinline__ int8v load_a(const uint8_t *blk, int lo, int hi)
     return a;
 }
 
+// fp4 (e2m1) expansion of two words of ternary 2-bit slots (low bit: nonzero, high bit:
+// negative), 32 weights: the nibble's exponent bit 1 takes the slot's nonzero bit and its sign
+// bit 3 the slot's negative bit, giving 0, +1.0 or -1.0 (code 10 gives -0).  Register 0 holds
+// the even slots of wa, 1 its odd slots, 2 and 3 those of wb, so B element j is weight
+// k(j) = 16 (j / 16) + 2 (j % 8) + (j / 8) % 2 of the 32.
+__device__ __forceinline__ int8v unpack_t2(uint32_t wa, uint32_t wb)
+{
+    int8v b;
+    b[0] = (int)(((wa << 1) & 0x22222222u) | ((wa << 2) & 0x88888888u));
+    b[1] = (int)(((wa >> 1) & 0x22222222u) | (wa & 0x88888888u));
+    b[2] = (int)(((wb << 1) & 0x22222222u) | ((wb << 2) & 0x88888888u));
+    b[3] = (int)(((wb >> 1) & 0x22222222u) | (wb & 0x88888888u));
+    b[4] = b[5] = b[6] = b[7] = 0;
+    return b;
+}
+
+template <int T>
+__device__ __forceinline__ float4v mma_b(const int8v &a, const int8v &b, int scA, float4v c)
+{
+    return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a, b, c, 0, 4, T, scA, 0, 127);
+}
+
 template <int T>
 __device__ __forceinline__ float4v mma(const int8v &a, uint32_t w, int scA, float4v c)
 {
-    return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a, unpack_fp4(w), c, 0, 4, T, scA, 0, 127);
+    return mma_b<T>(a, unpack_fp4(w), scA, c);
 }
 
 // Lane offsets of the A operand inside a limb block: rows m = 4G + r of the MFMA are
@@ -73,11 +95,18 @@ __device__ __forceinline__ void a_offsets(int lane, int &lo, int &hi)
 // p0, p1: the 16 fp16 values; `mx` must already be the max |x| over the whole 32-block.
 // blk: the block of (segment, word t); G: the block's MFMA K-block; scbyte: E8M0 bytes of
 // rows 4G..4G+3 for word t (stride 4 bytes), written by the h == 0 half.
-// Element j of a block row pairs with weight bit pi(j) = 4*(j%8) + j/8 (unpack_fp4 order):
-// activation i of the half sits at byte j = 8*(i%4) + 4h + i/4.
+// Element j of a block row must pair with the weight the B operand puts there:
+//  * binary (unpack_fp4): bit pi(j) = 4*(j%8) + j/8, so activation i of the half sits at byte
+//    j = 8*(i%4) + 4h + i/4 -- dword 2c + h holds activations c, 4+c, 8+c, 12+c;
+//  * ternary (unpack_t2): weight k(j) = 16 (j/16) + 2 (j%8) + (j/8)%2, so activation i sits at
+//    byte 16h + 8 (i%2) + i/2 -- dword 4h + c holds activations 8m + e, 8m + 2 + e, 8m + 4 + e,
+//    8m + 6 + e for c = 2e + m.
+template <bool T2 = false>
 __device__ __forceinline__ void convert16(const u4v p0, const u4v p1, float mx, uint8_t *blk, int G, int h,
                                           uint8_t *scbyte)
 {
+    // activation of byte b of dword slot c
+    auto idx = [](int c, int b) { return T2 ? 8 * (c & 1) + 2 * b + (c >> 1) : 4 * b + c; };
     const uint32_t hw[8] = {p0.x, p0.y, p0.z, p0.w, p1.x, p1.y, p1.z, p1.w};
     float u[16];
 #pragma unroll
@@ -91,9 +120,9 @@ __device__ __forceinline__ void convert16(const u4v p0, const u4v p1, float mx, 
         int d[4];
 #pragma unroll
         for (int c = 0; c < 4; ++c) {
-            int v = __builtin_amdgcn_cvt_pk_fp8_f32(u[c], u[4 + c], 0, false);
-            d[c] = __builtin_amdgcn_cvt_pk_fp8_f32(u[8 + c], u[12 + c], v, true);
-            *reinterpret_cast<int *>(blk + (4 * G + r) * 32 + (2 * c + h) * 4) = d[c];
+            int v = __builtin_amdgcn_cvt_pk_fp8_f32(u[idx(c, 0)], u[idx(c, 1)], 0, false);
+            d[c] = __builtin_amdgcn_cvt_pk_fp8_f32(u[idx(c, 2)], u[idx(c, 3)], v, true);
+            *reinterpret_cast<int *>(blk + (4 * G + r) * 32 + (T2 ? 4 * h + c : 2 * c + h) * 4) = d[c];
         }
         if (h == 0) scbyte[r * 4] = (uint8_t)(127 + e0 - 7 - 4 * r);
         if (r < 3) {
@@ -102,10 +131,10 @@ __device__ __forceinline__ void convert16(const u4v p0, const u4v p1, float mx, 
             // fma 16 u - 16 q rounds nothing.
 #pragma unroll
             for (int c = 0; c < 4; ++c) {
-                u[c] = fmaf(u[c], 16.f, -16.f * __builtin_amdgcn_cvt_f32_fp8(d[c], 0));
-                u[4 + c] = fmaf(u[4 + c], 16.f, -16.f * __builtin_amdgcn_cvt_f32_fp8(d[c], 1));
-                u[8 + c] = fmaf(u[8 + c], 16.f, -16.f * __builtin_amdgcn_cvt_f32_fp8(d[c], 2));
-                u[12 + c] = fmaf(u[12 + c], 16.f, -16.f * __builtin_amdgcn_cvt_f32_fp8(d[c], 3));
+                u[idx(c, 0)] = fmaf(u[idx(c, 0)], 16.f, -16.f * __builtin_amdgcn_cvt_f32_fp8(d[c], 0));
+                u[idx(c, 1)] = fmaf(u[idx(c, 1)], 16.f, -16.f * __builtin_amdgcn_cvt_f32_fp8(d[c], 1));
+                u[idx(c, 2)] = fmaf(u[idx(c, 2)], 16.f, -16.f * __builtin_amdgcn_cvt_f32_fp8(d[c], 2));
+                u[idx(c, 3)] = fmaf(u[idx(c, 3)], 16.f, -16.f * __builtin_amdgcn_cvt_f32_fp8(d[c], 3));
             }
         }
     }

@@ -69,11 +69,29 @@ __device__ __forceinline__ half8v expand_pairs(uint32_t nw, uint32_t s2abs)
     return __builtin_bit_cast(half8v, d);
 }
 
+// Ternary (2-bit slots: low bit nonzero, high bit negative) B dwords of a 16-weight word:
+// pair d = (slot d, slot d + 8) of nw.  The sign bits 2d + 1 and 2d + 17 land on bits 15 and 31
+// with one shift; the nonzero bits 2d and 2d + 16, moved to bits 0 and 16, times |s| put |s|
+// (or 0) into each half with one 24-bit multiply.
+template <int D>
+__device__ __forceinline__ uint32_t expand_t2_pair(uint32_t nw, uint32_t sabs)
+{
+    return ((nw << (14 - 2 * D)) & 0x80008000u) | mul24((nw >> (2 * D)) & 0x00010001u, sabs);
+}
+
+__device__ __forceinline__ half8v expand_t2(uint32_t nw, uint32_t sabs)
+{
+    const u4v d{expand_t2_pair<0>(nw, sabs), expand_t2_pair<1>(nw, sabs), expand_t2_pair<2>(nw, sabs),
+                expand_t2_pair<3>(nw, sabs)};
+    return __builtin_bit_cast(half8v, d);
+}
+
 }  // namespace
 
 // BM x BN tile, WM x WN waves; a wave computes (BM / WM) x (BN / WN) as FI x FJ 32x32 fragments.
 // WPE waves per SIMD (from one or several workgroups per CU).
-template <int BM, int WM, int WN, int WPE>
+// T2: ternary weights in 2-bit slots (16 per word) instead of sign bits (32 per word).
+template <int BM, int WM, int WN, int WPE, bool T2>
 __global__ __launch_bounds__(64 * WM * WN) __attribute__((amdgpu_waves_per_eu(WPE, WPE)))
 void prefill_kernel(const uint16_t *__restrict__ x, const uint32_t *__restrict__ W,
                     const uint16_t *__restrict__ S, uint16_t *__restrict__ y, int M, int K, int N,
@@ -89,16 +107,18 @@ void prefill_kernel(const uint16_t *__restrict__ x, const uint32_t *__restrict__
     const int wm = wave / WN, wn = wave % WN;
     const int bm = blockIdx.x % tiles_m, bn = blockIdx.x / tiles_m;
     const int m0 = bm * BM, n0 = bn * BN;
-    const int wpr = K >> 5, spr = K >> 7, nk = K / BK;
+    const int wpr = T2 ? K >> 4 : K >> 5, spr = K >> 7, nk = K / BK;
+    constexpr int kWS = T2 ? 8 : 4;                   // words of a row per K step
     const int fr = lane & 31, fh = lane >> 5;         // MFMA operand row / column and k-half
 
     const __amdgpu_buffer_rsrc_t rx = rsrc(x, (unsigned)M * (unsigned)K * 2u);
     const __amdgpu_buffer_rsrc_t rW = rsrc(W, (unsigned)N * (unsigned)wpr * 4u);
     const __amdgpu_buffer_rsrc_t rS = rsrc(S, (unsigned)N * (unsigned)spr * 2u);
 
-    // ---- activation staging.  Unit i of a thread (u = t + kThreads i) is one (row, word,
-    // half-word h) of a step: the 8-wide chunks h and h + 2 of that word, interleaved into 16
-    // permuted positions (32 bytes).  Eight consecutive lanes take units 0..3 of two adjacent
+    // ---- activation staging.  Unit i of a thread (u = t + kThreads i) is 16 permuted positions
+    // (32 bytes) of a row in a step, unit index idx: binary, (word idx / 2, half idx % 2) -- the
+    // 8-wide chunks h and h + 2 of that 32-weight word, interleaved; ternary, 16-weight word idx
+    // -- its chunks 0 and 1, interleaved.  Eight consecutive lanes take units 0..3 of two adjacent
     // rows, so the rows' 68-dword LDS stride puts their 16-byte writes in distinct banks, and
     // four lanes read 64 contiguous bytes of a row.
     unsigned a_gofs[kAUnits];                         // byte offset of the unit in x at step 0
@@ -109,14 +129,15 @@ void prefill_kernel(const uint16_t *__restrict__ x, const uint32_t *__restrict__
         const int row = 2 * (c % (BM / 2)) + ((u >> 2) & 1);
         const int idx = (u & 3) + 4 * (c / (BM / 2)), wd = idx >> 1, h = idx & 1;
         const int m = m0 + row;
-        a_gofs[i] = m < M ? ((unsigned)m * (unsigned)K + (unsigned)(32 * wd + 8 * h)) * 2u : kOob;
-        a_lofs[i] = row * LDK + 32 * wd + 16 * h;
+        const int k0 = T2 ? 16 * idx : 32 * wd + 8 * h;
+        a_gofs[i] = m < M ? ((unsigned)m * (unsigned)K + (unsigned)k0) * 2u : kOob;
+        a_lofs[i] = row * LDK + 16 * idx;
     }
     auto load_a1 = [&](int ks, int i, u4v (&r)[2]) {
         const bool ok = a_gofs[i] != kOob && ks < nk;
         const unsigned off = a_gofs[i] + (unsigned)(ks * BK * 2);
         r[0] = __builtin_amdgcn_raw_buffer_load_b128(rx, ok ? off : kOob, 0, 0);
-        r[1] = __builtin_amdgcn_raw_buffer_load_b128(rx, ok ? off + 32u : kOob, 0, 0);
+        r[1] = __builtin_amdgcn_raw_buffer_load_b128(rx, ok ? off + (T2 ? 16u : 32u) : kOob, 0, 0);
     };
     auto store_a1 = [&](uint16_t *buf, int i, const u4v (&r)[2]) {
         u4v o0, o1;
@@ -134,7 +155,7 @@ void prefill_kernel(const uint16_t *__restrict__ x, const uint32_t *__restrict__
         for (int i = 0; i < kAUnits; ++i) store_a1(buf, i, ra[i]);
     };
     // ---- weight bits of this wave's FJ column fragments: row n0 + TN wn + 32 j + fr, the four
-    // words of a step and the group scale
+    // (ternary: eight) words of a step and the group scale
     unsigned b_wofs[FJ], b_sofs[FJ];                   // byte offsets of this lane's rows at step 0
 #pragma unroll
     for (int j = 0; j < FJ; ++j) {
@@ -142,11 +163,14 @@ void prefill_kernel(const uint16_t *__restrict__ x, const uint32_t *__restrict__
         b_wofs[j] = n < N ? (unsigned)n * (unsigned)wpr * 4u : kOob;
         b_sofs[j] = n < N ? (unsigned)n * (unsigned)spr * 2u : kOob;
     }
-    auto load_b = [&](int ks, u4v (&rw)[FJ], uint32_t (&rs)[FJ]) {
+    auto load_b = [&](int ks, u4v (&rw)[FJ][kWS / 4], uint32_t (&rs)[FJ]) {
 #pragma unroll
         for (int j = 0; j < FJ; ++j) {
             const bool ok = b_wofs[j] != kOob && ks < nk;
-            rw[j] = __builtin_amdgcn_raw_buffer_load_b128(rW, ok ? b_wofs[j] + (unsigned)(16 * ks) : kOob, 0, 0);
+#pragma unroll
+            for (int v = 0; v < kWS / 4; ++v)
+                rw[j][v] = __builtin_amdgcn_raw_buffer_load_b128(
+                    rW, ok ? b_wofs[j] + (unsigned)(4 * kWS * ks + 16 * v) : kOob, 0, 0);
             rs[j] = __builtin_amdgcn_raw_buffer_load_b16(rS, ok ? b_sofs[j] + (unsigned)(2 * ks) : kOob, 0, 0);
         }
     };
@@ -165,7 +189,7 @@ void prefill_kernel(const uint16_t *__restrict__ x, const uint32_t *__restrict__
     // unconditional (out-of-range offsets past the last step) so the loop is straight-line and
     // each wait covers only the loads it needs.
     u4v ra[kAUnits][2];
-    u4v rw[FJ];
+    u4v rw[FJ][kWS / 4];
     uint32_t rs[FJ];
     load_a(0, ra);
     load_b(0, rw, rs);
@@ -180,16 +204,23 @@ void prefill_kernel(const uint16_t *__restrict__ x, const uint32_t *__restrict__
         const uint16_t *cur = lds + P * BUF_HALVES;
         uint16_t *nxt = lds + (P ^ 1) * BUF_HALVES;
         // this step's weights: fold each scale's sign into the bits, shift by this lane's k-half
-        uint32_t nw[FJ][4], s2[FJ];
+        uint32_t nw[FJ][kWS], s2[FJ];
 #pragma unroll
         for (int j = 0; j < FJ; ++j) {
             const uint32_t sv = rs[j] & 0xFFFFu;
-            const uint32_t flip = (sv & 0x8000u) ? 0u : 0xFFFFFFFFu;   // bit 1 of nw: negative product
-            s2[j] = (sv & 0x7FFFu) * 0x00010001u;
-            nw[j][0] = (rw[j].x ^ flip) >> (4 * fh);
-            nw[j][1] = (rw[j].y ^ flip) >> (4 * fh);
-            nw[j][2] = (rw[j].z ^ flip) >> (4 * fh);
-            nw[j][3] = (rw[j].w ^ flip) >> (4 * fh);
+            if constexpr (T2) {
+                // a negative scale flips every slot's negative bit; lane half fh takes slots
+                // 4 fh .. 4 fh + 3 (and + 8) of each word
+                const uint32_t flip = (sv & 0x8000u) ? 0xAAAAAAAAu : 0u;
+                s2[j] = sv & 0x7FFFu;
+#pragma unroll
+                for (int v = 0; v < 8; ++v) nw[j][v] = (rw[j][v / 4][v % 4] ^ flip) >> (8 * fh);
+            } else {
+                const uint32_t flip = (sv & 0x8000u) ? 0u : 0xFFFFFFFFu;   // bit 1 of nw: negative product
+                s2[j] = (sv & 0x7FFFu) * 0x00010001u;
+#pragma unroll
+                for (int v = 0; v < 4; ++v) nw[j][v] = (rw[j][0][v] ^ flip) >> (4 * fh);
+            }
         }
         load_b(ks + 1, rw, rs);                       // (past the last step: loads nothing)
         const uint16_t *as = cur + (wm * TM + fr) * LDK + 8 * fh;
@@ -202,9 +233,14 @@ void prefill_kernel(const uint16_t *__restrict__ x, const uint32_t *__restrict__
         for (int i = 0; i < FI; ++i) a[0][i] = *reinterpret_cast<const half8v *>(as + 32 * i * LDK);
         // B operands one substep ahead: a substep's MFMAs depend on nothing computed in it, so
         // the next substep's sign expansion, A reads and staging run in their shadow
+        // substep sub covers 16 k: binary word sub / 2, half sub % 2; ternary word sub
+        auto expand = [&](int j, int sub) {
+            if constexpr (T2) return expand_t2(nw[j][sub], s2[j]);
+            else return (sub & 1) ? expand_pairs<8>(nw[j][sub >> 1], s2[j]) : expand_pairs<0>(nw[j][sub >> 1], s2[j]);
+        };
         half8v b[2][FJ];
 #pragma unroll
-        for (int j = 0; j < FJ; ++j) b[0][j] = expand_pairs<0>(nw[j][0], s2[j]);
+        for (int j = 0; j < FJ; ++j) b[0][j] = expand(j, 0);
 #pragma unroll
         for (int sub = 0; sub < 8; ++sub) {           // 16 k per MFMA: word sub / 2, half sub % 2
             const int c = sub & 1;
@@ -214,13 +250,11 @@ void prefill_kernel(const uint16_t *__restrict__ x, const uint32_t *__restrict__
                 for (int j = 0; j < FJ; ++j)
                     acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(a[c][i], b[c][j], acc[i][j], 0, 0, 0);
             if (sub < 7) {
-                const int wd1 = (sub + 1) >> 1;
 #pragma unroll
                 for (int i = 0; i < FI; ++i)
                     a[c ^ 1][i] = *reinterpret_cast<const half8v *>(as + 32 * i * LDK + 16 * (sub + 1));
 #pragma unroll
-                for (int j = 0; j < FJ; ++j)
-                    b[c ^ 1][j] = ((sub + 1) & 1) ? expand_pairs<8>(nw[j][wd1], s2[j]) : expand_pairs<0>(nw[j][wd1], s2[j]);
+                for (int j = 0; j < FJ; ++j) b[c ^ 1][j] = expand(j, sub + 1);
             }
 #pragma unroll
             for (int i = sub; i < kAUnits; i += 8) {
@@ -251,17 +285,17 @@ void prefill_kernel(const uint16_t *__restrict__ x, const uint32_t *__restrict__
 }
 
 namespace {
-template <int BM, int WM, int WN, int WPE>
+template <int BM, int WM, int WN, int WPE, bool T2>
 hipError_t launch_prefill_t(const uint16_t *x, const uint32_t *W, const uint16_t *S, uint16_t *y, int M, int K,
                             int N, hipStream_t st)
 {
     constexpr int shm = 2 * BM * LDK * 2;
     static const hipError_t attr = hipFuncSetAttribute(
-        reinterpret_cast<const void *>(&prefill_kernel<BM, WM, WN, WPE>), hipFuncAttributeMaxDynamicSharedMemorySize,
+        reinterpret_cast<const void *>(&prefill_kernel<BM, WM, WN, WPE, T2>), hipFuncAttributeMaxDynamicSharedMemorySize,
         shm);
     if (attr != hipSuccess) return attr;
     const int tm = (M + BM - 1) / BM, tn = (N + BN - 1) / BN;
-    hipLaunchKernelGGL((prefill_kernel<BM, WM, WN, WPE>), dim3(tm * tn), dim3(64 * WM * WN), shm, st, x, W, S, y,
+    hipLaunchKernelGGL((prefill_kernel<BM, WM, WN, WPE, T2>), dim3(tm * tn), dim3(64 * WM * WN), shm, st, x, W, S, y,
                        M, K, N, tm);
     return hipGetLastError();
 }
@@ -272,7 +306,13 @@ hipError_t launch_prefill(const uint16_t *x, const uint32_t *W, const uint16_t *
 {
     // four waves of 128 x 96, one per SIMD: measured fastest of the 4- and 8-wave layouts
     // (the expansion and staging VALU work does not overlap the MFMAs of a second wave)
-    return launch_prefill_t<256, 2, 2, 1>(x, W, S, y, M, K, N, st);
+    return launch_prefill_t<256, 2, 2, 1, false>(x, W, S, y, M, K, N, st);
+}
+
+hipError_t launch_prefill_t2(const uint16_t *x, const uint32_t *T, const uint16_t *S, uint16_t *y,
+                             int M, int K, int N, hipStream_t st)
+{
+    return launch_prefill_t<256, 2, 2, 1, true>(x, T, S, y, M, K, N, st);
 }
 
 }  // namespace bin1

@@ -94,6 +94,22 @@ int bin1_gemv_group(const void *x, int count, const uint32_t *const *Wbits,
 int bin1_gemm_prefill(const void *x, const uint32_t *Wbits, const void *scales, void *y,
                       int M, int K, int N, void *stream);
 
+/* Ternary g128 products ["Bonsai 27B", section on the ternary weight format: each weight
+ * t in {-1, 0, +1}, w = s_g * t, one fp16 scale per group of 128; its deployment section:
+ * current kernels keep each ternary value in a 2-bit slot]:
+ *   y[m][n] = sum_k s[n][k/128] * t(n,k) * x[m][k]
+ *   Tbits  uint32 [N][K/16]: weight k of row n is the 2-bit slot at bits 2(k%16), 2(k%16)+1
+ *          of word [n][k/16] (LSB first); low bit = nonzero, high bit = negative: 00 -> 0,
+ *          01 -> +1, 11 -> -1, and 10 reads as 0.
+ * Everything else (x, scales, y, requirements, errors, streams) is as for bin1_gemv and
+ * bin1_gemm_prefill.  bin1_gemv_t2 runs M == 1 on the block-scaled matrix cores and other M
+ * on the prefill kernel; bin1_gemm_prefill_t2 is tuned for M >= 256.  There is no XOR patch
+ * for ternary weights (the Bankai page: XOR patches need true binary codes). */
+int bin1_gemv_t2(const void *x, const uint32_t *Tbits, const void *scales, void *y,
+                 int M, int K, int N, void *stream);
+int bin1_gemm_prefill_t2(const void *x, const uint32_t *Tbits, const void *scales, void *y,
+                         int M, int K, int N, void *stream);
+
 /* +-1 activations times +-1 weights, exact:
  *   y[m][n] = sum_k a(m,k) * w(n,k) = K - 2 * popcount(Abits[m] xor Wbits[n])  (int32).
  * Scales are not used.  ["PrismML Bonsai -- 1.15GB ...", section "What 1-bit is"] */

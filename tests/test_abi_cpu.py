@@ -29,6 +29,7 @@ def test_header_declares_the_entry_points():
     names = _declared()
     for fn in ["bin1_gemv", "bin1_gemv_group", "bin1_gemm_prefill", "bin1_gemv_pm1", "bin1_xor_patch_apply",
                "bin1_xor_patch_apply_multi", "bin1_xor_bits_apply", "bin1_rank_rows_by_scale",
+               "bin1_gemv_t2", "bin1_gemm_prefill_t2",
                "bin1_status_string", "bin1_last_error", "bin1_abi_version"]:
         assert fn in names
 
@@ -54,7 +55,7 @@ def test_version_and_status_strings(L):
 FAKE = 0x10000  # 16-byte-aligned fake address: never dereferenced, checks fail before use
 
 
-@pytest.mark.parametrize("fn", ["bin1_gemv", "bin1_gemm_prefill"])
+@pytest.mark.parametrize("fn", ["bin1_gemv", "bin1_gemm_prefill", "bin1_gemv_t2", "bin1_gemm_prefill_t2"])
 def test_product_validation(L, fn):
     f = getattr(L, fn)
     assert f(None, FAKE, FAKE, FAKE, 1, 128, 1, None) == -1

@@ -1,0 +1,102 @@
+"""GPU parity of the ternary g128 products (2-bit slots) against the fp64 oracle: the batch-1
+block-scaled kernel (every K variant, ragged N, odd group counts), other batch sizes and the
+prefill kernel, zero and never-written codes, negative and zero scales, full-size sampled rows.
+The normaliser is sum_k |s t x|, the terms the product actually adds."""
+import numpy as np
+import pytest
+import torch
+
+import bit_packed_sign_amd as b1
+from bit_packed_sign_amd import synth
+from parity import TOL, dev_tensors, norm_err, sample_rows
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def dev():
+    assert torch.cuda.is_available(), "GPU tests need a GPU"
+    return torch.device("cuda:0")
+
+
+def _case(t, M, K, N):
+    r = synth.rng_for(0, synth.WL_TEST, t)
+    x = synth.activations(r, M, K)
+    T = synth.ternary_words(r, N, K)
+    S = synth.group_scales(r, N, K)
+    S[::7] = -S[::7]                                   # negative scales fold into the signs
+    S[3::11, 0] = np.float16(0.0)
+    return x, T, S
+
+
+# K values cover every kernel variant (pairs per wave 1..5), odd group counts (K/128 odd) and a
+# last 1024-wide pair that is partly filled
+DECODE = [(128, 1), (384, 1000), (640, 33), (1024, 4096), (4096, 4096), (4096, 6144), (5120, 5120),
+          (9216, 300), (12288, 4096), (13312, 77), (17408, 5120), (20480, 64)]
+
+
+@pytest.mark.parametrize("K,N", DECODE)
+def test_ternary_decode_matches_oracle(orc, dev, K, N):
+    x, T, S = _case(11000 + K + N, 1, K, N)
+    xd, Td, Sd = dev_tensors(dev, x, T, S)
+    y = b1.gemv_t2(xd, Td, Sd)
+    rows = sample_rows(synth.rng_for(0, synth.WL_TEST, 11001 + N), N, k=384) if N > 2048 else np.arange(N)
+    ref, nrm = orc.gemv_t2_rows(x, T, S, rows)
+    assert norm_err(y.float().cpu().numpy()[:, rows], ref, nrm) <= TOL
+
+
+@pytest.mark.parametrize("M,K,N", [(2, 512, 300), (5, 4096, 1024), (16, 12288, 130), (300, 640, 200),
+                                   (1, 24576, 96)])
+def test_ternary_other_batches_match_oracle(orc, dev, M, K, N):
+    """M > 1 (and K past the batch-1 kernel's range) run on the prefill kernel."""
+    x, T, S = _case(12000 + M + K + N, M, K, N)
+    xd, Td, Sd = dev_tensors(dev, x, T, S)
+    ref, nrm = orc.gemv_t2(x, T, S)
+    assert norm_err(b1.gemv_t2(xd, Td, Sd), ref, nrm) <= TOL
+
+
+@pytest.mark.parametrize("M,K,N", [(256, 4096, 192), (513, 1024, 777), (2048, 4096, 12288)])
+def test_ternary_prefill_matches_oracle(orc, dev, M, K, N):
+    x, T, S = _case(13000 + M + N, M, K, N)
+    xd, Td, Sd = dev_tensors(dev, x, T, S)
+    y = b1.gemm_prefill_t2(xd, Td, Sd)
+    r = synth.rng_for(0, synth.WL_TEST, 13001 + N)
+    rows = sample_rows(r, N, k=96) if N > 1024 else np.arange(N)
+    ms = sample_rows(r, M, k=96) if M > 600 else np.arange(M)
+    ref, nrm = orc.gemv_t2_rows(x[ms], T, S, rows)
+    assert norm_err(y.float().cpu().numpy()[np.ix_(ms, rows)], ref, nrm) <= TOL
+
+
+@pytest.mark.parametrize("M", [1, 3, 256])
+def test_ternary_zero_and_unwritten_codes(orc, dev, M):
+    """Rows of only 00 or only 10 codes give exactly 0; 10 codes mixed into a row read as 0."""
+    K, N = 1024, 64
+    x, T, S = _case(14000 + M, M, K, N)
+    T[0] = 0
+    T[1] = np.uint32(0xAAAAAAAA)                       # every slot 10
+    T[2] = T[2] | (np.uint32(0xAAAAAAAA) & ~(T[2] << np.uint32(1)))   # 00 -> 10, 01 and 11 kept
+    xd, Td, Sd = dev_tensors(dev, x, T, S)
+    y = b1.gemv_t2(xd, Td, Sd) if M < 256 else b1.gemm_prefill_t2(xd, Td, Sd)
+    ref, nrm = orc.gemv_t2(x, T, S)
+    yh = y.float().cpu().numpy()
+    assert np.all(yh[:, :2] == 0.0)
+    assert norm_err(yh, ref, nrm) <= TOL
+
+
+def test_ternary_decode_full_27b_mlp_sampled(orc, dev):
+    """27B MLP shapes at full size in one process: gate 5120x17408 and down 17408x5120."""
+    for K, N in [(5120, 17408), (17408, 5120)]:
+        x, T, S = _case(15000 + K, 1, K, N)
+        xd, Td, Sd = dev_tensors(dev, x, T, S)
+        y = b1.gemv_t2(xd, Td, Sd)
+        rows = sample_rows(synth.rng_for(0, synth.WL_TEST, 15001 + K), N, k=256)
+        ref, nrm = orc.gemv_t2_rows(x, T, S, rows)
+        assert norm_err(y.float().cpu().numpy()[:, rows], ref, nrm) <= TOL
+
+
+def test_ternary_repeated_calls_are_deterministic(dev):
+    x, T, S = _case(16000, 1, 4096, 12288)
+    xd, Td, Sd = dev_tensors(dev, x, T, S)
+    y0 = b1.gemv_t2(xd, Td, Sd)
+    for _ in range(3):
+        assert torch.equal(b1.gemv_t2(xd, Td, Sd), y0)
