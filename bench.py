@@ -51,7 +51,7 @@ def parse():
     ap.add_argument("--no-extra", action="store_true")
     ap.add_argument("--only", default=None,
                     help="run one workload alone (for profiling): step8b, chain8b, lmhead, single, mlp16, "
-                         "prefill, step27b, pm1, bits, copy")
+                         "prefill, step27b, pm1, bits, ternary, copy")
     return ap.parse_args()
 
 
@@ -82,10 +82,11 @@ def time_fn(fn, reps, warm=2):
 class Step:
     """Device-resident weights/activations of a staged workload and a graph of one pass."""
 
-    def __init__(self, wl, device):
+    def __init__(self, wl, device, ternary=False):
         import torch
         from bit_packed_sign_amd import synth
         self.wl = wl
+        self.ternary = ternary
         self.stages = []                      # (x, [W...], [S...], [y...], bytes)
         t0 = time.time()
         gi = 0
@@ -93,22 +94,30 @@ class Step:
             xs = torch.from_numpy(synth.stage_activations(0, wl, s)).to(device)
             Ws, Ss, ys = [], [], []
             for g in stage.gemvs:
-                bits, scales = synth.gemv_tensors(0, wl, gi)
+                bits, scales = (synth.ternary_gemv_tensors if ternary else synth.gemv_tensors)(0, wl, gi)
                 Ws.append(torch.from_numpy(bits.view(np.int32)).to(device))
                 Ss.append(torch.from_numpy(scales).to(device))
                 ys.append(torch.empty((wl.M, g.N), dtype=torch.float16, device=device))
                 gi += 1
-            self.stages.append((xs, Ws, Ss, ys, sum(g.weight_bytes for g in stage.gemvs)))
+            nbytes = sum(round(g.N * g.K * synth.TERNARY_BYTES_PER_WEIGHT) if ternary else g.weight_bytes
+                         for g in stage.gemvs)
+            self.stages.append((xs, Ws, Ss, ys, nbytes))
         torch.cuda.synchronize()
-        log(f"[bench] {wl.name}: {gi} GEMVs in {len(self.stages)} stages, {wl.weight_bytes / 1e9:.3f} GB "
+        self.weight_bytes = sum(st[4] for st in self.stages)
+        log(f"[bench] {wl.name}{' (ternary)' if ternary else ''}: {gi} GEMVs in {len(self.stages)} stages, "
+            f"{self.weight_bytes / 1e9:.3f} GB "
             f"resident (generated in {time.time() - t0:.1f} s)")
         self.graph = None
 
-    @staticmethod
-    def run_stage(st):
+    def run_stage(self, st):
         import bit_packed_sign_amd as b1
         x, Ws, Ss, ys, _ = st
-        if len(Ws) == 1:
+        if self.ternary:
+            if len(Ws) == 1:
+                b1.gemv_t2(x, Ws[0], Ss[0], out=ys[0])
+            else:
+                b1.gemv_group_t2(x, Ws, Ss, outs=ys)
+        elif len(Ws) == 1:
             b1.gemv(x, Ws[0], Ss[0], out=ys[0])
         else:                                 # q/k/v or gate/up: same-input fusion
             b1.gemv_group(x, Ws, Ss, outs=ys)
@@ -332,6 +341,37 @@ def extra_rank27b(st, dev):
     return {"rank_rows_17408x5120_us": round(ms * 1e3, 1)}
 
 
+def extra_ternary(dev, steps):
+    """Ternary g128 (2-bit slots): the 8B decode step (one launch per stage, q/k/v and gate/up
+    fused, HIP graph), the lm_head product alone, and the prefill contraction."""
+    import torch
+    import bit_packed_sign_amd as b1
+    from bit_packed_sign_amd import synth
+    out = {"bytes_per_weight": synth.TERNARY_BYTES_PER_WEIGHT}
+    st = Step(synth.decode_8b(), dev, ternary=True)
+    st.capture()
+    ms = st.timed(steps, 3)
+    out["decode_8b"] = {"ms_per_step": round(ms, 4), "gbs": round(st.weight_bytes / ms / 1e6, 1),
+                        "tok_s": round(1e3 / ms, 1), "launches": len(st.stages),
+                        "weight_bytes": st.weight_bytes}
+    x, Ws, Ss, ys, nb = st.stages[-1]                 # lm_head 4096 x 151936
+    ms = time_fn(lambda: b1.gemv_t2(x, Ws[0], Ss[0], out=ys[0]), reps=20)
+    out["lm_head"] = {"us": round(ms * 1e3, 2), "gbs": round(nb / ms / 1e6, 1)}
+    del st
+    torch.cuda.empty_cache()
+    M, K, N = synth.PREFILL_M, synth.PREFILL_K, synth.PREFILL_N
+    r = synth.rng_for(0, synth.WL_PREFILL, 1)
+    x = torch.from_numpy(synth.activations(r, M, K)).to(dev)
+    T = torch.from_numpy(synth.ternary_words_fast(r, N, K).view(np.int32)).to(dev)
+    S = torch.from_numpy(synth.group_scales(r, N, K)).to(dev)
+    y = torch.empty((M, N), dtype=torch.float16, device=dev)
+    ms = time_fn(lambda: b1.gemm_prefill_t2(x, T, S, out=y), reps=50)
+    tf = 2.0 * M * K * N / (ms * 1e-3) / 1e12
+    out["prefill"] = {"us": round(ms * 1e3, 2), "tflops": round(tf, 1),
+                      "frac_of_fp16_mfma_peak": round(tf / FP16_MFMA_PEAK_TFLOPS, 4)}
+    return out
+
+
 def extra_prefill(dev):
     import torch
     import bit_packed_sign_amd as b1
@@ -450,6 +490,8 @@ def main():
         log(f"[bench] 27b: {extra['decode_27b']}")
         del st
         torch.cuda.empty_cache()
+        extra["ternary"] = extra_ternary(dev, args.steps)
+        log(f"[bench] ternary: {extra['ternary']}")
         extra["pm1"] = extra_pm1(dev)
         log(f"[bench] pm1: {extra['pm1']} ({time.time() - t0:.0f} s of extras)")
 
@@ -518,6 +560,8 @@ def run_only(args, dev):
         log(f"[bench] {o} patch {extra_patch27b(st, dev)} rank {extra_rank27b(st, dev)}")
     elif name == "pm1":
         log(f"[bench] {extra_pm1(dev)}")
+    elif name == "ternary":
+        log(f"[bench] {extra_ternary(dev, args.steps)}")
     elif name == "copy":
         # a plain device copy of known size, to scale the HBM traffic counters
         src = torch.empty(256 << 20, dtype=torch.uint8, device=dev).fill_(1)

@@ -4,5 +4,5 @@ The computation lives in libbin1.so (C ABI: include/bin1.h, HIP kernels in csrc/
 functions below are its thin torch binding.  ``synth`` holds the seeded input generators.
 """
 from .binding import (Bin1Error, ChainPlan, PatchTable, gemm_prefill, gemm_prefill_t2, gemv, gemv_group,  # noqa: F401
-                      gemv_pm1, gemv_t2, lib,
+                      gemv_group_t2, gemv_pm1, gemv_t2, lib,
                       rank_rows_by_scale, xor_bits_apply, xor_patch_apply, xor_patch_apply_multi)

@@ -30,6 +30,7 @@ _SIGS = {
     "bin1_gemv_t2": [_p, _p, _p, _p, _i, _i, _i, _p],
     "bin1_gemm_prefill_t2": [_p, _p, _p, _p, _i, _i, _i, _p],
     "bin1_gemv_group": [_p, _i, _p, _p, _p, _p, _i, _i, _p],
+    "bin1_gemv_group_t2": [_p, _i, _p, _p, _p, _p, _i, _i, _p],
     "bin1_gemv_pm1": [_p, _p, _p, _i, _i, _i, _p],
     "bin1_xor_patch_apply": [_p, _p, _i, _i, _i, _p, _p],
     "bin1_xor_patch_apply_multi": [_p, _p, _p, _i, _p, _i, _p, _p],
@@ -142,7 +143,7 @@ def gemm_prefill_t2(x: torch.Tensor, Tbits: torch.Tensor, scales: torch.Tensor, 
 
 
 def gemv_group(x: torch.Tensor, Wbits: Sequence[torch.Tensor], scales: Sequence[torch.Tensor],
-               outs: Optional[Sequence[torch.Tensor]] = None):
+               outs: Optional[Sequence[torch.Tensor]] = None, _fn: str = "bin1_gemv_group", _per_word: int = 32):
     """Products of several matrices with the same activations x (e.g. q/k/v), one launch for M <= 16.
     Returns the list of outputs y_i [M][N_i]."""
     _need(x, "x", (torch.float16,), 2)
@@ -154,7 +155,7 @@ def gemv_group(x: torch.Tensor, Wbits: Sequence[torch.Tensor], scales: Sequence[
     for i, (W, S) in enumerate(zip(Wbits, scales)):
         _need(W, f"Wbits[{i}]", _BITS, 2)
         _need(S, f"scales[{i}]", (torch.float16,), 2)
-        if W.shape[1] * 32 != K or tuple(S.shape) != (W.shape[0], K // 128):
+        if W.shape[1] * _per_word != K or tuple(S.shape) != (W.shape[0], K // 128):
             raise ValueError(f"matrix {i}: shapes do not match x")
         Ns.append(W.shape[0])
     if outs is None:
@@ -170,10 +171,15 @@ def gemv_group(x: torch.Tensor, Wbits: Sequence[torch.Tensor], scales: Sequence[
     yp = arr_p(*[o.data_ptr() for o in outs])
     npv = (ctypes.c_int * count)(*Ns)
     with torch.cuda.device(x.device):
-        _check("bin1_gemv_group", lib().bin1_gemv_group(x.data_ptr(), count, wp, sp, yp, npv, M, K,
-                                                         _stream(x)))
+        _check(_fn, getattr(lib(), _fn)(x.data_ptr(), count, wp, sp, yp, npv, M, K, _stream(x)))
     return list(outs)
 
+
+
+def gemv_group_t2(x: torch.Tensor, Tbits: Sequence[torch.Tensor], scales: Sequence[torch.Tensor],
+                  outs: Optional[Sequence[torch.Tensor]] = None):
+    """Same-input fusion for ternary weights (Tbits[i] [N_i][K/16]); one launch at M = 1."""
+    return gemv_group(x, Tbits, scales, outs, _fn="bin1_gemv_group_t2", _per_word=16)
 
 def gemm_prefill(x: torch.Tensor, Wbits: torch.Tensor, scales: torch.Tensor, out: Optional[torch.Tensor] = None):
     """Same product as :func:`gemv`, on the matrix-core prefill kernel (for M >= 256)."""

@@ -269,21 +269,26 @@ int bin1_gemv(const void *x, const uint32_t *Wbits, const void *scales, void *y,
                     "bin1_gemv");
 }
 
-int bin1_gemv_group(const void *x, int count, const uint32_t *const *Wbits,
-                    const void *const *scales, void *const *y, const int *N, int M, int K,
-                    void *stream)
+}  // extern "C"
+
+namespace {
+
+// Same-input products of 1..4 matrices; t2: ternary weights in 2-bit slots.
+int gemv_group_impl(const char *fn, bool t2, const void *x, int count, const uint32_t *const *Wbits,
+                    const void *const *scales, void *const *y, const int *N, int M, int K, void *stream)
 {
+    const int bits = t2 ? 2 : 1;
     if (count < 1 || count > bin1::kMaxMats)
         return fail(BIN1_ERR_SHAPE, "count must be 1..%d (got %d)", bin1::kMaxMats, count);
     if (!Wbits || !scales || !y || !N) return fail(BIN1_ERR_NULL, "pointer arrays must be non-NULL");
     for (int i = 0; i < count; ++i) {
-        int st = check_product_host(x, Wbits[i], scales[i], y[i], M, K, N[i]);
+        int st = check_product_host(x, Wbits[i], scales[i], y[i], M, K, N[i], bits);
         if (st) return st;
         for (int j = 0; j < count; ++j) {
             if (j == i) continue;
             const size_t yb = (size_t)M * N[i] * 2;
             if (overlap(y[i], yb, y[j], (size_t)M * N[j] * 2) ||
-                overlap(y[i], yb, Wbits[j], (size_t)N[j] * (K / 8)) ||
+                overlap(y[i], yb, Wbits[j], (size_t)N[j] * (K / 8) * bits) ||
                 overlap(y[i], yb, scales[j], (size_t)N[j] * (K / 128) * 2))
                 return fail(BIN1_ERR_ALIAS, "y[%d] overlaps an input or output of matrix %d", i, j);
         }
@@ -305,8 +310,18 @@ int bin1_gemv_group(const void *x, int count, const uint32_t *const *Wbits,
             set.tile_end[i] = tiles;
         }
         set.count = count;
-        return launched(bin1::launch_gemv_mx(static_cast<const uint16_t *>(x), set, K, st),
-                        "bin1_gemv_group");
+        return launched(t2 ? bin1::launch_gemv_mx_t2(static_cast<const uint16_t *>(x), set, K, st)
+                           : bin1::launch_gemv_mx(static_cast<const uint16_t *>(x), set, K, st),
+                        fn);
+    }
+    if (t2) {                                             // other batch sizes: the prefill kernel
+        for (int i = 0; i < count; ++i) {
+            hipError_t e = bin1::launch_prefill_t2(static_cast<const uint16_t *>(x), Wbits[i],
+                                                   static_cast<const uint16_t *>(scales[i]),
+                                                   static_cast<uint16_t *>(y[i]), M, K, N[i], st);
+            if (e != hipSuccess) return launched(e, fn);
+        }
+        return ok();
     }
     if (M >= 2 && M <= 16) {                              // small batch: one launch as well
         bin1::MxSet set{};
@@ -317,16 +332,31 @@ int bin1_gemv_group(const void *x, int count, const uint32_t *const *Wbits,
             set.N[i] = N[i];
         }
         set.count = count;
-        return launched(bin1::launch_gemv_smallm(static_cast<const uint16_t *>(x), set, M, K, st),
-                        "bin1_gemv_group");
+        return launched(bin1::launch_gemv_smallm(static_cast<const uint16_t *>(x), set, M, K, st), fn);
     }
     for (int i = 0; i < count; ++i) {
         hipError_t e = bin1::launch_gemv(static_cast<const uint16_t *>(x), Wbits[i],
                                          static_cast<const uint16_t *>(scales[i]),
                                          static_cast<uint16_t *>(y[i]), M, K, N[i], st);
-        if (e != hipSuccess) return launched(e, "bin1_gemv_group");
+        if (e != hipSuccess) return launched(e, fn);
     }
     return ok();
+}
+
+}  // namespace
+
+extern "C" {
+
+int bin1_gemv_group(const void *x, int count, const uint32_t *const *Wbits, const void *const *scales,
+                    void *const *y, const int *N, int M, int K, void *stream)
+{
+    return gemv_group_impl("bin1_gemv_group", false, x, count, Wbits, scales, y, N, M, K, stream);
+}
+
+int bin1_gemv_group_t2(const void *x, int count, const uint32_t *const *Tbits, const void *const *scales,
+                       void *const *y, const int *N, int M, int K, void *stream)
+{
+    return gemv_group_impl("bin1_gemv_group_t2", true, x, count, Tbits, scales, y, N, M, K, stream);
 }
 
 int bin1_gemm_prefill(const void *x, const uint32_t *Wbits, const void *scales, void *y, int M,

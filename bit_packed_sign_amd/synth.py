@@ -190,6 +190,25 @@ def gemv_tensors(seed: int, wl: Workload, i: int) -> Tuple[np.ndarray, np.ndarra
             group_scales(rng_for(seed, wl.wid, 2 * i + 1), g.N, g.K))
 
 
+def ternary_words_fast(rng: np.random.Generator, N: int, K: int) -> np.ndarray:
+    """uint32 [N][K/16] of 2-bit slots from uniform random words, every never-written code 10
+    turned into 00: weights 0 with probability 1/2, +1 and -1 with 1/4 each.  For large
+    workloads (the benchmark), where drawing each weight separately would not fit in memory."""
+    w = rng.integers(0, 2 ** 32, size=(N, K // 16), dtype=np.uint32)
+    lo = w & np.uint32(0x55555555)
+    return (lo | (w & np.uint32(0xAAAAAAAA) & (lo << np.uint32(1)))).astype(np.uint32)
+
+
+def ternary_gemv_tensors(seed: int, wl: Workload, i: int) -> Tuple[np.ndarray, np.ndarray]:
+    """Ternary weights (2-bit slots) and scales of GEMV i of a workload, for the benchmark."""
+    g = wl.gemvs[i]
+    return (ternary_words_fast(rng_for(seed, wl.wid, 30_000 + 2 * i), g.N, g.K),
+            group_scales(rng_for(seed, wl.wid, 30_000 + 2 * i + 1), g.N, g.K))
+
+
+TERNARY_BYTES_PER_WEIGHT = 2 / 8 + 2 / GROUP        # 2-bit slot + the fp16 group scale
+
+
 def stage_activations(seed: int, wl: Workload, s: int) -> np.ndarray:
     return activations(rng_for(seed, wl.wid, 10_000 + s), wl.M, wl.stages[s].K)
 

@@ -109,6 +109,11 @@ int bin1_gemv_t2(const void *x, const uint32_t *Tbits, const void *scales, void 
                  int M, int K, int N, void *stream);
 int bin1_gemm_prefill_t2(const void *x, const uint32_t *Tbits, const void *scales, void *y,
                          int M, int K, int N, void *stream);
+/* Same-input fusion for ternary weights: as bin1_gemv_group, with Tbits[i] [N[i]][K/16];
+ * one launch when M == 1. */
+int bin1_gemv_group_t2(const void *x, int count, const uint32_t *const *Tbits,
+                       const void *const *scales, void *const *y, const int *N,
+                       int M, int K, void *stream);
 
 /* +-1 activations times +-1 weights, exact:
  *   y[m][n] = sum_k a(m,k) * w(n,k) = K - 2 * popcount(Abits[m] xor Wbits[n])  (int32).

@@ -29,7 +29,7 @@ def test_header_declares_the_entry_points():
     names = _declared()
     for fn in ["bin1_gemv", "bin1_gemv_group", "bin1_gemm_prefill", "bin1_gemv_pm1", "bin1_xor_patch_apply",
                "bin1_xor_patch_apply_multi", "bin1_xor_bits_apply", "bin1_rank_rows_by_scale",
-               "bin1_gemv_t2", "bin1_gemm_prefill_t2",
+               "bin1_gemv_t2", "bin1_gemm_prefill_t2", "bin1_gemv_group_t2",
                "bin1_status_string", "bin1_last_error", "bin1_abi_version"]:
         assert fn in names
 

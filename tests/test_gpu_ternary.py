@@ -100,3 +100,22 @@ def test_ternary_repeated_calls_are_deterministic(dev):
     y0 = b1.gemv_t2(xd, Td, Sd)
     for _ in range(3):
         assert torch.equal(b1.gemv_t2(xd, Td, Sd), y0)
+
+
+@pytest.mark.parametrize("M,K,Ns", [(1, 4096, (4096, 1024, 1024)), (1, 5120, (17408, 17408)), (1, 384, (7, 33, 100, 16)),
+                                    (3, 1024, (300, 65))])
+def test_ternary_group_matches_oracle_and_separate_calls(orc, dev, M, K, Ns):
+    r = synth.rng_for(0, synth.WL_TEST, 17000 + K + sum(Ns) + M)
+    x = synth.activations(r, M, K)
+    Ts = [synth.ternary_words(r, n, K) for n in Ns]
+    Ss = [synth.group_scales(r, n, K) for n in Ns]
+    xd = dev_tensors(dev, x)[0]
+    Td = [dev_tensors(dev, W=T)[0] for T in Ts]
+    Sd = [dev_tensors(dev, S=S)[0] for S in Ss]
+    outs = b1.gemv_group_t2(xd, Td, Sd)
+    for T, S, Tdev, Sdev, y in zip(Ts, Ss, Td, Sd, outs):
+        N = T.shape[0]
+        rows = sample_rows(r, N, k=128) if N > 2048 else np.arange(N)
+        ref, nrm = orc.gemv_t2_rows(x, T, S, rows)
+        assert norm_err(y.float().cpu().numpy()[:, rows], ref, nrm) <= TOL
+        assert torch.equal(b1.gemv_t2(xd, Tdev, Sdev), y)
