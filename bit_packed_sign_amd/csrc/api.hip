@@ -68,12 +68,17 @@ int launched(hipError_t e, const char *what)
 
 // Shared validation of the (x, Wbits, scales, y, M, K, N) products: host-side checks first.
 // bits: bits per weight of W (1: signs, 2: ternary slots)
+// Returns kEmpty (> 0) for a product with no outputs (M == 0 or N == 0): nothing to compute,
+// and its pointers are not used.
+constexpr int kEmpty = 1;
+
 int check_product_host(const void *x, const void *W, const void *S, const void *y, int M, int K, int N,
                        int bits = 1)
 {
+    if (M < 0 || N < 0 || K < 128 || K % 128 != 0)
+        return fail(BIN1_ERR_SHAPE, "need M>=0, N>=0, K>=128, K%%128==0 (got M=%d K=%d N=%d)", M, K, N);
+    if (M == 0 || N == 0) return kEmpty;
     if (!x || !W || !S || !y) return fail(BIN1_ERR_NULL, "x, Wbits, scales and y must be non-NULL");
-    if (M < 1 || N < 1 || K < 128 || K % 128 != 0)
-        return fail(BIN1_ERR_SHAPE, "need M>=1, N>=1, K>=128, K%%128==0 (got M=%d K=%d N=%d)", M, K, N);
     if (!aligned16(x) || !aligned16(W) || !aligned16(S) || !aligned16(y))
         return fail(BIN1_ERR_ALIGN, "x, Wbits, scales and y must be 16-byte aligned");
     const size_t xb = (size_t)M * K * 2, wb = (size_t)N * (K / 8) * bits, sb = (size_t)N * (K / 128) * 2,
@@ -146,6 +151,7 @@ int bin1_chain_prepare(const bin1_stage *stages, int nstages, void *workspace, s
         const int sp = ((g.K >> 10) + 3) / 4;
         if (sp > spmax) spmax = sp;
         for (int i = 0; i < g.count; ++i) {
+            if (g.N[i] < 1) return fail(BIN1_ERR_SHAPE, "stage %d: every product needs N >= 1", s);
             if ((st = check_product_host(g.x, g.Wbits[i], g.scales[i], g.y[i], 1, g.K, g.N[i]))) return st;
             if ((st = check_product_device(g.x, g.Wbits[i], g.scales[i], g.y[i]))) return st;
         }
@@ -261,7 +267,7 @@ int bin1_gemv(const void *x, const uint32_t *Wbits, const void *scales, void *y,
               int N, void *stream)
 {
     int st = check_product(x, Wbits, scales, y, M, K, N);
-    if (st) return st;
+    if (st) return st == kEmpty ? ok() : st;
     return launched(bin1::launch_gemv(static_cast<const uint16_t *>(x), Wbits,
                                       static_cast<const uint16_t *>(scales),
                                       static_cast<uint16_t *>(y), M, K, N,
@@ -281,9 +287,27 @@ int gemv_group_impl(const char *fn, bool t2, const void *x, int count, const uin
     if (count < 1 || count > bin1::kMaxMats)
         return fail(BIN1_ERR_SHAPE, "count must be 1..%d (got %d)", bin1::kMaxMats, count);
     if (!Wbits || !scales || !y || !N) return fail(BIN1_ERR_NULL, "pointer arrays must be non-NULL");
+    // products with no outputs (M == 0 or N[i] == 0) are dropped; the rest go ahead
+    const uint32_t *Wk[bin1::kMaxMats];
+    const void *Sk[bin1::kMaxMats];
+    void *yk[bin1::kMaxMats];
+    int Nk[bin1::kMaxMats], kept = 0;
     for (int i = 0; i < count; ++i) {
-        int st = check_product_host(x, Wbits[i], scales[i], y[i], M, K, N[i], bits);
-        if (st) return st;
+        const int st = check_product_host(x, Wbits[i], scales[i], y[i], M, K, N[i], bits);
+        if (st < 0) return st;
+        if (st == kEmpty) continue;
+        Wk[kept] = Wbits[i];
+        Sk[kept] = scales[i];
+        yk[kept] = y[i];
+        Nk[kept++] = N[i];
+    }
+    if (kept == 0) return ok();
+    count = kept;
+    Wbits = Wk;
+    scales = Sk;
+    y = yk;
+    N = Nk;
+    for (int i = 0; i < count; ++i) {
         for (int j = 0; j < count; ++j) {
             if (j == i) continue;
             const size_t yb = (size_t)M * N[i] * 2;
@@ -363,7 +387,7 @@ int bin1_gemm_prefill(const void *x, const uint32_t *Wbits, const void *scales, 
                       int K, int N, void *stream)
 {
     int st = check_product(x, Wbits, scales, y, M, K, N);
-    if (st) return st;
+    if (st) return st == kEmpty ? ok() : st;
     return launched(bin1::launch_prefill(static_cast<const uint16_t *>(x), Wbits,
                                          static_cast<const uint16_t *>(scales),
                                          static_cast<uint16_t *>(y), M, K, N,
@@ -374,9 +398,10 @@ int bin1_gemm_prefill(const void *x, const uint32_t *Wbits, const void *scales, 
 int bin1_gemv_pm1(const uint32_t *Abits, const uint32_t *Wbits, int32_t *y, int M, int K, int N,
                   void *stream)
 {
+    if (M < 0 || N < 0 || K < 128 || K % 128 != 0)
+        return fail(BIN1_ERR_SHAPE, "need M>=0, N>=0, K>=128, K%%128==0 (got M=%d K=%d N=%d)", M, K, N);
+    if (M == 0 || N == 0) return ok();                 // no outputs
     if (!Abits || !Wbits || !y) return fail(BIN1_ERR_NULL, "Abits, Wbits and y must be non-NULL");
-    if (M < 1 || N < 1 || K < 128 || K % 128 != 0)
-        return fail(BIN1_ERR_SHAPE, "need M>=1, N>=1, K>=128, K%%128==0 (got M=%d K=%d N=%d)", M, K, N);
     if (!aligned16(Abits) || !aligned16(Wbits) || !aligned16(y))
         return fail(BIN1_ERR_ALIGN, "Abits, Wbits and y must be 16-byte aligned");
     const size_t ab = (size_t)M * (K / 8), wb = (size_t)N * (K / 8), yb = (size_t)M * N * 4;
@@ -460,9 +485,10 @@ int bin1_xor_bits_apply(uint32_t *const *Wtab, const int32_t *Ktab, const int32_
 
 int bin1_rank_rows_by_scale(const void *scales, int N, int K, int64_t *score, int32_t *order, void *stream)
 {
+    if (N < 0 || N > (1 << 20) || K < 128 || K % 128 != 0)
+        return fail(BIN1_ERR_SHAPE, "need 0 <= N <= 2^20, K >= 128, K %% 128 == 0 (got N=%d K=%d)", N, K);
+    if (N == 0) return ok();                           // no rows to rank
     if (!scales || !score || !order) return fail(BIN1_ERR_NULL, "scales, score and order must be non-NULL");
-    if (N < 1 || N > (1 << 20) || K < 128 || K % 128 != 0)
-        return fail(BIN1_ERR_SHAPE, "need 1 <= N <= 2^20, K >= 128, K %% 128 == 0 (got N=%d K=%d)", N, K);
     if (!aligned16(scales) || reinterpret_cast<uintptr_t>(score) & 7u || reinterpret_cast<uintptr_t>(order) & 3u)
         return fail(BIN1_ERR_ALIGN, "scales must be 16-byte aligned, score 8-byte, order 4-byte");
     const size_t sb = (size_t)N * (K / 128) * 2, cb = (size_t)N * 8, ob = (size_t)N * 4;
@@ -481,7 +507,7 @@ int bin1_gemv_t2(const void *x, const uint32_t *Tbits, const void *scales, void 
                  void *stream)
 {
     int st = check_product(x, Tbits, scales, y, M, K, N, 2);
-    if (st) return st;
+    if (st) return st == kEmpty ? ok() : st;
     const hipStream_t s = static_cast<hipStream_t>(stream);
     if (M == 1 && K <= bin1::mx_max_k()) {
         bin1::MxSet set{};
@@ -502,7 +528,7 @@ int bin1_gemm_prefill_t2(const void *x, const uint32_t *Tbits, const void *scale
                          void *stream)
 {
     int st = check_product(x, Tbits, scales, y, M, K, N, 2);
-    if (st) return st;
+    if (st) return st == kEmpty ? ok() : st;
     return launched(bin1::launch_prefill_t2(static_cast<const uint16_t *>(x), Tbits,
                                             static_cast<const uint16_t *>(scales), static_cast<uint16_t *>(y),
                                             M, K, N, static_cast<hipStream_t>(stream)),

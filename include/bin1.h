@@ -40,9 +40,12 @@
  *    captured into a HIP graph.
  *  - Validation happens before anything is enqueued; on any error nothing is enqueued
  *    and the outputs are untouched.
- *  - Requirements: M >= 1, N >= 1, K >= 128, K % 128 == 0; x, Wbits, scales, y, Abits
+ *  - Requirements: M >= 0, N >= 0, K >= 128, K % 128 == 0; x, Wbits, scales, y, Abits
  *    16-byte aligned; y must not overlap any input.  Products also need N < 2^24 - 64
- *    and x, Wbits and y each under 2 GiB (else BIN1_ERR_SHAPE).
+ *    and x, Wbits and y each under 2 GiB (else BIN1_ERR_SHAPE).  A product with no
+ *    outputs (M == 0 or N == 0) returns BIN1_OK without enqueuing anything; its
+ *    pointers are not read and may be NULL.  (K cannot be 0: a row is a whole number of
+ *    128-weight groups, each with its scale.)
  *  - Device-side faults surface at the caller's next synchronisation, as with any
  *    HIP kernel.  BIN1_ERR_LAUNCH carries the HIP error text in bin1_last_error().
  *  - The library is stateless apart from a thread-local error string: calls are
@@ -82,7 +85,8 @@ int bin1_gemv(const void *x, const uint32_t *Wbits, const void *scales, void *y,
  * M <= 16.  Wbits, scales, y and N are HOST arrays of `count` entries; entry i describes
  * matrix i exactly as in bin1_gemv (Wbits[i] [N[i]][K/32], scales[i] [N[i]][K/128],
  * y[i] [M][N[i]]).  Every y[i] must be disjoint from every input and from the other
- * outputs.  Results equal `count` separate bin1_gemv calls. */
+ * outputs.  Results equal `count` separate bin1_gemv calls; a matrix with N[i] == 0 is
+ * skipped. */
 int bin1_gemv_group(const void *x, int count, const uint32_t *const *Wbits,
                     const void *const *scales, void *const *y, const int *N,
                     int M, int K, void *stream);
@@ -161,8 +165,8 @@ int bin1_xor_bits_apply(uint32_t *const *Wtab, const int32_t *Ktab, const int32_
  * score (device int64[N]): the sum over the row's groups of |scale|, exactly, in units of
  * 2^-24 (an inf/NaN scale counts as its magnitude bits would, (f + 2^10) << 30), and order
  * (device int32[N]): the rows by score, largest first, equal scores by ascending row.
- * Requires 1 <= N <= 2^20 (the ranking counts over all pairs), K >= 128, K % 128 == 0,
- * and no overlap between scales, score and order. */
+ * Requires 0 <= N <= 2^20 (the ranking counts over all pairs; N == 0 is a no-op), K >= 128,
+ * K % 128 == 0, and no overlap between scales, score and order. */
 int bin1_rank_rows_by_scale(const void *scales, int N, int K, int64_t *score, int32_t *order, void *stream);
 
 /* ------------------------------------------------------------------------------------
@@ -174,8 +178,8 @@ int bin1_rank_rows_by_scale(const void *scales, int N, int K, int64_t *score, in
  * "Low-bit kernels for hybrid attention"]; the chain keeps one workgroup per CU resident for
  * the whole step, streams the next stage's weights while a stage waits, and orders stages
  * with device-scope release/acquire flags in the workspace.
- * Requirements: K_s % 256 == 0 and K_s <= 20480; the GPU has at least 256 compute units; the
- * products follow bin1_gemv's layouts.  An output may be (and usually is) a later stage's x, but
+ * Requirements: K_s % 256 == 0 and K_s <= 20480, every N >= 1; the GPU has at least 256
+ * compute units; the products follow bin1_gemv's layouts.  An output may be (and usually is) a later stage's x, but
  * must not overlap its own stage's x, any Wbits or scales of the chain, or another output of
  * its stage.
  * The workspace (device memory, caller-owned, bin1_chain_workspace_bytes(nstages) bytes,

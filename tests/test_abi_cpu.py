@@ -60,10 +60,14 @@ def test_product_validation(L, fn):
     f = getattr(L, fn)
     assert f(None, FAKE, FAKE, FAKE, 1, 128, 1, None) == -1
     assert b"non-NULL" in L.bin1_last_error()
-    assert f(FAKE, FAKE, FAKE, FAKE * 2, 0, 128, 1, None) == -2
+    # a product with no outputs returns at once, its pointers unread (NULL allowed)
+    assert f(None, None, None, None, 0, 128, 1, None) == 0
+    assert f(None, None, None, None, 3, 128, 0, None) == 0
+    assert f(None, None, None, None, 0, 100, 1, None) == -2     # K is checked first
+    assert f(FAKE, FAKE, FAKE, FAKE * 2, -1, 128, 1, None) == -2
+    assert f(FAKE, FAKE, FAKE, FAKE * 2, 1, 128, -1, None) == -2
     assert f(FAKE, FAKE, FAKE, FAKE * 2, 1, 100, 1, None) == -2
     assert f(FAKE, FAKE, FAKE, FAKE * 2, 1, 0, 1, None) == -2
-    assert f(FAKE, FAKE, FAKE, FAKE * 2, 1, 128, 0, None) == -2
     assert f(FAKE, FAKE, FAKE, FAKE * 2, 1, 128, 1 << 24, None) == -2            # rows past 24-bit
     assert f(FAKE, FAKE, FAKE, FAKE * 2, 1, 1 << 20, 1 << 14, None) == -2        # Wbits of 2 GiB
     assert b"2 GiB" in L.bin1_last_error()
@@ -84,6 +88,10 @@ def test_group_validation(L):
     S = arr(FAKE * 12, FAKE * 16)
     Y = arr(FAKE * 8 + 16, FAKE * 20)
     assert L.bin1_gemv_group(FAKE, 2, W, S, Y, n, 1, 128, None) == -4
+    # every product empty: nothing to do
+    assert L.bin1_gemv_group(None, 2, arr(None, None), arr(None, None), arr(None, None), n, 0, 128, None) == 0
+    z = (ctypes.c_int * 2)(0, 0)
+    assert L.bin1_gemv_group(None, 2, arr(None, None), arr(None, None), arr(None, None), z, 1, 128, None) == 0
 
 
 def test_chain_validation(L):
@@ -102,6 +110,9 @@ def test_chain_validation(L):
 
 def test_pm1_and_patch_validation(L):
     assert L.bin1_gemv_pm1(None, FAKE, FAKE, 1, 128, 1, None) == -1
+    assert L.bin1_gemv_pm1(None, None, None, 0, 128, 1, None) == 0          # no outputs
+    assert L.bin1_gemv_pm1(None, None, None, 2, 128, 0, None) == 0
+    assert L.bin1_gemv_pm1(FAKE, FAKE * 2, FAKE * 3, -1, 128, 1, None) == -2
     assert L.bin1_gemv_pm1(FAKE, FAKE * 2, FAKE * 3, 1, 96, 1, None) == -2
     assert L.bin1_gemv_pm1(FAKE, FAKE * 2, FAKE + 4, 1, 128, 1, None) == -3
     # an empty patch is a no-op that succeeds without touching anything
@@ -124,7 +135,8 @@ def test_bit_patch_and_rank_validation(L):
     assert L.bin1_xor_bits_apply(FAKE + 4, FAKE, FAKE, 1, FAKE, 1, None, None) == -3
     # rank: NULLs, shapes, alignment and overlap
     assert L.bin1_rank_rows_by_scale(None, 1, 128, FAKE, FAKE * 2, None) == -1
-    assert L.bin1_rank_rows_by_scale(FAKE, 0, 128, FAKE * 2, FAKE * 3, None) == -2
+    assert L.bin1_rank_rows_by_scale(None, 0, 128, None, None, None) == 0    # no rows
+    assert L.bin1_rank_rows_by_scale(FAKE, -1, 128, FAKE * 2, FAKE * 3, None) == -2
     assert L.bin1_rank_rows_by_scale(FAKE, (1 << 20) + 1, 128, FAKE * 2, FAKE * 3, None) == -2
     assert L.bin1_rank_rows_by_scale(FAKE, 4, 96, FAKE * 2, FAKE * 3, None) == -2
     assert L.bin1_rank_rows_by_scale(FAKE + 2, 4, 128, FAKE * 2, FAKE * 3, None) == -3

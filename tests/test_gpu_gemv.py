@@ -157,3 +157,25 @@ def test_gemv_repeated_calls_are_deterministic(dev):
     y0 = b1.gemv(xd, Wd, Sd)
     for _ in range(3):
         assert torch.equal(b1.gemv(xd, Wd, Sd), y0)
+
+
+def test_empty_products_are_no_ops(orc, dev):
+    """Degenerate shapes: M == 0 or N == 0 products return at once (nothing is written), and a
+    grouped call with an empty matrix among others equals the calls on the non-empty ones."""
+    K = 512
+    x, W, S = _case(7400, 3, K, 40)
+    xd, Wd, Sd = dev_tensors(dev, x, W, S)
+    for fn in (b1.gemv, b1.gemm_prefill):
+        y = fn(xd[:0], Wd, Sd)                                   # M == 0
+        assert tuple(y.shape) == (0, 40)
+        y = fn(xd, Wd[:0], Sd[:0])                               # N == 0
+        assert tuple(y.shape) == (3, 0)
+    outs = b1.gemv_group(xd, [Wd, Wd[:0], Wd], [Sd, Sd[:0], Sd])
+    ref, nrm = orc.gemv(x, W, S)
+    assert tuple(outs[1].shape) == (3, 0)
+    assert norm_err(outs[0], ref, nrm) <= TOL and torch.equal(outs[0], outs[2])
+    assert torch.equal(outs[0], b1.gemv(xd, Wd, Sd))
+    assert tuple(b1.gemv_pm1(torch.zeros((0, K // 32), dtype=torch.int32, device=dev),
+                             Wd).shape) == (0, 40)
+    score, order = b1.rank_rows_by_scale(Sd[:0])
+    assert score.numel() == 0 and order.numel() == 0
