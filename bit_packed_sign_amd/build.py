@@ -24,6 +24,9 @@ FLAGS = [
     f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC", "-Wall",
     # Packed fp32 ops stay off in generated code (the v_pk_*_f32 forms are avoided).
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+    # the leading scalar kernel arguments arrive preloaded in SGPRs (no kernarg load in front
+    # of a kernel's first memory accesses)
+    "-mllvm", "-amdgpu-kernarg-preload-count=16",
     "-I", os.path.join(ROOT, "include"), "-I", CSRC,
 ]
 

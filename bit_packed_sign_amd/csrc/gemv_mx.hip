@@ -148,7 +148,8 @@ struct Slot {
 
 template <int SP, int P, int R, bool ODD, bool T2>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 4)))
-void gemv_mx_kernel(const uint16_t *__restrict__ x, MxSet set, int K, int ntiles)
+void gemv_mx_kernel(const uint16_t *__restrict__ x, int K, int tq, int tr, int grid, const uint32_t *W0,
+                    const uint16_t *S0, int N0, int te0, MxSet set)
 {
     extern __shared__ __attribute__((aligned(16))) uint8_t lds[];
     const int tid = threadIdx.x, lane = tid & 63;
@@ -157,8 +158,12 @@ void gemv_mx_kernel(const uint16_t *__restrict__ x, MxSet set, int K, int ntiles
     const int npair = (K + 1023) >> 10, nseg = 2 * npair;
     const int wpr = T2 ? K >> 4 : K >> 5, spr = K >> 7;   // words per row: 16 or 32 weights each
     constexpr int kGW = T2 ? 8 : 4;                      // words per scale group
-    const int my_tiles = __builtin_amdgcn_readfirstlane(
-        blockIdx.x < ntiles ? (ntiles - 1 - blockIdx.x) / gridDim.x + 1 : 0);   // <= 64
+    // The scalars come first in the argument list so that they arrive preloaded in registers
+    // (with matrix 0's pointers, its row count and tile end): the tile count is split on the
+    // host (tiles = tq * grid + tr), so no load of the grid size and no division sit in front
+    // of the first loads, and a workgroup whose first tile is in matrix 0 starts its weight
+    // loads without waiting for the argument table.
+    const int my_tiles = tq + (blockIdx.x < (unsigned)tr ? 1 : 0);         // <= 64
 
     Slot<SP, R, T2> ring[P];
 
@@ -205,12 +210,23 @@ void gemv_mx_kernel(const uint16_t *__restrict__ x, MxSet set, int K, int ntiles
     constexpr int XT = SP;                           // activation tasks per thread (K <= 4096*SP)
     XLoad<XT> xl;
     x_load<XT>(K, x, xl);
+    __builtin_amdgcn_sched_barrier(0);               // x loads go out before the argument-table loads
     {
-        const TileTab t0 = tile_tab<R>(set, blockIdx.x);          // uniform
-        issue_t(t0.row0, my_tiles > 0 ? t0.N : 0, t0.W, t0.S, ring[0]);
+        // only the scalars are chosen under the (uniform) branch: one issue after it, so no
+        // load sits on either side of a join
+        unsigned long long Wp = (unsigned long long)W0, Sp = (unsigned long long)S0;
+        int row0 = (int)blockIdx.x * 16 * R, Nt = N0;
+        if (blockIdx.x >= (unsigned)te0) {
+            const TileTab t0 = tile_tab<R>(set, blockIdx.x);
+            Wp = t0.W;
+            Sp = t0.S;
+            row0 = t0.row0;
+            Nt = t0.N;
+        }
+        issue_t(row0, my_tiles > 0 ? Nt : 0, Wp, Sp, ring[0]);
     }
     limbs_fill(K, lds);
-    const TileTab tab = tile_tab<R>(set, blockIdx.x + lane * gridDim.x);
+    const TileTab tab = tile_tab<R>(set, blockIdx.x + lane * grid);
 #pragma unroll
     for (int p = 1; p < P; ++p) issue(tab, p, ring[p]);
     __syncthreads();                                  // zero-filled limb area visible
@@ -338,7 +354,8 @@ hipError_t launch_mx(const uint16_t *x, const MxSet &set0, int K, hipStream_t st
     const int grid = tiles < cap ? tiles : (need > cap ? need : cap);
     const int rows_per_wg = (tiles + grid - 1) / grid * 16 * R;
     hipLaunchKernelGGL((gemv_mx_kernel<SP, P, R, ODD, T2>), dim3(grid), dim3(256), shm_bytes(K, rows_per_wg),
-                       st, x, set, K, tiles);
+                       st, x, K, tiles / grid, tiles % grid, grid, set.W[0], set.S[0], set.N[0], set.tile_end[0],
+                       set);
     return hipGetLastError();
 }
 
