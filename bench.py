@@ -197,10 +197,11 @@ class ChainStep:
 
 
 def kernel_source_sha(*names):
-    """Hash of the kernel sources a stored counter summary was taken with."""
+    """Hash of the kernel sources (and of the build script, which holds the compile flags) a
+    stored counter summary was taken with."""
     import hashlib
     h = hashlib.sha256()
-    for n in names:
+    for n in (*names, "../build.py"):
         with open(os.path.join(ROOT, "bit_packed_sign_amd", "csrc", n), "rb") as f:
             h.update(f.read())
     return h.hexdigest()[:16]
@@ -384,8 +385,19 @@ def extra_prefill(dev):
     y = torch.empty((M, N), dtype=torch.float16, device=dev)
     ms = time_fn(lambda: b1.gemm_prefill(x, W, S, out=y), reps=50)
     tf = 2.0 * M * K * N / (ms * 1e-3) / 1e12
+    # context only: a dense fp16 GEMM of the same shape through torch (the vendor BLAS), with
+    # the weights as a plain fp16 matrix (row-major [K][N] and transposed [N][K])
+    del W, S
+    a = torch.randn((M, K), dtype=torch.float16, device=dev)
+    b = torch.randn((K, N), dtype=torch.float16, device=dev)
+    bt = b.t().contiguous()
+    ref = {}
+    for name, fn in (("b_row_major", lambda: a @ b), ("b_transposed", lambda: a @ bt.t())):
+        rms = time_fn(fn, reps=50)
+        ref[name] = {"us": round(rms * 1e3, 2), "tflops": round(2.0 * M * K * N / (rms * 1e-3) / 1e12, 1)}
     return {"workload": "prefill M=2048 K=4096 N=12288", "us": round(ms * 1e3, 2),
-            "tflops": round(tf, 1), "frac_of_fp16_mfma_peak": round(tf / FP16_MFMA_PEAK_TFLOPS, 4)}
+            "tflops": round(tf, 1), "frac_of_fp16_mfma_peak": round(tf / FP16_MFMA_PEAK_TFLOPS, 4),
+            "dense_fp16_gemm_same_shape_torch": ref}
 
 
 def extra_pm1(dev):
