@@ -2,7 +2,7 @@
 //
 // Weights: one packed word (32 signs, bit 1 = +1) becomes 32 fp4 e2m1 values +-1 (the
 // multiply-free sign expansion of the "PrismML Bonsai -- 1.15GB" page, section "What 1-bit
-// is"); activations: each 32-element block of x becomes four e4m3 limbs with per-block E8M0
+// is"); activations: each 32-element block of x becomes e4m3 limbs with per-block E8M0
 // exponents.  v_mfma_scale_f32_16x16x128_f8f6f4 contracts them, one 128-weight group per
 // chain of four instructions ("Bonsai 27B" page, section "Binary weight format", eq. b_eff).
 #pragma once
@@ -115,17 +115,26 @@ __device__ __forceinline__ void convert16(const u4v p0, const u4v p1, float mx, 
     const float mul = __builtin_ldexpf(1.0f, 7 - e0);
 #pragma unroll
     for (int i = 0; i < 16; ++i) u[i] *= mul;        // |u| < 256, exact
+    // Three limbs carry 12 significant bits, one more than fp16: every element within 2^10 of
+    // the block's maximum is represented exactly, and no element is off by more than 2^-25 of
+    // that maximum (e4m3's subnormals limit the smallest ones; checked over every fp16 value and
+    // block exponent).  The fourth limb row of the A operand is stored as zeros, with a finite
+    // exponent byte, so it contributes exactly 0.
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
         int d[4];
 #pragma unroll
         for (int c = 0; c < 4; ++c) {
-            int v = __builtin_amdgcn_cvt_pk_fp8_f32(u[idx(c, 0)], u[idx(c, 1)], 0, false);
-            d[c] = __builtin_amdgcn_cvt_pk_fp8_f32(u[idx(c, 2)], u[idx(c, 3)], v, true);
+            if (r < 3) {
+                int v = __builtin_amdgcn_cvt_pk_fp8_f32(u[idx(c, 0)], u[idx(c, 1)], 0, false);
+                d[c] = __builtin_amdgcn_cvt_pk_fp8_f32(u[idx(c, 2)], u[idx(c, 3)], v, true);
+            } else {
+                d[c] = 0;
+            }
             *reinterpret_cast<int *>(blk + (4 * G + r) * 32 + (T2 ? 4 * h + c : 2 * c + h) * 4) = d[c];
         }
         if (h == 0) scbyte[r * 4] = (uint8_t)(127 + e0 - 7 - 4 * r);
-        if (r < 3) {
+        if (r < 2) {
             // next limb's input: 16 (u - q), q = the fp8 value just stored.  u - q is exact
             // (q is u rounded to 4 significant bits) and so are 16 u and 16 q, so the single
             // fma 16 u - 16 q rounds nothing.
