@@ -13,10 +13,11 @@
 //    (the bit goes straight into the nibble's sign position), and the block-scaled MFMA
 //    v_mfma_scale_f32_16x16x128_f8f6f4 does the 4096 +-x adds per instruction.
 //  * The MFMA's other operand must be fp8, so each 32-element block of x is split into
-//    four e4m3 limbs x = 2^(e-7) (L0 + L1/16 + L2/256 + L3/4096) with e the block's max
-//    exponent; the limb exponents go into the MFMA's per-32-element E8M0 scales.  Four
-//    limbs carry >= 16 significant bits, more than fp16's 11, so for normal-range x the
-//    split is exact.  The limbs are built once per workgroup into LDS.
+//    three e4m3 limbs x = 2^(e-7) (L0 + L1/16 + L2/256) with e the block's max exponent
+//    (the fourth limb row of the A operand is zero); the limb exponents go into the MFMA's
+//    per-32-element E8M0 scales.  Three limbs carry 12 significant bits, more than fp16's
+//    11: an element within 2^10 of its block's maximum is exact, and none is off by more
+//    than 2^-25 of that maximum.  The limbs are built once per workgroup into LDS.
 //  * One 16x16x128 MFMA covers 16 rows x 128 weights: lane (n, g) supplies word t of its
 //    row's group g, and the 16 A rows are (group G, limb r) with A zero outside group G,
 //    so C[4G+r][n] is the unscaled limb-r partial of group G -- exactly what lane (n, G)
@@ -24,7 +25,9 @@
 //  * Weights are streamed with nontemporal buffer loads, several row tiles ahead per wave.
 //    A lane owns two adjacent scale groups (32 contiguous bytes of its row and one dword of
 //    scales), so each wave reads whole 128-byte lines; the 4 waves of a workgroup split K
-//    in 1024-weight "pairs" (8 groups) and combine their partial rows in LDS.
+//    in 1024-weight "pairs" (8 groups) and combine their partial rows in LDS.  Long rows
+//    (K > 8192, one tile per workgroup) use 8 waves instead, two per SIMD: each wave then
+//    converts and contracts at most half as many pairs.
 //  * Segment sigma (two per pair p, h = sigma % 2) is what one chain of four MFMAs covers:
 //    MFMA K-block G of segment sigma is scale group gamma = 8p + 2G + h.
 #include "common.hpp"
@@ -41,7 +44,7 @@ using namespace mx;
 // Block beta = k/32 holds the 32 activations of packed word beta (word t = beta % 4 of group
 // gamma = beta / 4); within the block, element j pairs with weight bit pi(j) = 4*(j%8) + j/8
 // (the order unpack_fp4 produces).  Task tau covers activations [16 tau, 16 tau + 16); thread
-// t takes tasks t, t+256, ...  The x loads are issued before the weight prefetch (loads retire
+// t of NT takes tasks t, t+NT, ...  The x loads are issued before the weight prefetch (loads retire
 // in order, so waiting on them later does not drain the prefetch).
 template <int XT>
 struct XLoad {
@@ -50,14 +53,14 @@ struct XLoad {
 
 __device__ __forceinline__ int nseg_of(int K) { return 2 * ((K + 1023) >> 10); }
 
-template <int XT>
+template <int XT, int NT>
 __device__ __forceinline__ void x_load(int K, const uint16_t *__restrict__ x, XLoad<XT> &xl)
 {
     const int tid = threadIdx.x;
     const __amdgpu_buffer_rsrc_t rx = rsrc(x, (unsigned)K * 2u);
 #pragma unroll
     for (int q = 0; q < XT; ++q) {
-        const unsigned off = 32u * (unsigned)(tid + 256 * q);    // past K: zeros, no traffic
+        const unsigned off = 32u * (unsigned)(tid + NT * q);     // past K: zeros, no traffic
         xl.v[q][0] = __builtin_amdgcn_raw_buffer_load_b128(rx, off, 0, 0);
         xl.v[q][1] = __builtin_amdgcn_raw_buffer_load_b128(rx, off + 16u, 0, 0);
     }
@@ -66,19 +69,20 @@ __device__ __forceinline__ void x_load(int K, const uint16_t *__restrict__ x, XL
 // What limbs_build leaves unwritten: the zero bytes of every block, and, when K is not a
 // multiple of 1024, the last pair's two segments in full (zero limbs, unit exponents 2^0),
 // so that groups past K add nothing.  Every row of a segment inside K is written by the build.
+template <int NT>
 __device__ __forceinline__ void limbs_fill(int K, uint8_t *lds)
 {
     const int nseg = nseg_of(K);
     const int full = ((K >> 7) & 7) ? nseg - 2 : nseg;     // segments the build covers
     uint32_t *sc = reinterpret_cast<uint32_t *>(lds + nseg * 4 * kBlk);
     const int tid = threadIdx.x;
-    for (int i = tid; i < nseg * 4; i += 256) *reinterpret_cast<u4v *>(lds + i * kBlk + kZero) = u4v{0, 0, 0, 0};
+    for (int i = tid; i < nseg * 4; i += NT) *reinterpret_cast<u4v *>(lds + i * kBlk + kZero) = u4v{0, 0, 0, 0};
     u4v *tail = reinterpret_cast<u4v *>(lds + full * 4 * kBlk);
-    for (int i = tid; i < (nseg - full) * 4 * kBlk / 16; i += 256) tail[i] = u4v{0, 0, 0, 0};
-    for (int i = tid; i < (nseg - full) * 16; i += 256) sc[full * 16 + i] = 0x7F7F7F7Fu;
+    for (int i = tid; i < (nseg - full) * 4 * kBlk / 16; i += NT) tail[i] = u4v{0, 0, 0, 0};
+    for (int i = tid; i < (nseg - full) * 16; i += NT) sc[full * 16 + i] = 0x7F7F7F7Fu;
 }
 
-template <int XT, bool T2>
+template <int XT, bool T2, int NT>
 __device__ __forceinline__ void limbs_build(int K, uint8_t *lds, const XLoad<XT> &xl)
 {
     const int nseg = nseg_of(K);
@@ -87,8 +91,8 @@ __device__ __forceinline__ void limbs_build(int K, uint8_t *lds, const XLoad<XT>
     const int ntask = K >> 4;                       // even, so a 32-block's two tasks pair up
 #pragma unroll
     for (int q = 0; q < XT; ++q) {
-        const int tau = tid + 256 * q;
-        if (256 * q >= ntask) break;                  // uniform: no task of this round
+        const int tau = tid + NT * q;
+        if (NT * q >= ntask) break;                   // uniform: no task of this round
         const u4v p0 = xl.v[q][0], p1 = xl.v[q][1];
         float mx = absmax16(p0, p1);
         mx = fmaxf(mx, __shfl_xor(mx, 1, kWave));        // the other half of the 32-block
@@ -146,8 +150,8 @@ struct Slot {
     uint16_t s1[R][SP];
 };
 
-template <int SP, int P, int R, bool ODD, bool T2>
-__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 4)))
+template <int SP, int P, int R, bool ODD, bool T2, int NW>
+__global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(NW / 4, 4)))
 void gemv_mx_kernel(const uint16_t *__restrict__ x, int K, int tq, int tr, int grid, const uint32_t *W0,
                     const uint16_t *S0, int N0, int te0, MxSet set)
 {
@@ -155,6 +159,7 @@ void gemv_mx_kernel(const uint16_t *__restrict__ x, int K, int tq, int tr, int g
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);      // wave-uniform
     const int n = lane & 15, g = lane >> 4;
+    constexpr int NT = 64 * NW;                      // threads
     const int npair = (K + 1023) >> 10, nseg = 2 * npair;
     const int wpr = T2 ? K >> 4 : K >> 5, spr = K >> 7;   // words per row: 16 or 32 weights each
     constexpr int kGW = T2 ? 8 : 4;                      // words per scale group
@@ -179,7 +184,7 @@ void gemv_mx_kernel(const uint16_t *__restrict__ x, int K, int tq, int tr, int g
             const bool rok = row < N;
 #pragma unroll
             for (int q = 0; q < SP; ++q) {
-                const int gam = 8 * (wave + 4 * q) + 2 * g;     // this lane's first group
+                const int gam = 8 * (wave + NW * q) + 2 * g;    // this lane's first group
                 const bool ok0 = rok && gam < spr, ok1 = rok && gam + 1 < spr;
                 const unsigned ow = (mul24((unsigned)row, (unsigned)wpr) + (unsigned)kGW * gam) * 4u;
                 const unsigned os = (mul24((unsigned)row, (unsigned)spr) + gam) * 2u;
@@ -207,9 +212,9 @@ void gemv_mx_kernel(const uint16_t *__restrict__ x, int K, int tq, int tr, int g
     // Entry: the x loads, then the first tile's weights straight from the kernel argument
     // (most launches give a workgroup one tile, whose weight latency is then the critical
     // path), and only then the LDS fill and the lane table for the other ring slots.
-    constexpr int XT = SP;                           // activation tasks per thread (K <= 4096*SP)
+    constexpr int XT = SP;                           // activation tasks per thread (K <= 1024*NW*SP)
     XLoad<XT> xl;
-    x_load<XT>(K, x, xl);
+    x_load<XT, NT>(K, x, xl);
     __builtin_amdgcn_sched_barrier(0);               // x loads go out before the argument-table loads
     {
         // only the scalars are chosen under the (uniform) branch: one issue after it, so no
@@ -225,12 +230,12 @@ void gemv_mx_kernel(const uint16_t *__restrict__ x, int K, int tq, int tr, int g
         }
         issue_t(row0, my_tiles > 0 ? Nt : 0, Wp, Sp, ring[0]);
     }
-    limbs_fill(K, lds);
+    limbs_fill<NT>(K, lds);
     const TileTab tab = tile_tab<R>(set, blockIdx.x + lane * grid);
 #pragma unroll
     for (int p = 1; p < P; ++p) issue(tab, p, ring[p]);
     __syncthreads();                                  // zero-filled limb area visible
-    limbs_build<XT, T2>(K, lds, xl);
+    limbs_build<XT, T2, NT>(K, lds, xl);
     __syncthreads();                                  // limbs visible
 
     const uint32_t *sc = reinterpret_cast<const uint32_t *>(lds + nseg * 4 * kBlk);
@@ -247,8 +252,8 @@ void gemv_mx_kernel(const uint16_t *__restrict__ x, int K, int tq, int tr, int g
     for (int q = 0; q < SP; ++q)
 #pragma unroll
         for (int h = 0; h < 2; ++h) {
-            const int sigma = 2 * (wave + 4 * q) + h;
-            const bool v = wave + 4 * q < npair;
+            const int sigma = 2 * (wave + NW * q) + h;
+            const bool v = wave + NW * q < npair;
             const uint8_t *blk = lds + (v ? sigma : 0) * 4 * kBlk;
 #pragma unroll
             for (int t = 0; t < 4; ++t) A[q][h][t] = load_a(blk + t * kBlk, lo, hi);
@@ -268,7 +273,7 @@ void gemv_mx_kernel(const uint16_t *__restrict__ x, int K, int tq, int tr, int g
             for (int r = 0; r < R; ++r) acc[r] = 0.f;
 #pragma unroll
             for (int q = 0; q < SP; ++q) {
-                const int pr = wave + 4 * q;
+                const int pr = wave + NW * q;
                 if (pr < npair) {                     // wave-uniform
                     const int gam = 8 * pr + 2 * g;
 #pragma unroll
@@ -302,42 +307,46 @@ void gemv_mx_kernel(const uint16_t *__restrict__ x, int K, int tq, int tr, int g
                 }
             }
             issue(tab, it + P, ring[p]);
-            float *rb = red + it * (64 * R);          // [tile][16R rows][4 waves]
+            float *rb = red + it * (16 * NW * R);     // [tile][16R rows][NW waves]
 #pragma unroll
             for (int r = 0; r < R; ++r) {
                 const float v = sum_groups(acc[r]);
-                if (lane < 16) rb[(16 * r + lane) * 4 + wave] = v;
+                if (lane < 16) rb[(16 * r + lane) * NW + wave] = v;
             }
         }
     }
 done:
     __syncthreads();
-    // Merge: thread t finishes rows t, t+256, ... of the workgroup's tiles in order.
-    for (int e = tid; e < my_tiles * 16 * R; e += 256) {
+    // Merge: thread t finishes rows t, t+NT, ... of the workgroup's tiles in order.
+    for (int e = tid; e < my_tiles * 16 * R; e += NT) {
         const int it = e / (16 * R), j = e - it * (16 * R);
         const int row = __shfl(tab.row0, it, kWave) + j, N = __shfl(tab.N, it, kWave);
         const unsigned long long yp = ((unsigned long long)(unsigned)__shfl((unsigned)(tab.y >> 32), it, kWave) << 32) |
                                       (unsigned)__shfl((unsigned)tab.y, it, kWave);
-        const float4v pr4 = *reinterpret_cast<const float4v *>(red + e * 4);
-        const float tot = (pr4[0] + pr4[1]) + (pr4[2] + pr4[3]);
+        const float4v pr4 = *reinterpret_cast<const float4v *>(red + e * NW);
+        float tot = (pr4[0] + pr4[1]) + (pr4[2] + pr4[3]);
+        if constexpr (NW == 8) {
+            const float4v pr8 = *reinterpret_cast<const float4v *>(red + e * NW + 4);
+            tot += (pr8[0] + pr8[1]) + (pr8[2] + pr8[3]);
+        }
         if (row < N) reinterpret_cast<uint16_t *>(yp)[row] = f2h_rne(tot);
     }
 }
 
 constexpr int kMaxPairs = 20;                         // K <= 20480 (A operands fit in registers)
 constexpr int kMaxTileRows = 2048;                     // rows per workgroup held in the merge table
-// LDS: limb blocks and exponents for K, then the merge table [tile][16R rows][4 waves] fp32.
-constexpr size_t shm_bytes(int K, int rows_per_wg)
+// LDS: limb blocks and exponents for K, then the merge table [tile][16R rows][NW waves] fp32.
+constexpr size_t shm_bytes(int K, int rows_per_wg, int NW)
 {
-    return (size_t)(2 * ((K + 1023) >> 10)) * (4 * kBlk + 64) + (size_t)rows_per_wg * 4 * 4;
+    return (size_t)(2 * ((K + 1023) >> 10)) * (4 * kBlk + 64) + (size_t)rows_per_wg * NW * 4;
 }
 
-template <int SP, int P, int R, bool ODD, bool T2>
+template <int SP, int P, int R, bool ODD, bool T2, int NW = 4>
 hipError_t launch_mx(const uint16_t *x, const MxSet &set0, int K, hipStream_t st)
 {
     static const hipError_t attr = hipFuncSetAttribute(
-        reinterpret_cast<const void *>(&gemv_mx_kernel<SP, P, R, ODD, T2>),
-        hipFuncAttributeMaxDynamicSharedMemorySize, (int)shm_bytes(kMaxPairs * 1024, kMaxTileRows));
+        reinterpret_cast<const void *>(&gemv_mx_kernel<SP, P, R, ODD, T2, NW>),
+        hipFuncAttributeMaxDynamicSharedMemorySize, (int)shm_bytes(kMaxPairs * 1024, kMaxTileRows, NW));
     if (attr != hipSuccess) return attr;
     MxSet set = set0;
     int tiles = 0;
@@ -347,13 +356,13 @@ hipError_t launch_mx(const uint16_t *x, const MxSet &set0, int K, hipStream_t st
     }
     // Resident workgroups per CU follow the register budget (A operands dominate it); the
     // grid grows past that only when a workgroup's rows would overflow the merge table.
-    const int cap = SP <= 2 ? 2 * 256 : 256;
+    const int cap = SP <= 2 && NW == 4 ? 2 * 256 : 256;
     // tiles per workgroup: at most what the merge table holds and the one-per-lane tile table
     constexpr int kMaxT = kMaxTileRows / (16 * R) < 64 ? kMaxTileRows / (16 * R) : 64;
     const int need = (tiles + kMaxT - 1) / kMaxT;
     const int grid = tiles < cap ? tiles : (need > cap ? need : cap);
     const int rows_per_wg = (tiles + grid - 1) / grid * 16 * R;
-    hipLaunchKernelGGL((gemv_mx_kernel<SP, P, R, ODD, T2>), dim3(grid), dim3(256), shm_bytes(K, rows_per_wg),
+    hipLaunchKernelGGL((gemv_mx_kernel<SP, P, R, ODD, T2, NW>), dim3(grid), dim3(64 * NW), shm_bytes(K, rows_per_wg, NW),
                        st, x, K, tiles / grid, tiles % grid, grid, set.W[0], set.S[0], set.N[0], set.tile_end[0],
                        set);
     return hipGetLastError();
@@ -383,10 +392,12 @@ hipError_t dispatch_mx(const uint16_t *x, const MxSet &set, int K, hipStream_t s
     case 2: return one16 ? launch_mx<2, 1, 1, ODD, T2>(x, set, K, st)
                  : one   ? launch_mx<2, 1, 2, ODD, T2>(x, set, K, st)
                  : few16 ? launch_mx<2, 2, 1, ODD, T2>(x, set, K, st) : launch_mx<2, 2, 2, ODD, T2>(x, set, K, st);
-    case 3: return one16 ? launch_mx<3, 1, 1, ODD, T2>(x, set, K, st)
+    // long rows with one 16-row tile per workgroup: 8 waves, at most ceil(pairs / 8) pairs each
+    case 3: return one16 ? launch_mx<2, 1, 1, ODD, T2, 8>(x, set, K, st)
                  : one   ? launch_mx<3, 1, 2, ODD, T2>(x, set, K, st) : launch_mx<3, 2, 2, ODD, T2>(x, set, K, st);
     // (ternary rows are twice as many bytes: 16-row tiles keep the ring in registers)
     case 4:
+        if (one16) return launch_mx<2, 1, 1, ODD, T2, 8>(x, set, K, st);
         if constexpr (T2) return launch_mx<4, 1, 1, ODD, T2>(x, set, K, st);
         else return launch_mx<4, 1, 2, ODD, T2>(x, set, K, st);
     default:

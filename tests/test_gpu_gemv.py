@@ -21,7 +21,8 @@ def _case(t, M, K, N):
     return synth.activations(r, M, K), synth.sign_words(r, N, K), synth.group_scales(r, N, K)
 
 
-SMALL = [(128, 1), (128, 7), (256, 64), (512, 300), (1024, 1000), (4096, 1024), (12288, 130), (17408, 33)]
+SMALL = [(128, 1), (128, 7), (256, 64), (512, 300), (1024, 1000), (4096, 1024), (12288, 130), (13440, 90),
+         (16384, 48), (17408, 33)]
 
 
 @pytest.mark.parametrize("K,N", SMALL)
