@@ -88,7 +88,7 @@ struct SmTile {     // one tile of the workgroup, resolved once
 // load in flight where the paths meet).
 template <int TB, int D>
 __global__ __launch_bounds__(64 * kWaves) __attribute__((amdgpu_waves_per_eu(2, 2)))
-void gemv_smallm_kernel(const uint16_t *__restrict__ x, MxSet set, int M, int K, int ntiles)
+void gemv_smallm_kernel(const uint16_t *__restrict__ x, int M, int K, int tq, int tr, int G, MxSet set)
 {
     extern __shared__ __attribute__((aligned(16))) uint16_t xs[];   // staged chunk [16][kXRow]
     float *red = reinterpret_cast<float *>(xs);                     // then [tile][wave][lane][4]
@@ -97,9 +97,23 @@ void gemv_smallm_kernel(const uint16_t *__restrict__ x, MxSet set, int M, int K,
     const int n = lane & 15, b = lane >> 4;
     const int wpr = K >> 5, spr = K >> 7;
     const int nchunk = (spr + kChunkGroups - 1) / kChunkGroups;
-    const int G = gridDim.x;
-    const int nb = __builtin_amdgcn_readfirstlane(blockIdx.x < ntiles ? (ntiles - 1 - blockIdx.x) / G + 1 : 0);  // <= TB
+    // the scalars come first in the argument list and arrive preloaded in registers; the tile
+    // count is split on the host (tiles = tq * G + tr, G the grid size)
+    const int nb = tq + (blockIdx.x < (unsigned)tr ? 1 : 0);                              // <= TB
     const __amdgpu_buffer_rsrc_t rx = rsrc(x, (unsigned)M * (unsigned)K * 2u);
+
+    // thread t's share of a chunk: 8 k of every token row; rows past M are outside the buffer
+    // range, and k past K starts from an out-of-range base, so both load zeros
+    u4v xr[16];
+    auto fetch_x = [&](int c) {
+        const unsigned kc = (unsigned)(c * kChunkK) + 8u * threadIdx.x;
+        const unsigned base = kc < (unsigned)K ? kc * 2u : kOob;
+#pragma unroll
+        for (int m = 0; m < 16; ++m)
+            xr[m] = __builtin_amdgcn_raw_buffer_load_b128(rx, base + (unsigned)m * (unsigned)K * 2u, 0, 0);
+    };
+    fetch_x(0);                                       // first: staging it waits on nothing else
+    __builtin_amdgcn_sched_barrier(0);               // (ahead of the argument-table loads)
 
     // lane t resolves tile slot t (matrix, first row) with vector selects; the results are
     // then read into scalar registers, so every wave holds them at the cost of a few readlanes
@@ -140,17 +154,6 @@ void gemv_smallm_kernel(const uint16_t *__restrict__ x, MxSet set, int M, int K,
         sl.w = __builtin_amdgcn_raw_buffer_load_b128(rW, (mul24(row, (unsigned)wpr) + 4u * gb) * 4u, 0, kNT);
         sl.s = __builtin_amdgcn_raw_buffer_load_b16(rS, (mul24(row, (unsigned)spr) + gb) * 2u, 0, 0);
     };
-    // thread t's share of a chunk: 8 k of every token row; rows past M are outside the buffer
-    // range, and k past K starts from an out-of-range base, so both load zeros
-    u4v xr[16];
-    auto fetch_x = [&](int c) {
-        const unsigned kc = (unsigned)(c * kChunkK) + 8u * threadIdx.x;
-        const unsigned base = kc < (unsigned)K ? kc * 2u : kOob;
-#pragma unroll
-        for (int m = 0; m < 16; ++m)
-            xr[m] = __builtin_amdgcn_raw_buffer_load_b128(rx, base + (unsigned)m * (unsigned)K * 2u, 0, 0);
-    };
-    fetch_x(0);                                       // first: staging it waits on nothing else
 #pragma unroll
     for (int d = 0; d < DS; ++d)
 #pragma unroll
@@ -246,8 +249,8 @@ hipError_t launch_sm(const uint16_t *x, const MxSet &set, int M, int K, int tile
                                                        hipFuncAttributeMaxDynamicSharedMemorySize, kXBytes);
     if (attr != hipSuccess) return attr;
     const int grid = (tiles + TB - 1) / TB;
-    hipLaunchKernelGGL((gemv_smallm_kernel<TB, D>), dim3(grid), dim3(64 * kWaves), kXBytes, st, x, set, M, K,
-                       tiles);
+    hipLaunchKernelGGL((gemv_smallm_kernel<TB, D>), dim3(grid), dim3(64 * kWaves), kXBytes, st, x, M, K,
+                       tiles / grid, tiles % grid, grid, set);
     return hipGetLastError();
 }
 
