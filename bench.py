@@ -418,8 +418,8 @@ def extra_pm1(dev):
 def main():
     args = parse()
     if args.gpus != 1:
-        print(json.dumps({"error": "this benchmark runs on one GPU only; runs on several GPUs are not "
-                                   "part of this build (the design notes describe how the path shards)",
+        print(json.dumps({"error": "this benchmark measures one GPU only: the products here run on one "
+                                   "GPU's share of the weights, and no multi-GPU path is provided",
                           "n_gpus": args.gpus}))
         sys.exit(2)
     import torch

@@ -22,7 +22,7 @@
  *    section: a patch is a list of (layer, projection, row) entries whose bits
  *    are flipped; the same XOR applies and removes it.
  *
- * Readings where the pages are silent (each also listed in the design notes):
+ * Readings where the pages are silent:
  *  - bit order: bit b of word j is weight k = 32*j + b (LSB first); bit 1 = +1.
  *  - the scale group runs along K, aligned at k = 0; G is a parameter here only
  *    so that tiny cases (K < 128) can be enumerated exhaustively.
