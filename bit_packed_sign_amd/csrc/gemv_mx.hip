@@ -131,6 +131,22 @@ __device__ __forceinline__ TileTab tile_tab(const MxSet &set, int tile)
     return t;
 }
 
+// The same for a launch of at most two matrices, from scalar kernel arguments (no argument-table
+// loads); the output pointer is filled in later, for the merge.
+template <int R>
+__device__ __forceinline__ TileTab tile_tab2(const uint32_t *W0, const uint16_t *S0, int N0, int te0,
+                                             const uint32_t *W1, const uint16_t *S1, int N1, int tile)
+{
+    const bool m1 = tile >= te0;
+    TileTab t;
+    t.row0 = (tile - (m1 ? te0 : 0)) * 16 * R;
+    t.N = m1 ? N1 : N0;
+    t.W = (unsigned long long)(m1 ? W1 : W0);
+    t.S = (unsigned long long)(m1 ? S1 : S0);
+    t.y = 0;
+    return t;
+}
+
 __device__ __forceinline__ int lane_of(int v, int l) { return __builtin_amdgcn_readlane(v, l); }
 
 __device__ __forceinline__ unsigned long long lane_of(unsigned long long v, int l)
@@ -150,11 +166,13 @@ struct Slot {
     uint16_t s1[R][SP];
 };
 
-template <int SP, int P, int R, bool ODD, bool T2, int NW>
+template <int SP, int P, int R, bool ODD, bool T2, int NW, bool TWO>
 __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(NW / 4, 4)))
-void gemv_mx_kernel(const uint16_t *__restrict__ x, int K, int tq, int tr, int grid, const uint32_t *W0,
-                    const uint16_t *S0, int N0, int te0, MxSet set)
+void gemv_mx_kernel(const uint16_t *__restrict__ x, int Ktq, int trg, const uint32_t *W0, const uint16_t *S0,
+                    const uint32_t *W1, const uint16_t *S1, int N0, int N1, MxSet set)
 {
+    const int K = Ktq & 0xFFFF, tq = Ktq >> 16, tr = trg & 0xFFFF, grid = trg >> 16;
+    const int te0 = (N0 + 16 * R - 1) / (16 * R);   // matrix 0's tiles
     extern __shared__ __attribute__((aligned(16))) uint8_t lds[];
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);      // wave-uniform
@@ -164,10 +182,12 @@ void gemv_mx_kernel(const uint16_t *__restrict__ x, int K, int tq, int tr, int g
     const int wpr = T2 ? K >> 4 : K >> 5, spr = K >> 7;   // words per row: 16 or 32 weights each
     constexpr int kGW = T2 ? 8 : 4;                      // words per scale group
     // The scalars come first in the argument list so that they arrive preloaded in registers
-    // (with matrix 0's pointers, its row count and tile end): the tile count is split on the
-    // host (tiles = tq * grid + tr), so no load of the grid size and no division sit in front
-    // of the first loads, and a workgroup whose first tile is in matrix 0 starts its weight
-    // loads without waiting for the argument table.
+    // (14 dwords, what the hardware preloads: K and tq, tr and the grid size packed in halves;
+    // the first two matrices' pointers and row counts): the tile count is split on the host
+    // (tiles = tq * grid + tr), so no load of the grid size and no division sit in front of the
+    // first loads.  With at most two matrices (TWO) the whole tile table comes from these
+    // scalars; otherwise a workgroup whose first tile is in matrix 0 starts its weight loads
+    // without waiting for the argument table.
     const int my_tiles = tq + (blockIdx.x < (unsigned)tr ? 1 : 0);         // <= 64
 
     Slot<SP, R, T2> ring[P];
@@ -216,7 +236,13 @@ void gemv_mx_kernel(const uint16_t *__restrict__ x, int K, int tq, int tr, int g
     XLoad<XT> xl;
     x_load<XT, NT>(K, x, xl);
     __builtin_amdgcn_sched_barrier(0);               // x loads go out before the argument-table loads
-    {
+    TileTab tab;
+    if constexpr (TWO) {
+        tab = tile_tab2<R>(W0, S0, N0, te0, W1, S1, N1, blockIdx.x + lane * grid);
+#pragma unroll
+        for (int p = 0; p < P; ++p) issue(tab, p, ring[p]);
+        limbs_fill<NT>(K, lds);
+    } else {
         // only the scalars are chosen under the (uniform) branch: one issue after it, so no
         // load sits on either side of a join
         unsigned long long Wp = (unsigned long long)W0, Sp = (unsigned long long)S0;
@@ -229,11 +255,11 @@ void gemv_mx_kernel(const uint16_t *__restrict__ x, int K, int tq, int tr, int g
             Nt = t0.N;
         }
         issue_t(row0, my_tiles > 0 ? Nt : 0, Wp, Sp, ring[0]);
-    }
-    limbs_fill<NT>(K, lds);
-    const TileTab tab = tile_tab<R>(set, blockIdx.x + lane * grid);
+        limbs_fill<NT>(K, lds);
+        tab = tile_tab<R>(set, blockIdx.x + lane * grid);
 #pragma unroll
-    for (int p = 1; p < P; ++p) issue(tab, p, ring[p]);
+        for (int p = 1; p < P; ++p) issue(tab, p, ring[p]);
+    }
     __syncthreads();                                  // zero-filled limb area visible
     limbs_build<XT, T2, NT>(K, lds, xl);
     __syncthreads();                                  // limbs visible
@@ -316,6 +342,10 @@ void gemv_mx_kernel(const uint16_t *__restrict__ x, int K, int tq, int tr, int g
         }
     }
 done:
+    if constexpr (TWO) {                              // the outputs, for the merge
+        const int tile = blockIdx.x + lane * grid;
+        tab.y = (unsigned long long)(tile >= te0 ? set.y[1] : set.y[0]);
+    }
     __syncthreads();
     // Merge: thread t finishes rows t, t+NT, ... of the workgroup's tiles in order.
     for (int e = tid; e < my_tiles * 16 * R; e += NT) {
@@ -341,11 +371,11 @@ constexpr size_t shm_bytes(int K, int rows_per_wg, int NW)
     return (size_t)(2 * ((K + 1023) >> 10)) * (4 * kBlk + 64) + (size_t)rows_per_wg * NW * 4;
 }
 
-template <int SP, int P, int R, bool ODD, bool T2, int NW = 4>
-hipError_t launch_mx(const uint16_t *x, const MxSet &set0, int K, hipStream_t st)
+template <int SP, int P, int R, bool ODD, bool T2, int NW, bool TWO>
+hipError_t launch_mx_t(const uint16_t *x, const MxSet &set0, int K, hipStream_t st)
 {
     static const hipError_t attr = hipFuncSetAttribute(
-        reinterpret_cast<const void *>(&gemv_mx_kernel<SP, P, R, ODD, T2, NW>),
+        reinterpret_cast<const void *>(&gemv_mx_kernel<SP, P, R, ODD, T2, NW, TWO>),
         hipFuncAttributeMaxDynamicSharedMemorySize, (int)shm_bytes(kMaxPairs * 1024, kMaxTileRows, NW));
     if (attr != hipSuccess) return attr;
     MxSet set = set0;
@@ -362,10 +392,20 @@ hipError_t launch_mx(const uint16_t *x, const MxSet &set0, int K, hipStream_t st
     const int need = (tiles + kMaxT - 1) / kMaxT;
     const int grid = tiles < cap ? tiles : (need > cap ? need : cap);
     const int rows_per_wg = (tiles + grid - 1) / grid * 16 * R;
-    hipLaunchKernelGGL((gemv_mx_kernel<SP, P, R, ODD, T2, NW>), dim3(grid), dim3(64 * NW), shm_bytes(K, rows_per_wg, NW),
-                       st, x, K, tiles / grid, tiles % grid, grid, set.W[0], set.S[0], set.N[0], set.tile_end[0],
-                       set);
+    const bool two = set.count == 2;
+    hipLaunchKernelGGL((gemv_mx_kernel<SP, P, R, ODD, T2, NW, TWO>), dim3(grid), dim3(64 * NW),
+                       shm_bytes(K, rows_per_wg, NW), st, x, K | (tiles / grid) << 16, (tiles % grid) | grid << 16,
+                       set.W[0], set.S[0], two ? set.W[1] : nullptr, two ? set.S[1] : nullptr, set.N[0],
+                       two ? set.N[1] : 0, set);
     return hipGetLastError();
+}
+
+// Launches of at most two matrices take their whole tile table from scalar arguments.
+template <int SP, int P, int R, bool ODD, bool T2, int NW = 4>
+hipError_t launch_mx(const uint16_t *x, const MxSet &set, int K, hipStream_t st)
+{
+    return set.count <= 2 ? launch_mx_t<SP, P, R, ODD, T2, NW, true>(x, set, K, st)
+                          : launch_mx_t<SP, P, R, ODD, T2, NW, false>(x, set, K, st);
 }
 
 template <bool ODD, bool T2>
