@@ -260,7 +260,9 @@ void gemv_mx_kernel(const uint16_t *__restrict__ x, int Ktq, int trg, const uint
 #pragma unroll
         for (int p = 1; p < P; ++p) issue(tab, p, ring[p]);
     }
-    __syncthreads();                                  // zero-filled limb area visible
+    // The fill and the build write disjoint bytes unless the last pair is partial (the fill then
+    // zeroes the build's last segments first): only then must the fill be complete before it.
+    if ((K >> 7) & 7) __syncthreads();
     limbs_build<XT, T2, NT>(K, lds, xl);
     __syncthreads();                                  // limbs visible
 
