@@ -92,13 +92,27 @@ class Step:
         gi = 0
         for s, stage in enumerate(wl.stages):
             xs = torch.from_numpy(synth.stage_activations(0, wl, s)).to(device)
-            Ws, Ss, ys = [], [], []
+            # The projections of one stage (q/k/v, gate/up) live back to back in one allocation
+            # each for weights, scales and (at batch 1) outputs, the usual fused layout.
+            bits_l, scales_l = [], []
             for g in stage.gemvs:
                 bits, scales = (synth.ternary_gemv_tensors if ternary else synth.gemv_tensors)(0, wl, gi)
-                Ws.append(torch.from_numpy(bits.view(np.int32)).to(device))
-                Ss.append(torch.from_numpy(scales).to(device))
-                ys.append(torch.empty((wl.M, g.N), dtype=torch.float16, device=device))
+                bits_l.append(bits.view(np.int32))
+                scales_l.append(scales)
                 gi += 1
+            W_all = torch.from_numpy(np.concatenate(bits_l)).to(device)
+            S_all = torch.from_numpy(np.concatenate(scales_l)).to(device)
+            ntot = sum(g.N for g in stage.gemvs)
+            y_all = torch.empty((wl.M, ntot), dtype=torch.float16, device=device) if wl.M == 1 else None
+            Ws, Ss, ys = [], [], []
+            r = 0
+            for g in stage.gemvs:
+                Ws.append(W_all[r:r + g.N])
+                Ss.append(S_all[r:r + g.N])
+                ys.append(y_all[:, r:r + g.N] if y_all is not None
+                          else torch.empty((wl.M, g.N), dtype=torch.float16, device=device))
+                r += g.N
+            del bits_l, scales_l
             nbytes = sum(round(g.N * g.K * synth.TERNARY_BYTES_PER_WEIGHT) if ternary else g.weight_bytes
                          for g in stage.gemvs)
             self.stages.append((xs, Ws, Ss, ys, nbytes))

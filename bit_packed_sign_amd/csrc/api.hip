@@ -296,6 +296,20 @@ int gemv_group_impl(const char *fn, bool t2, const void *x, int count, const uin
         const int st = check_product_host(x, Wbits[i], scales[i], y[i], M, K, N[i], bits);
         if (st < 0) return st;
         if (st == kEmpty) continue;
+        // At M == 1, a matrix stored right after the previous kept one (its weights, scales and
+        // outputs each start where the previous one's end, as in a fused q/k/v layout) extends
+        // that one: rows are independent, so the taller matrix gives the same products.
+        if (M == 1 && kept > 0) {
+            const int p = kept - 1;
+            const size_t n = (size_t)Nk[p], nn = n + (size_t)N[i];
+            const bool adjacent = Wbits[i] == Wk[p] + n * (size_t)(K / 32) * bits &&
+                                  scales[i] == static_cast<const char *>(Sk[p]) + n * (size_t)(K / 128) * 2 &&
+                                  y[i] == static_cast<char *>(yk[p]) + n * 2;
+            if (adjacent && nn < (1u << 24) - 64 && nn * (size_t)(K / 8) * bits < (1ull << 31)) {
+                Nk[p] = (int)nn;
+                continue;
+            }
+        }
         Wk[kept] = Wbits[i];
         Sk[kept] = scales[i];
         yk[kept] = y[i];

@@ -86,7 +86,9 @@ int bin1_gemv(const void *x, const uint32_t *Wbits, const void *scales, void *y,
  * matrix i exactly as in bin1_gemv (Wbits[i] [N[i]][K/32], scales[i] [N[i]][K/128],
  * y[i] [M][N[i]]).  Every y[i] must be disjoint from every input and from the other
  * outputs.  Results equal `count` separate bin1_gemv calls; a matrix with N[i] == 0 is
- * skipped. */
+ * skipped.  At M == 1, matrices stored back to back (weights, scales and outputs of one
+ * each starting where the previous one's end, as in a fused q/k/v allocation) are run as
+ * one taller matrix, which launches faster and gives the same results. */
 int bin1_gemv_group(const void *x, int count, const uint32_t *const *Wbits,
                     const void *const *scales, void *const *y, const int *N,
                     int M, int K, void *stream);

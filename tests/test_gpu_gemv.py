@@ -151,6 +151,51 @@ def test_gemv_group_equals_separate_calls(dev, M):
         assert torch.equal(b1.gemv(xd, W, S), y)
 
 
+def _back_to_back(dev, mats, M, widths):
+    """Device views of one allocation each for weights, scales and outputs, matrix i's rows right
+    after matrix i-1's (a fused q/k/v layout)."""
+    W_all = dev_tensors(dev, W=np.concatenate([W for W, _ in mats]))[0]
+    S_all = dev_tensors(dev, S=np.concatenate([S for _, S in mats]))[0]
+    y_all = torch.full((M, sum(widths)), float("nan"), dtype=torch.float16, device=dev)
+    offs = np.concatenate([[0], np.cumsum(widths)])
+    return ([W_all[a:b] for a, b in zip(offs[:-1], offs[1:])], [S_all[a:b] for a, b in zip(offs[:-1], offs[1:])],
+            [y_all[:, a:b] for a, b in zip(offs[:-1], offs[1:])])
+
+
+@pytest.mark.parametrize("K,Ns", [(4096, (4096, 1024, 1024)), (4096, (12288, 12288)), (4352, (296, 1000, 24, 2047)),
+                                  (384, (8, 40, 104, 17)), (12288, (1000, 24))])
+def test_gemv_group_back_to_back(orc, dev, K, Ns):
+    """Matrices stored back to back (weights, scales and outputs) run as one taller matrix at
+    M == 1: every output matches the oracle and the one-call-per-matrix results; a mixed group
+    (only some neighbours adjacent, or adjacent weights with separate outputs) as well."""
+    r = synth.rng_for(0, synth.WL_TEST, 7500 + K + sum(Ns))
+    x = synth.activations(r, 1, K)
+    mats = [(synth.sign_words(r, n, K), synth.group_scales(r, n, K)) for n in Ns]
+    xd = dev_tensors(dev, x)[0]
+    Wv, Sv, yv = _back_to_back(dev, mats, 1, Ns)
+    outs = [y.clone() for y in b1.gemv_group(xd, Wv, Sv, outs=yv)]
+    for (W, S), y, Wd, Sd in zip(mats, outs, Wv, Sv):
+        N = W.shape[0]
+        rows = sample_rows(r, N, k=128) if N > 2048 else np.arange(N)
+        ref, nrm = orc.gemv_rows(x, W, S, rows)
+        assert norm_err(y.float().cpu().numpy()[:, rows], ref, nrm) <= TOL
+        if K <= 8192:                            # same kernel layout per row: identical bits
+            assert torch.equal(y, b1.gemv(xd, Wd, Sd))
+    separate = b1.gemv_group(xd, Wv, Sv)         # adjacent weights, outputs allocated per matrix
+    mixed = list(Wv), list(Sv), list(yv)
+    if len(Ns) > 2:                              # matrix 1 moved out: 0, 1 no longer adjacent, 2, 3 still
+        mixed[0][1], mixed[1][1] = Wv[1].clone(), Sv[1].clone()
+    for y in yv:
+        y.fill_(float("nan"))
+    mixed_out = b1.gemv_group(xd, mixed[0], mixed[1], outs=mixed[2])
+    for (W, S), a, b, c in zip(mats, outs, separate, mixed_out):
+        if K <= 8192:
+            assert torch.equal(a, b) and torch.equal(a, c)
+        else:                                    # long rows: the split over waves may differ
+            ref, nrm = orc.gemv(x, W, S)
+            assert norm_err(b, ref, nrm) <= TOL and norm_err(c, ref, nrm) <= TOL
+
+
 def test_gemv_repeated_calls_are_deterministic(dev):
     """The same inputs give bit-identical outputs on every call (fixed accumulation order)."""
     x, W, S = _case(7100, 1, 4096, 12288)

@@ -119,3 +119,28 @@ def test_ternary_group_matches_oracle_and_separate_calls(orc, dev, M, K, Ns):
         ref, nrm = orc.gemv_t2_rows(x, T, S, rows)
         assert norm_err(y.float().cpu().numpy()[:, rows], ref, nrm) <= TOL
         assert torch.equal(b1.gemv_t2(xd, Tdev, Sdev), y)
+
+
+@pytest.mark.parametrize("K,Ns", [(4096, (4096, 1024, 1024)), (5120, (17408, 17408)), (384, (8, 40, 104, 17))])
+def test_ternary_group_back_to_back(orc, dev, K, Ns):
+    """Ternary matrices stored back to back (slots, scales and outputs) run as one taller matrix
+    at M == 1; outputs match the oracle and the one-call-per-matrix results bit for bit."""
+    r = synth.rng_for(0, synth.WL_TEST, 17500 + K + sum(Ns))
+    x = synth.activations(r, 1, K)
+    Ts = [synth.ternary_words(r, n, K) for n in Ns]
+    Ss = [synth.group_scales(r, n, K) for n in Ns]
+    xd = dev_tensors(dev, x)[0]
+    T_all = dev_tensors(dev, W=np.concatenate(Ts))[0]
+    S_all = dev_tensors(dev, S=np.concatenate(Ss))[0]
+    y_all = torch.full((1, sum(Ns)), float("nan"), dtype=torch.float16, device=dev)
+    offs = np.concatenate([[0], np.cumsum(Ns)])
+    Tv = [T_all[a:b] for a, b in zip(offs[:-1], offs[1:])]
+    Sv = [S_all[a:b] for a, b in zip(offs[:-1], offs[1:])]
+    yv = [y_all[:, a:b] for a, b in zip(offs[:-1], offs[1:])]
+    outs = b1.gemv_group_t2(xd, Tv, Sv, outs=yv)
+    for T, S, Tdev, Sdev, y in zip(Ts, Ss, Tv, Sv, outs):
+        N = T.shape[0]
+        rows = sample_rows(r, N, k=128) if N > 2048 else np.arange(N)
+        ref, nrm = orc.gemv_t2_rows(x, T, S, rows)
+        assert norm_err(y.float().cpu().numpy()[:, rows], ref, nrm) <= TOL
+        assert torch.equal(b1.gemv_t2(xd, Tdev, Sdev), y)
