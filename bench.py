@@ -64,6 +64,34 @@ def events():
     return torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
 
 
+def graph_launch_floor_us(device, n, reps=20):
+    """Per-launch time of a replayed graph of n dependent launches of a one-element fill (one
+    workgroup, no traffic): the launch cost that every dependent stage pays."""
+    import torch
+    t = torch.zeros(1, device=device)
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        for i in range(n):
+            t.fill_(float(i))
+    torch.cuda.current_stream().wait_stream(s)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        for i in range(n):
+            t.fill_(float(i))
+    for _ in range(3):
+        g.replay()
+    torch.cuda.synchronize()
+    e0, e1 = events()
+    e0.record()
+    for _ in range(reps):
+        g.replay()
+    e1.record()
+    torch.cuda.synchronize()
+    return e0.elapsed_time(e1) * 1e3 / reps / n
+
+
 def time_fn(fn, reps, warm=2):
     """Average ms per call of fn() over `reps` calls, HIP events on the current stream."""
     import torch
@@ -459,12 +487,15 @@ def main():
     # time over the launches (rocprofv3 kernel traces of the same command agree)
     per = step.per_launch_ms()
     nl = len(step.stages)
+    floor_us = graph_launch_floor_us(dev, nl)
+    log(f"[bench] graph of {nl} dependent one-workgroup launches: {floor_us:.2f} us per launch")
     big = max(range(nl), key=lambda i: step.stages[i][4])
     paths = {
         "graph": {"ms_per_step": round(ms_graph, 5), "gbs": round(wbytes / ms_graph / 1e6, 1),
                   "tok_s": round(1e3 / ms_graph, 1),
                   "launches": nl, "avg_launch_us_in_graph": round(ms_graph * 1e3 / nl, 3),
                   "eager_launch_sum_us": round(float(per.sum() * 1e3), 1),
+                  "graph_floor_us_per_launch": round(floor_us, 3),
                   "largest_launch_eager": {"stage": "lm_head 4096x151936", "bytes": step.stages[big][4],
                                            "us": round(float(per[big] * 1e3), 2),
                                            "gbs": round(step.stages[big][4] / (per[big] * 1e-3) / 1e9, 1)}},

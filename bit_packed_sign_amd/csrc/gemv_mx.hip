@@ -386,9 +386,10 @@ hipError_t launch_mx_t(const uint16_t *x, const MxSet &set0, int K, hipStream_t 
         tiles += (set.N[i] + 16 * R - 1) / (16 * R);
         set.tile_end[i] = tiles;
     }
-    // Resident workgroups per CU follow the register budget (A operands dominate it); the
-    // grid grows past that only when a workgroup's rows would overflow the merge table.
-    const int cap = SP <= 2 && NW == 4 ? 2 * 256 : 256;
+    // Resident workgroups per CU follow the register budget (A operands dominate it: three
+    // fit at one pair per wave, two at two); the grid grows past that only when a workgroup's
+    // rows would overflow the merge table.
+    const int cap = NW != 4 ? 256 : SP == 1 ? 3 * 256 : SP == 2 ? 2 * 256 : 256;
     // tiles per workgroup: at most what the merge table holds and the one-per-lane tile table
     constexpr int kMaxT = kMaxTileRows / (16 * R) < 64 ? kMaxTileRows / (16 * R) : 64;
     const int need = (tiles + kMaxT - 1) / kMaxT;
@@ -425,12 +426,12 @@ hipError_t dispatch_mx(const uint16_t *x, const MxSet &set, int K, hipStream_t s
     }
     // Up to three 16-row tiles per workgroup still beat 32-row tiles (even shares, shorter
     // dependent chains); past that the larger tile wins.
-    const int cap = SP <= 2 ? 2 * 256 : 256;
+    const int cap = SP == 1 ? 3 * 256 : SP == 2 ? 2 * 256 : 256;
     const bool one16 = t16 <= cap, one = t32 <= cap, few16 = t16 <= 3 * cap;
     switch (SP) {
     case 1: return one16 ? launch_mx<1, 1, 1, ODD, T2>(x, set, K, st)
                  : one   ? launch_mx<1, 1, 2, ODD, T2>(x, set, K, st)
-                 : few16 ? launch_mx<1, 3, 1, ODD, T2>(x, set, K, st) : launch_mx<1, 3, 2, ODD, T2>(x, set, K, st);
+                 : few16 ? launch_mx<1, 3, 1, ODD, T2>(x, set, K, st) : launch_mx<1, 2, 2, ODD, T2>(x, set, K, st);
     case 2: return one16 ? launch_mx<2, 1, 1, ODD, T2>(x, set, K, st)
                  : one   ? launch_mx<2, 1, 2, ODD, T2>(x, set, K, st)
                  : few16 ? launch_mx<2, 2, 1, ODD, T2>(x, set, K, st) : launch_mx<2, 2, 2, ODD, T2>(x, set, K, st);
