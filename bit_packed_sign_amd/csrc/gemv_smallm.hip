@@ -42,6 +42,8 @@ constexpr int kWaves = 8;                            // waves per workgroup
 constexpr int kChunkGroups = 4 * kWaves;             // scale groups per K chunk (4096 k)
 constexpr int kChunkK = 128 * kChunkGroups;
 constexpr int kXRow = kChunkK + 8;                   // LDS row stride of the staged chunk (halves)
+// thread t stages and wave w reads the chunk's columns [512 w, 512 w + 512): waves never share them
+static_assert(kChunkK == 8 * 64 * kWaves, "one 512-column slice of the chunk per wave");
 constexpr int kXBytes = 16 * kXRow * 2;              // 16 token rows
 static_assert(kChunkK == 8 * 64 * kWaves && kWaves == 8, "one 16-byte load per thread per token row");
 
@@ -103,14 +105,17 @@ void gemv_smallm_kernel(const uint16_t *__restrict__ x, int M, int K, int tq, in
     const __amdgpu_buffer_rsrc_t rx = rsrc(x, (unsigned)M * (unsigned)K * 2u);
 
     // thread t's share of a chunk: 8 k of every token row; rows past M are outside the buffer
-    // range, and k past K starts from an out-of-range base, so both load zeros
+    // range, and k past K starts from an out-of-range base, so both load zeros.  Register m
+    // holds token row (m + rot) % 16: every workgroup reads the same activations, and starting
+    // each one at a different row spreads their simultaneous requests over the L2 channels.
     u4v xr[16];
+    const int rot = (int)(blockIdx.x & 15);
     auto fetch_x = [&](int c) {
         const unsigned kc = (unsigned)(c * kChunkK) + 8u * threadIdx.x;
         const unsigned base = kc < (unsigned)K ? kc * 2u : kOob;
 #pragma unroll
         for (int m = 0; m < 16; ++m)
-            xr[m] = __builtin_amdgcn_raw_buffer_load_b128(rx, base + (unsigned)m * (unsigned)K * 2u, 0, 0);
+            xr[m] = __builtin_amdgcn_raw_buffer_load_b128(rx, base + (unsigned)((m + rot) & 15) * (unsigned)K * 2u, 0, 0);
     };
     fetch_x(0);                                       // first: staging it waits on nothing else
     __builtin_amdgcn_sched_barrier(0);               // (ahead of the argument-table loads)
@@ -164,12 +169,15 @@ void gemv_smallm_kernel(const uint16_t *__restrict__ x, int M, int K, int tq, in
     for (int t = 0; t < TB; ++t) acc[t] = float4v{0.f, 0.f, 0.f, 0.f};
     // stage chunk c's x (in xr) into LDS and start loading chunk c + 1 (past K: zeros, no
     // traffic).  Staging comes last in a chunk, so its wait is for loads issued before that
-    // chunk's refills.
+    // chunk's refills.  Wave w stages columns [512 w, 512 w + 512) of every token row, and its A
+    // operands come from those same columns: no other wave reads them, and one wave's LDS
+    // accesses execute in order, so no workgroup barrier is needed (the empty asm keeps the
+    // compiler from moving LDS accesses across the hand-over).
     auto stage = [&](int c) {
 #pragma unroll
-        for (int m = 0; m < 16; ++m) *reinterpret_cast<u4v *>(xs + m * kXRow + 8 * threadIdx.x) = xr[m];
+        for (int m = 0; m < 16; ++m) *reinterpret_cast<u4v *>(xs + ((m + rot) & 15) * kXRow + 8 * threadIdx.x) = xr[m];
         if (D > 0) fetch_x(c + 1);
-        __syncthreads();
+        asm volatile("" ::: "memory");
     };
     stage(0);
     half8 A[16];
@@ -211,7 +219,7 @@ void gemv_smallm_kernel(const uint16_t *__restrict__ x, int M, int K, int tq, in
                 __builtin_amdgcn_sched_barrier(0);        // tiles one after another: bounded registers
             }
             if (D > 0) {                              // compile-time
-                __syncthreads();                      // every wave has its A of chunk c
+                asm volatile("" ::: "memory");     // this wave's A of chunk c is in registers
                 stage(c + 1);
             }
         }
