@@ -92,6 +92,19 @@ def graph_launch_floor_us(device, n, reps=20):
     return e0.elapsed_time(e1) * 1e3 / reps / n
 
 
+def stream_read_gbs(device, nbytes=2 << 30, reps=10):
+    """A reference read rate for this GPU's HBM: torch's row sums over a 2 GiB fp32 tensor in
+    8192-wide rows (reads every byte once, writes 1/8192 of it); of the plain torch reductions
+    and copies tried on this GPU it reads fastest."""
+    import torch
+    t = torch.ones(nbytes // 4, dtype=torch.float32, device=device).view(-1, 8192)
+    out = torch.empty(t.shape[0], dtype=torch.float32, device=device)
+    ms = time_fn(lambda: torch.sum(t, dim=1, out=out), reps)
+    del t
+    torch.cuda.empty_cache()
+    return nbytes / (ms * 1e-3) / 1e9
+
+
 def time_fn(fn, reps, warm=2):
     """Average ms per call of fn() over `reps` calls, HIP events on the current stream."""
     import torch
@@ -193,6 +206,21 @@ class Step:
         e1.record()
         torch.cuda.synchronize()
         return e0.elapsed_time(e1) / steps
+
+    def replay_percentiles_us(self, reps=50):
+        """p10 / p50 / p90 of single graph replays (each bracketed by its own HIP events)."""
+        import torch
+        ev = [events() for _ in range(reps)]
+        for _ in range(3):
+            self.graph.replay()
+        torch.cuda.synchronize()
+        for a, b in ev:
+            a.record()
+            self.graph.replay()
+            b.record()
+        torch.cuda.synchronize()
+        t = np.sort([a.elapsed_time(b) * 1e3 for a, b in ev])
+        return {f"p{q}": round(float(np.percentile(t, q)), 1) for q in (10, 50, 90)}
 
     def per_launch_ms(self, reps=3):
         """Per-launch kernel durations (one launch per stage) from HIP events recorded on the
@@ -489,6 +517,9 @@ def main():
     nl = len(step.stages)
     floor_us = graph_launch_floor_us(dev, nl)
     log(f"[bench] graph of {nl} dependent one-workgroup launches: {floor_us:.2f} us per launch")
+    pct = step.replay_percentiles_us()
+    read_gbs = stream_read_gbs(dev)
+    log(f"[bench] single replays {pct} us; stream read {read_gbs:.0f} GB/s")
     big = max(range(nl), key=lambda i: step.stages[i][4])
     paths = {
         "graph": {"ms_per_step": round(ms_graph, 5), "gbs": round(wbytes / ms_graph / 1e6, 1),
@@ -496,6 +527,7 @@ def main():
                   "launches": nl, "avg_launch_us_in_graph": round(ms_graph * 1e3 / nl, 3),
                   "eager_launch_sum_us": round(float(per.sum() * 1e3), 1),
                   "graph_floor_us_per_launch": round(floor_us, 3),
+                  "single_replay_us": pct,
                   "largest_launch_eager": {"stage": "lm_head 4096x151936", "bytes": step.stages[big][4],
                                            "us": round(float(per[big] * 1e3), 2),
                                            "gbs": round(step.stages[big][4] / (per[big] * 1e-3) / 1e9, 1)}},
@@ -569,6 +601,8 @@ def main():
                    "step_path": head,
                    "weight_bytes_per_step": wbytes, "global_batch": 1, "parallelism": "none (1 GPU)"},
         "pct_hbm_peak": round(100 * gbs / HBM_PEAK_GBS, 2),
+        "pct_of_stream_read": round(100 * gbs / read_gbs, 2),
+        "stream_read_gbs": round(read_gbs, 1),
         "implied_tok_s": round(1e3 / ms, 1),
         "roofline": roof,
         "cpu_baseline": cpu,
