@@ -301,17 +301,24 @@ hipError_t launch_prefill_t(const uint16_t *x, const uint32_t *W, const uint16_t
 }
 }  // namespace
 
+// Four waves of 128 x 96 on 256 x 192 tiles, one wave per SIMD: measured fastest of the 4- and
+// 8-wave layouts when the tiles fill the GPU twice over (the expansion and staging VALU work does
+// not overlap the MFMAs of a second wave).  With fewer tiles than that (M <= 1024 at N = 12288)
+// 128 x 192 tiles with two workgroups per CU keep every CU busy (M = 512: 59-63 us against
+// 81-84 us).
+static bool prefill_small_tiles(int M, int N) { return (long long)((M + 255) / 256) * ((N + 191) / 192) < 512; }
+
 hipError_t launch_prefill(const uint16_t *x, const uint32_t *W, const uint16_t *S, uint16_t *y,
                           int M, int K, int N, hipStream_t st)
 {
-    // four waves of 128 x 96, one per SIMD: measured fastest of the 4- and 8-wave layouts
-    // (the expansion and staging VALU work does not overlap the MFMAs of a second wave)
+    if (prefill_small_tiles(M, N)) return launch_prefill_t<128, 2, 2, 2, false>(x, W, S, y, M, K, N, st);
     return launch_prefill_t<256, 2, 2, 1, false>(x, W, S, y, M, K, N, st);
 }
 
 hipError_t launch_prefill_t2(const uint16_t *x, const uint32_t *T, const uint16_t *S, uint16_t *y,
                              int M, int K, int N, hipStream_t st)
 {
+    if (prefill_small_tiles(M, N)) return launch_prefill_t<128, 2, 2, 2, true>(x, T, S, y, M, K, N, st);
     return launch_prefill_t<256, 2, 2, 1, true>(x, T, S, y, M, K, N, st);
 }
 

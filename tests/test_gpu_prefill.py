@@ -42,6 +42,19 @@ def test_prefill_full_size_sampled(orc, dev):
     assert np.all(np.isfinite(y))
 
 
+@pytest.mark.parametrize("M,K,N", [(512, 4096, 12288), (2100, 256, 12300), (1030, 640, 6000)])
+def test_prefill_both_tile_shapes_sampled(orc, dev, M, K, N):
+    """256-row tiles when they fill the GPU twice over, 128-row tiles below that: a 512-token
+    prompt at full width (128-row tiles), ragged M and N on 256-row tiles (2100 x 12300: 585 of
+    them), and a ragged case between; sampled weight rows checked for every token."""
+    x, W, S = _case(5300 + M + K + N, M, K, N)
+    y = b1.gemm_prefill(*dev_tensors(dev, x, W, S)).float().cpu().numpy()
+    rows = sample_rows(synth.rng_for(0, synth.WL_TEST, 5301 + M), N, k=48, edge=16)
+    ref, nrm = orc.gemv_rows(x, W, S, rows)
+    assert norm_err(y[:, rows], ref, nrm) <= TOL
+    assert np.all(np.isfinite(y))
+
+
 def test_gemv_routes_large_m_to_prefill(orc, dev):
     M, K, N = 40, 256, 50
     x, W, S = _case(5200, M, K, N)

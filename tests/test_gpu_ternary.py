@@ -55,7 +55,7 @@ def test_ternary_other_batches_match_oracle(orc, dev, M, K, N):
     assert norm_err(b1.gemv_t2(xd, Td, Sd), ref, nrm) <= TOL
 
 
-@pytest.mark.parametrize("M,K,N", [(256, 4096, 192), (513, 1024, 777), (2048, 4096, 12288)])
+@pytest.mark.parametrize("M,K,N", [(256, 4096, 192), (513, 1024, 777), (2048, 4096, 12288), (2100, 256, 12300)])
 def test_ternary_prefill_matches_oracle(orc, dev, M, K, N):
     x, T, S = _case(13000 + M + N, M, K, N)
     xd, Td, Sd = dev_tensors(dev, x, T, S)
