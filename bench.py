@@ -105,6 +105,11 @@ def stream_read_gbs(device, nbytes=2 << 30, reps=10):
     return nbytes / (ms * 1e-3) / 1e9
 
 
+# Matrix-core work reaches its steady clock only after some milliseconds of load: the prefill
+# timings (and the dense GEMMs beside them) run this many untimed calls first (~20 ms at M = 2048).
+PREFILL_WARM = 100
+
+
 def time_fn(fn, reps, warm=2):
     """Average ms per call of fn() over `reps` calls, HIP events on the current stream."""
     import torch
@@ -436,7 +441,7 @@ def extra_ternary(dev, steps):
     T = torch.from_numpy(synth.ternary_words_fast(r, N, K).view(np.int32)).to(dev)
     S = torch.from_numpy(synth.group_scales(r, N, K)).to(dev)
     y = torch.empty((M, N), dtype=torch.float16, device=dev)
-    ms = time_fn(lambda: b1.gemm_prefill_t2(x, T, S, out=y), reps=50)
+    ms = time_fn(lambda: b1.gemm_prefill_t2(x, T, S, out=y), reps=50, warm=PREFILL_WARM)
     tf = 2.0 * M * K * N / (ms * 1e-3) / 1e12
     out["prefill"] = {"us": round(ms * 1e3, 2), "tflops": round(tf, 1),
                       "frac_of_fp16_mfma_peak": round(tf / FP16_MFMA_PEAK_TFLOPS, 4)}
@@ -453,12 +458,12 @@ def extra_prefill(dev):
     W = torch.from_numpy(synth.sign_words(r, N, K).view(np.int32)).to(dev)
     S = torch.from_numpy(synth.group_scales(r, N, K)).to(dev)
     y = torch.empty((M, N), dtype=torch.float16, device=dev)
-    ms = time_fn(lambda: b1.gemm_prefill(x, W, S, out=y), reps=50)
+    ms = time_fn(lambda: b1.gemm_prefill(x, W, S, out=y), reps=50, warm=PREFILL_WARM)
     tf = 2.0 * M * K * N / (ms * 1e-3) / 1e12
     # a 512-token prompt (the pages' pp512 point) on the same weights: the first 512 rows of x
     m5 = 512
     y5 = torch.empty((m5, N), dtype=torch.float16, device=dev)
-    ms5 = time_fn(lambda: b1.gemm_prefill(x[:m5], W, S, out=y5), reps=50)
+    ms5 = time_fn(lambda: b1.gemm_prefill(x[:m5], W, S, out=y5), reps=50, warm=4 * PREFILL_WARM)
     tf5 = 2.0 * m5 * K * N / (ms5 * 1e-3) / 1e12
     # context only: a dense fp16 GEMM of the same shape through torch (the vendor BLAS), with
     # the weights as a plain fp16 matrix (row-major [K][N] and transposed [N][K])
@@ -468,7 +473,7 @@ def extra_prefill(dev):
     bt = b.t().contiguous()
     ref = {}
     for name, fn in (("b_row_major", lambda: a @ b), ("b_transposed", lambda: a @ bt.t())):
-        rms = time_fn(fn, reps=50)
+        rms = time_fn(fn, reps=50, warm=PREFILL_WARM)
         ref[name] = {"us": round(rms * 1e3, 2), "tflops": round(2.0 * M * K * N / (rms * 1e-3) / 1e12, 1)}
     return {"workload": "prefill M=2048 K=4096 N=12288", "us": round(ms * 1e3, 2),
             "tflops": round(tf, 1), "frac_of_fp16_mfma_peak": round(tf / FP16_MFMA_PEAK_TFLOPS, 4),
