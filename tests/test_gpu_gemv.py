@@ -22,7 +22,7 @@ def _case(t, M, K, N):
 
 
 SMALL = [(128, 1), (128, 7), (256, 64), (512, 300), (1024, 1000), (4096, 1024), (12288, 130), (13440, 90),
-         (16384, 48), (17408, 33)]
+         (16384, 48), (17408, 33), (24576, 40)]
 
 
 @pytest.mark.parametrize("K,N", SMALL)
@@ -194,6 +194,25 @@ def test_gemv_group_back_to_back(orc, dev, K, Ns):
         else:                                    # long rows: the split over waves may differ
             ref, nrm = orc.gemv(x, W, S)
             assert norm_err(b, ref, nrm) <= TOL and norm_err(c, ref, nrm) <= TOL
+
+
+@pytest.mark.parametrize("M", [1, 2])
+def test_gemv_largest_row_count(orc, dev, M):
+    """The largest accepted N (2^24 - 65 rows, K = 128): row offsets near the 24-bit limit of the
+    kernels' row products, sampled rows (the last ones included) checked against the oracle."""
+    K, N = 128, (1 << 24) - 65
+    r = synth.rng_for(0, synth.WL_TEST, 7600 + M)
+    x = synth.activations(r, M, K)
+    W = r.integers(0, 1 << 32, size=(N, K // 32), dtype=np.uint32)
+    S = synth.group_scales(r, N, K)
+    xd, Wd, Sd = dev_tensors(dev, x, W, S)
+    y = b1.gemv(xd, Wd, Sd)
+    rows = sample_rows(synth.rng_for(0, synth.WL_TEST, 7601), N, k=256, edge=64)
+    ref, nrm = orc.gemv_rows(x, W, S, rows)
+    assert norm_err(y.float().cpu().numpy()[:, rows], ref, nrm) <= TOL
+    with pytest.raises(b1.Bin1Error):
+        b1.gemv(xd, torch.zeros((N + 1, K // 32), dtype=torch.int32, device=dev),
+                torch.zeros((N + 1, K // 128), dtype=torch.float16, device=dev))
 
 
 def test_gemv_repeated_calls_are_deterministic(dev):
