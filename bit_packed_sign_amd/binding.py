@@ -86,8 +86,26 @@ def _check(fn: str, status: int) -> None:
         raise Bin1Error(fn, status, detail)
 
 
+# the current stream of a device as a raw handle (torch's own accessor when it has one: no
+# Stream object is built per call)
+_raw_stream = getattr(torch._C, "_cuda_getCurrentRawStream", None)
+
+
 def _stream(t: torch.Tensor) -> int:
+    if _raw_stream is not None:
+        return _raw_stream(t.get_device())
     return torch.cuda.current_stream(t.device).cuda_stream
+
+
+def _call(fn: str, device: int, *args) -> None:
+    """Call `fn` of the library with `device` current (switching only when it is not already)."""
+    f = getattr(_lib if _lib is not None else lib(), fn)
+    if torch.cuda.current_device() == device:
+        status = f(*args)
+    else:
+        with torch.cuda.device(device):
+            status = f(*args)
+    _check(fn, status)
 
 
 def _need(t: torch.Tensor, name: str, dtypes, ndim: int):
@@ -120,9 +138,8 @@ def _product(fn: str, x, Wbits, scales, out, per_word: int = 32):
         _need(out, "out", (torch.float16,), 2)
         if tuple(out.shape) != (M, N):
             raise ValueError("out has the wrong shape")
-    with torch.cuda.device(x.device):
-        _check(fn, getattr(lib(), fn)(x.data_ptr(), Wbits.data_ptr(), scales.data_ptr(), out.data_ptr(),
-                                      M, K, N, _stream(x)))
+    _call(fn, x.get_device(), x.data_ptr(), Wbits.data_ptr(), scales.data_ptr(), out.data_ptr(), M, K, N,
+          _stream(x))
     return out
 
 
@@ -170,8 +187,7 @@ def gemv_group(x: torch.Tensor, Wbits: Sequence[torch.Tensor], scales: Sequence[
     sp = arr_p(*[S.data_ptr() for S in scales])
     yp = arr_p(*[o.data_ptr() for o in outs])
     npv = (ctypes.c_int * count)(*Ns)
-    with torch.cuda.device(x.device):
-        _check(_fn, getattr(lib(), _fn)(x.data_ptr(), count, wp, sp, yp, npv, M, K, _stream(x)))
+    _call(_fn, x.get_device(), x.data_ptr(), count, wp, sp, yp, npv, M, K, _stream(x))
     return list(outs)
 
 
@@ -201,9 +217,8 @@ def gemv_pm1(Abits: torch.Tensor, Wbits: torch.Tensor, out: Optional[torch.Tenso
         _need(out, "out", (torch.int32,), 2)
         if tuple(out.shape) != (M, N):
             raise ValueError("out has the wrong shape")
-    with torch.cuda.device(Abits.device):
-        _check("bin1_gemv_pm1", lib().bin1_gemv_pm1(Abits.data_ptr(), Wbits.data_ptr(), out.data_ptr(),
-                                                     M, K, N, _stream(Abits)))
+    _call("bin1_gemv_pm1", Abits.get_device(), Abits.data_ptr(), Wbits.data_ptr(), out.data_ptr(), M, K, N,
+          _stream(Abits))
     return out
 
 
