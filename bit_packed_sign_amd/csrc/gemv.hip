@@ -76,13 +76,9 @@ hipError_t launch_gemv(const uint16_t *x, const uint32_t *W, const uint16_t *S, 
         set.count = 1;
         return launch_gemv_smallm(x, set, M, K, st);
     }
+    // M == 1 with K past the block-scaled kernel's register budget: select/accumulate
     dim3 grid((N + 3) / 4), block(256);
-    if (M == 1)
-        hipLaunchKernelGGL(gemv_select_kernel<1>, grid, block, 0, st, x, W, S, y, M, K, N);
-    else if (M <= 4)
-        hipLaunchKernelGGL(gemv_select_kernel<4>, grid, block, 0, st, x, W, S, y, M, K, N);
-    else
-        hipLaunchKernelGGL(gemv_select_kernel<8>, grid, block, 0, st, x, W, S, y, M, K, N);
+    hipLaunchKernelGGL(gemv_select_kernel<1>, grid, block, 0, st, x, W, S, y, M, K, N);
     return hipGetLastError();
 }
 
