@@ -30,6 +30,8 @@
 //    converts and contracts at most half as many pairs.
 //  * Segment sigma (two per pair p, h = sigma % 2) is what one chain of four MFMAs covers:
 //    MFMA K-block G of segment sigma is scale group gamma = 8p + 2G + h.
+#include <algorithm>
+
 #include "common.hpp"
 #include "kernels.hpp"
 #include "mx_common.hpp"
@@ -357,9 +359,10 @@ done:
                                       (unsigned)__shfl((unsigned)tab.y, it, kWave);
         const float4v pr4 = *reinterpret_cast<const float4v *>(red + e * NW);
         float tot = (pr4[0] + pr4[1]) + (pr4[2] + pr4[3]);
-        if constexpr (NW == 8) {
-            const float4v pr8 = *reinterpret_cast<const float4v *>(red + e * NW + 4);
-            tot += (pr8[0] + pr8[1]) + (pr8[2] + pr8[3]);
+#pragma unroll
+        for (int v = 4; v < NW; v += 4) {             // waves 4.. of a wider workgroup
+            const float4v prv = *reinterpret_cast<const float4v *>(red + e * NW + v);
+            tot += (prv[0] + prv[1]) + (prv[2] + prv[3]);
         }
         if (row < N) reinterpret_cast<uint16_t *>(yp)[row] = f2h_rne(tot);
     }
@@ -367,6 +370,7 @@ done:
 
 constexpr int kMaxPairs = 20;                         // K <= 20480 (A operands fit in registers)
 constexpr int kMaxTileRows = 2048;                     // rows per workgroup held in the merge table
+constexpr size_t kMaxLds = 160 * 1024;                 // LDS per workgroup on gfx950
 // LDS: limb blocks and exponents for K, then the merge table [tile][16R rows][NW waves] fp32.
 constexpr size_t shm_bytes(int K, int rows_per_wg, int NW)
 {
@@ -378,7 +382,8 @@ hipError_t launch_mx_t(const uint16_t *x, const MxSet &set0, int K, hipStream_t 
 {
     static const hipError_t attr = hipFuncSetAttribute(
         reinterpret_cast<const void *>(&gemv_mx_kernel<SP, P, R, ODD, T2, NW, TWO>),
-        hipFuncAttributeMaxDynamicSharedMemorySize, (int)shm_bytes(kMaxPairs * 1024, kMaxTileRows, NW));
+        hipFuncAttributeMaxDynamicSharedMemorySize,
+        (int)std::min<size_t>(shm_bytes(kMaxPairs * 1024, kMaxTileRows, NW), kMaxLds));
     if (attr != hipSuccess) return attr;
     MxSet set = set0;
     int tiles = 0;
@@ -389,7 +394,7 @@ hipError_t launch_mx_t(const uint16_t *x, const MxSet &set0, int K, hipStream_t 
     // Resident workgroups per CU follow the register budget (A operands dominate it: three
     // fit at one pair per wave, two at two); the grid grows past that only when a workgroup's
     // rows would overflow the merge table.
-    const int cap = NW != 4 ? 256 : SP == 1 ? 3 * 256 : SP == 2 ? 2 * 256 : 256;
+    const int cap = NW == 4 ? (SP == 1 ? 3 * 256 : SP == 2 ? 2 * 256 : 256) : (NW == 8 && SP == 1 ? 2 * 256 : 256);
     // tiles per workgroup: at most what the merge table holds and the one-per-lane tile table
     constexpr int kMaxT = kMaxTileRows / (16 * R) < 64 ? kMaxTileRows / (16 * R) : 64;
     const int need = (tiles + kMaxT - 1) / kMaxT;
@@ -432,15 +437,16 @@ hipError_t dispatch_mx(const uint16_t *x, const MxSet &set, int K, hipStream_t s
     case 1: return one16 ? launch_mx<1, 1, 1, ODD, T2>(x, set, K, st)
                  : one   ? launch_mx<1, 1, 2, ODD, T2>(x, set, K, st)
                  : few16 ? launch_mx<1, 3, 1, ODD, T2>(x, set, K, st) : launch_mx<1, 2, 2, ODD, T2>(x, set, K, st);
-    case 2: return one16 ? launch_mx<2, 1, 1, ODD, T2>(x, set, K, st)
+    // One 16-row tile per workgroup: as many waves as pairs (up to 16), one pair each, so no wave
+    // carries a second pair on the critical path (the wider workgroups fit fewer per CU).
+    case 2: return one16 ? launch_mx<1, 1, 1, ODD, T2, 8>(x, set, K, st)
                  : one   ? launch_mx<2, 1, 2, ODD, T2>(x, set, K, st)
                  : few16 ? launch_mx<2, 2, 1, ODD, T2>(x, set, K, st) : launch_mx<2, 2, 2, ODD, T2>(x, set, K, st);
-    // long rows with one 16-row tile per workgroup: 8 waves, at most ceil(pairs / 8) pairs each
-    case 3: return one16 ? launch_mx<2, 1, 1, ODD, T2, 8>(x, set, K, st)
+    case 3: return one16 ? launch_mx<1, 1, 1, ODD, T2, 12>(x, set, K, st)
                  : one   ? launch_mx<3, 1, 2, ODD, T2>(x, set, K, st) : launch_mx<3, 2, 2, ODD, T2>(x, set, K, st);
     // (ternary rows are twice as many bytes: 16-row tiles keep the ring in registers)
     case 4:
-        if (one16) return launch_mx<2, 1, 1, ODD, T2, 8>(x, set, K, st);
+        if (one16) return launch_mx<1, 1, 1, ODD, T2, 16>(x, set, K, st);
         if constexpr (T2) return launch_mx<4, 1, 1, ODD, T2>(x, set, K, st);
         else return launch_mx<4, 1, 2, ODD, T2>(x, set, K, st);
     default:
