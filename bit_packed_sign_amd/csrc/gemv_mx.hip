@@ -25,9 +25,9 @@
 //  * Weights are streamed with nontemporal buffer loads, several row tiles ahead per wave.
 //    A lane owns two adjacent scale groups (32 contiguous bytes of its row and one dword of
 //    scales), so each wave reads whole 128-byte lines; the 4 waves of a workgroup split K
-//    in 1024-weight "pairs" (8 groups) and combine their partial rows in LDS.  Long rows
-//    (K > 8192, one tile per workgroup) use 8 waves instead, two per SIMD: each wave then
-//    converts and contracts at most half as many pairs.
+//    in 1024-weight "pairs" (8 groups) and combine their partial rows in LDS.  Longer rows
+//    with one tile per workgroup (4096 < K <= 16384) use one wave per pair instead (8, 12 or
+//    16 waves, two to four per SIMD), so no wave converts or contracts a second pair.
 //  * Segment sigma (two per pair p, h = sigma % 2) is what one chain of four MFMAs covers:
 //    MFMA K-block G of segment sigma is scale group gamma = 8p + 2G + h.
 #include <algorithm>
