@@ -348,7 +348,7 @@ def extra_single(dev):
     ms_cold = time_fn(cold, reps=copies)
     ms_hot = time_fn(lambda: b1.gemv(x, W0, S0, out=y), reps=200)
     rows = torch.from_numpy(synth.patch_rows_single()).to(dev)
-    ms_patch = time_fn(lambda: b1.xor_patch_apply(W0, rows, check_distinct=False), reps=200)
+    ms_patch = time_fn(lambda: b1.xor_patch_apply(W0, rows), reps=200)
     del Ws, Ss
     return {"workload": "4096x4096 GEMV, M=1", "pool_copies": copies,
             "us_cold": round(ms_cold * 1e3, 2), "gbs_cold": round(g.weight_bytes / ms_cold / 1e6, 1),
@@ -385,7 +385,7 @@ def extra_patch27b(st, dev):
     table = b1.PatchTable(mlp)
     ent_np = synth.patch_entries_27b()
     ent = torch.from_numpy(ent_np).to(dev)
-    ms = time_fn(lambda: b1.xor_patch_apply_multi(table, ent, check_distinct=False), reps=200)
+    ms = time_fn(lambda: b1.xor_patch_apply_multi(table, ent), reps=200)
     row_bytes = np.array([m.shape[1] * 4 for m in mlp])[ent_np[:, 0]].sum()
     return {"patch_2000_rows_us": round(ms * 1e3, 2), "patch_bytes_read_and_written": int(2 * row_bytes)}
 

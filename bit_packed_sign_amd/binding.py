@@ -12,6 +12,7 @@ import os
 import threading
 from typing import Optional, Sequence
 
+import numpy as np
 import torch
 
 HERE = os.path.dirname(os.path.abspath(__file__))
@@ -40,6 +41,8 @@ _SIGS = {
     "bin1_chain_prepare": [_p, _i, _p, ctypes.c_size_t, _p],
     "bin1_gemv_chain": [_p, _p],
     "bin1_chain_status": [_p, _p, _p],
+    "bin1_stream_read": [_p, ctypes.c_size_t, _p, _i, _i, _p],
+    "bin1_kernel_variant": [_i, _i, _i, _i, _p, _p, _i],
     "bin1_status_string": [_i],
     "bin1_last_error": [],
     "bin1_abi_version": [],
@@ -223,10 +226,12 @@ def gemv_pm1(Abits: torch.Tensor, Wbits: torch.Tensor, out: Optional[torch.Tenso
 
 
 def xor_patch_apply(Wbits: torch.Tensor, rows: torch.Tensor, bad_rows: Optional[torch.Tensor] = None,
-                    check_distinct: bool = True) -> None:
+                    check_distinct: bool = False) -> None:
     """Flip (in place) every sign of the listed output rows of Wbits [N][K/32]; calling it again
-    with the same rows removes the patch.  ``rows``: device int32 [nrows], distinct.  Rows out of
-    range are skipped and counted into ``bad_rows`` (device int32 [1]) when given."""
+    with the same rows removes the patch.  ``rows``: device int32 [nrows]; a row listed twice is
+    flipped twice, i.e. unchanged.  Rows out of range are skipped and counted into ``bad_rows``
+    (device int32 [1]) when given.  ``check_distinct=True`` rejects repeated rows first; that check
+    reads the list back to the host (a synchronisation, so not inside graph capture)."""
     _need(Wbits, "Wbits", _BITS, 2)
     _need(rows, "rows", (torch.int32,), 1)
     if check_distinct and rows.numel() and torch.unique(rows).numel() != rows.numel():
@@ -263,8 +268,10 @@ class PatchTable:
 
 
 def xor_patch_apply_multi(table: PatchTable, entries: torch.Tensor, bad_rows: Optional[torch.Tensor] = None,
-                          check_distinct: bool = True) -> None:
-    """Patch many matrices in one launch.  ``entries``: device int32 [n][2] of (matrix id, row)."""
+                          check_distinct: bool = False) -> None:
+    """Patch many matrices in one launch.  ``entries``: device int32 [n][2] of (matrix id, row);
+    repeated entries commute as in :func:`xor_patch_apply` (``check_distinct=True`` rejects them,
+    with a host synchronisation)."""
     _need(entries, "entries", (torch.int32,), 2)
     if entries.shape[1] != 2:
         raise ValueError("entries must be [n][2]")
@@ -375,3 +382,32 @@ class ChainPlan:
             _check("bin1_chain_status", lib().bin1_chain_status(ctypes.byref(self.plan), ctypes.byref(runs),
                                                                   ctypes.byref(err)))
         return runs.value, err.value
+
+
+def stream_read(buf: torch.Tensor, sink: Optional[torch.Tensor] = None, grid: int = 2048, unroll: int = 8):
+    """Read every byte of the device tensor ``buf`` once (a measurement of the HBM read rate; no
+    arithmetic of the method).  Returns the per-wave digest tensor (uint32 viewed as int32 [4 * grid])."""
+    if not isinstance(buf, torch.Tensor) or not buf.is_cuda or not buf.is_contiguous():
+        raise ValueError("buf must be a contiguous device tensor")
+    if sink is None:
+        sink = torch.empty(4 * grid, dtype=torch.int32, device=buf.device)
+    _need(sink, "sink", (torch.int32,), 1)
+    if sink.numel() < 4 * grid:
+        raise ValueError("sink needs 4 * grid entries")
+    nbytes = buf.numel() * buf.element_size()
+    _call("bin1_stream_read", buf.get_device(), buf.data_ptr(), nbytes, sink.data_ptr(), grid, unroll, _stream(buf))
+    return sink
+
+
+_VARIANT_OPS = {"gemv": 0, "gemv_t2": 1, "prefill": 2, "prefill_t2": 3}
+
+
+def kernel_variant(op: str, M: int, K: int, N) -> str:
+    """The kernel variant(s) and grid a product call would launch (no GPU needed).  ``op``: "gemv"
+    (bin1_gemv / bin1_gemv_group), "gemv_t2", "prefill" or "prefill_t2"; ``N``: an int or the list
+    of row counts of a group call, as it would launch them."""
+    Ns = [int(N)] if isinstance(N, (int, np.integer)) else [int(n) for n in N]
+    buf = ctypes.create_string_buffer(1024)
+    arr = (ctypes.c_int * len(Ns))(*Ns)
+    _check("bin1_kernel_variant", lib().bin1_kernel_variant(_VARIANT_OPS[op], M, K, len(Ns), arr, buf, len(buf)))
+    return buf.value.decode()

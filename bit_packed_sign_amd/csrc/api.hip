@@ -7,6 +7,7 @@
 #include <cstdio>
 #include <cstring>
 #include <string>
+#include <utility>
 #include <vector>
 
 #include "bin1.h"
@@ -43,8 +44,25 @@ bool overlap(const void *a, size_t na, const void *b, size_t nb)
 }
 
 // The pointer must be device memory (or managed memory) visible on the current device.
+// Allocation ranges that passed are remembered per thread (a few of them, most recent first):
+// a later pointer inside one of them, on the same device, is accepted without a new runtime query.
+struct Validated {
+    uintptr_t base, end;
+    int device;
+};
+thread_local Validated g_valid[16];
+thread_local int g_nvalid = 0;
+
 int check_device(const void *p, const char *name)
 {
+    int dev = -1;
+    if (hipGetDevice(&dev) != hipSuccess) return fail(BIN1_ERR_DEVICE, "%s: no current HIP device", name);
+    const uintptr_t a = reinterpret_cast<uintptr_t>(p);
+    for (int i = 0; i < g_nvalid; ++i)
+        if (g_valid[i].device == dev && a >= g_valid[i].base && a < g_valid[i].end) {
+            if (i > 0) std::swap(g_valid[i], g_valid[0]);
+            return BIN1_OK;
+        }
     hipPointerAttribute_t attr;
     hipError_t e = hipPointerGetAttributes(&attr, p);
     if (e != hipSuccess) {
@@ -53,10 +71,18 @@ int check_device(const void *p, const char *name)
     }
     if (attr.type != hipMemoryTypeDevice && attr.type != hipMemoryTypeManaged)
         return fail(BIN1_ERR_DEVICE, "%s: not device memory (memory type %d)", name, (int)attr.type);
-    int dev = -1;
-    if (hipGetDevice(&dev) != hipSuccess || attr.device != dev)
+    if (attr.device != dev)
         return fail(BIN1_ERR_DEVICE, "%s: allocated on device %d, current device is %d", name,
                     attr.device, dev);
+    hipDeviceptr_t base = nullptr;
+    size_t size = 0;
+    if (hipMemGetAddressRange(&base, &size, const_cast<void *>(p)) == hipSuccess && size > 0) {
+        const int slot = g_nvalid < 16 ? g_nvalid++ : 15;
+        for (int i = slot; i > 0; --i) g_valid[i] = g_valid[i - 1];
+        g_valid[0] = Validated{reinterpret_cast<uintptr_t>(base), reinterpret_cast<uintptr_t>(base) + size, dev};
+    } else {
+        (void)hipGetLastError();
+    }
     return BIN1_OK;
 }
 
@@ -279,6 +305,72 @@ int bin1_gemv(const void *x, const uint32_t *Wbits, const void *scales, void *y,
 
 namespace {
 
+// Launches of the same-input products of 1..4 matrices (validated, back-to-back ones already merged);
+// with `desc`, describes them instead (the variant query).  t2: ternary weights in 2-bit slots.
+hipError_t route_group(bool t2, const void *x, int count, const uint32_t *const *Wbits, const void *const *scales,
+                       void *const *y, const int *N, int M, int K, hipStream_t st, std::string *desc)
+{
+    if (M == 1 && K <= bin1::mx_max_k()) {
+        bin1::MxSet set{};
+        int tiles = 0;
+        for (int i = 0; i < count; ++i) {
+            set.W[i] = Wbits[i];
+            set.S[i] = static_cast<const uint16_t *>(scales[i]);
+            set.y[i] = static_cast<uint16_t *>(y[i]);
+            set.N[i] = N[i];
+            tiles += (N[i] + 15) / 16;
+            set.tile_end[i] = tiles;
+        }
+        set.count = count;
+        return t2 ? bin1::launch_gemv_mx_t2(static_cast<const uint16_t *>(x), set, K, st, desc)
+                  : bin1::launch_gemv_mx(static_cast<const uint16_t *>(x), set, K, st, desc);
+    }
+    if (t2) {                                             // other batch sizes: the prefill kernel
+        for (int i = 0; i < count; ++i) {
+            hipError_t e = bin1::launch_prefill_t2(static_cast<const uint16_t *>(x), Wbits[i],
+                                                   static_cast<const uint16_t *>(scales[i]),
+                                                   static_cast<uint16_t *>(y[i]), M, K, N[i], st, desc);
+            if (e != hipSuccess) return e;
+        }
+        return hipSuccess;
+    }
+    if (M >= 2 && M <= 16) {                              // small batch: one launch as well
+        bin1::MxSet set{};
+        for (int i = 0; i < count; ++i) {
+            set.W[i] = Wbits[i];
+            set.S[i] = static_cast<const uint16_t *>(scales[i]);
+            set.y[i] = static_cast<uint16_t *>(y[i]);
+            set.N[i] = N[i];
+        }
+        set.count = count;
+        return bin1::launch_gemv_smallm(static_cast<const uint16_t *>(x), set, M, K, st, desc);
+    }
+    for (int i = 0; i < count; ++i) {
+        hipError_t e = bin1::launch_gemv(static_cast<const uint16_t *>(x), Wbits[i],
+                                         static_cast<const uint16_t *>(scales[i]),
+                                         static_cast<uint16_t *>(y[i]), M, K, N[i], st, desc);
+        if (e != hipSuccess) return e;
+    }
+    return hipSuccess;
+}
+
+// Ternary product of one matrix: M == 1 on the block-scaled decode kernel, other M on the prefill kernel.
+hipError_t route_t2(const void *x, const uint32_t *Tbits, const void *scales, void *y, int M, int K, int N,
+                    hipStream_t s, std::string *desc)
+{
+    if (M == 1 && K <= bin1::mx_max_k()) {
+        bin1::MxSet set{};
+        set.W[0] = Tbits;
+        set.S[0] = static_cast<const uint16_t *>(scales);
+        set.y[0] = static_cast<uint16_t *>(y);
+        set.N[0] = N;
+        set.count = 1;
+        return bin1::launch_gemv_mx_t2(static_cast<const uint16_t *>(x), set, K, s, desc);
+    }
+    return bin1::launch_prefill_t2(static_cast<const uint16_t *>(x), Tbits, static_cast<const uint16_t *>(scales),
+                                   static_cast<uint16_t *>(y), M, K, N, s, desc);
+}
+
 // Same-input products of 1..4 matrices; t2: ternary weights in 2-bit slots.
 int gemv_group_impl(const char *fn, bool t2, const void *x, int count, const uint32_t *const *Wbits,
                     const void *const *scales, void *const *y, const int *N, int M, int K, void *stream)
@@ -288,14 +380,31 @@ int gemv_group_impl(const char *fn, bool t2, const void *x, int count, const uin
         return fail(BIN1_ERR_SHAPE, "count must be 1..%d (got %d)", bin1::kMaxMats, count);
     if (!Wbits || !scales || !y || !N) return fail(BIN1_ERR_NULL, "pointer arrays must be non-NULL");
     // products with no outputs (M == 0 or N[i] == 0) are dropped; the rest go ahead
+    int live[bin1::kMaxMats], nlive = 0;
+    for (int i = 0; i < count; ++i) {
+        const int st = check_product_host(x, Wbits[i], scales[i], y[i], M, K, N[i], bits);
+        if (st < 0) return st;
+        if (st != kEmpty) live[nlive++] = i;
+    }
+    if (nlive == 0) return ok();
+    // every output against every other product's inputs and output, on the caller's list (before
+    // any merge below, so that an output touching a neighbour's weights is still caught)
+    for (int a = 0; a < nlive; ++a)
+        for (int b = 0; b < nlive; ++b) {
+            const int i = live[a], j = live[b];
+            if (i == j) continue;
+            const size_t yb = (size_t)M * N[i] * 2;
+            if (overlap(y[i], yb, y[j], (size_t)M * N[j] * 2) ||
+                overlap(y[i], yb, Wbits[j], (size_t)N[j] * (K / 8) * bits) ||
+                overlap(y[i], yb, scales[j], (size_t)N[j] * (K / 128) * 2))
+                return fail(BIN1_ERR_ALIAS, "y[%d] overlaps an input or output of matrix %d", i, j);
+        }
     const uint32_t *Wk[bin1::kMaxMats];
     const void *Sk[bin1::kMaxMats];
     void *yk[bin1::kMaxMats];
     int Nk[bin1::kMaxMats], kept = 0;
-    for (int i = 0; i < count; ++i) {
-        const int st = check_product_host(x, Wbits[i], scales[i], y[i], M, K, N[i], bits);
-        if (st < 0) return st;
-        if (st == kEmpty) continue;
+    for (int a = 0; a < nlive; ++a) {
+        const int i = live[a];
         // At M == 1, a matrix stored right after the previous kept one (its weights, scales and
         // outputs each start where the previous one's end, as in a fused q/k/v layout) extends
         // that one: rows are independent, so the taller matrix gives the same products.
@@ -315,70 +424,13 @@ int gemv_group_impl(const char *fn, bool t2, const void *x, int count, const uin
         yk[kept] = y[i];
         Nk[kept++] = N[i];
     }
-    if (kept == 0) return ok();
-    count = kept;
-    Wbits = Wk;
-    scales = Sk;
-    y = yk;
-    N = Nk;
-    for (int i = 0; i < count; ++i) {
-        for (int j = 0; j < count; ++j) {
-            if (j == i) continue;
-            const size_t yb = (size_t)M * N[i] * 2;
-            if (overlap(y[i], yb, y[j], (size_t)M * N[j] * 2) ||
-                overlap(y[i], yb, Wbits[j], (size_t)N[j] * (K / 8) * bits) ||
-                overlap(y[i], yb, scales[j], (size_t)N[j] * (K / 128) * 2))
-                return fail(BIN1_ERR_ALIAS, "y[%d] overlaps an input or output of matrix %d", i, j);
-        }
-    }
-    for (int i = 0; i < count; ++i) {
-        int st = check_product_device(x, Wbits[i], scales[i], y[i]);
-        if (st) return st;
-    }
-    const hipStream_t st = static_cast<hipStream_t>(stream);
-    if (M == 1 && K <= bin1::mx_max_k()) {
-        bin1::MxSet set{};
-        int tiles = 0;
-        for (int i = 0; i < count; ++i) {
-            set.W[i] = Wbits[i];
-            set.S[i] = static_cast<const uint16_t *>(scales[i]);
-            set.y[i] = static_cast<uint16_t *>(y[i]);
-            set.N[i] = N[i];
-            tiles += (N[i] + 15) / 16;
-            set.tile_end[i] = tiles;
-        }
-        set.count = count;
-        return launched(t2 ? bin1::launch_gemv_mx_t2(static_cast<const uint16_t *>(x), set, K, st)
-                           : bin1::launch_gemv_mx(static_cast<const uint16_t *>(x), set, K, st),
-                        fn);
-    }
-    if (t2) {                                             // other batch sizes: the prefill kernel
-        for (int i = 0; i < count; ++i) {
-            hipError_t e = bin1::launch_prefill_t2(static_cast<const uint16_t *>(x), Wbits[i],
-                                                   static_cast<const uint16_t *>(scales[i]),
-                                                   static_cast<uint16_t *>(y[i]), M, K, N[i], st);
-            if (e != hipSuccess) return launched(e, fn);
-        }
-        return ok();
-    }
-    if (M >= 2 && M <= 16) {                              // small batch: one launch as well
-        bin1::MxSet set{};
-        for (int i = 0; i < count; ++i) {
-            set.W[i] = Wbits[i];
-            set.S[i] = static_cast<const uint16_t *>(scales[i]);
-            set.y[i] = static_cast<uint16_t *>(y[i]);
-            set.N[i] = N[i];
-        }
-        set.count = count;
-        return launched(bin1::launch_gemv_smallm(static_cast<const uint16_t *>(x), set, M, K, st), fn);
-    }
-    for (int i = 0; i < count; ++i) {
-        hipError_t e = bin1::launch_gemv(static_cast<const uint16_t *>(x), Wbits[i],
-                                         static_cast<const uint16_t *>(scales[i]),
-                                         static_cast<uint16_t *>(y[i]), M, K, N[i], st);
-        if (e != hipSuccess) return launched(e, fn);
-    }
-    return ok();
+    int st;
+    if ((st = check_device(x, "x"))) return st;
+    for (int i = 0; i < kept; ++i)
+        if ((st = check_device(Wk[i], "Wbits")) || (st = check_device(Sk[i], "scales")) ||
+            (st = check_device(yk[i], "y")))
+            return st;
+    return launched(route_group(t2, x, kept, Wk, Sk, yk, Nk, M, K, static_cast<hipStream_t>(stream), nullptr), fn);
 }
 
 }  // namespace
@@ -522,19 +574,7 @@ int bin1_gemv_t2(const void *x, const uint32_t *Tbits, const void *scales, void 
 {
     int st = check_product(x, Tbits, scales, y, M, K, N, 2);
     if (st) return st == kEmpty ? ok() : st;
-    const hipStream_t s = static_cast<hipStream_t>(stream);
-    if (M == 1 && K <= bin1::mx_max_k()) {
-        bin1::MxSet set{};
-        set.W[0] = Tbits;
-        set.S[0] = static_cast<const uint16_t *>(scales);
-        set.y[0] = static_cast<uint16_t *>(y);
-        set.N[0] = N;
-        set.count = 1;
-        return launched(bin1::launch_gemv_mx_t2(static_cast<const uint16_t *>(x), set, K, s), "bin1_gemv_t2");
-    }
-    return launched(bin1::launch_prefill_t2(static_cast<const uint16_t *>(x), Tbits,
-                                            static_cast<const uint16_t *>(scales), static_cast<uint16_t *>(y),
-                                            M, K, N, s),
+    return launched(route_t2(x, Tbits, scales, y, M, K, N, static_cast<hipStream_t>(stream), nullptr),
                     "bin1_gemv_t2");
 }
 
@@ -547,6 +587,70 @@ int bin1_gemm_prefill_t2(const void *x, const uint32_t *Tbits, const void *scale
                                             static_cast<const uint16_t *>(scales), static_cast<uint16_t *>(y),
                                             M, K, N, static_cast<hipStream_t>(stream)),
                     "bin1_gemm_prefill_t2");
+}
+
+int bin1_stream_read(const void *buf, size_t bytes, uint32_t *sink, int grid, int unroll, void *stream)
+{
+    if (bytes == 0 || bytes % 16 != 0 || grid < 1 || grid > 65536 || (unroll != 4 && unroll != 8 && unroll != 16))
+        return fail(BIN1_ERR_SHAPE, "need bytes a positive multiple of 16, 1 <= grid <= 65536, unroll 4, 8 or 16 "
+                    "(got %zu, %d, %d)", bytes, grid, unroll);
+    if (!buf || !sink) return fail(BIN1_ERR_NULL, "buf and sink must be non-NULL");
+    if (!aligned16(buf) || reinterpret_cast<uintptr_t>(sink) & 3u)
+        return fail(BIN1_ERR_ALIGN, "buf must be 16-byte aligned and sink 4-byte aligned");
+    if (overlap(sink, (size_t)grid * 16, buf, bytes)) return fail(BIN1_ERR_ALIAS, "sink overlaps buf");
+    int st;
+    if ((st = check_device(buf, "buf")) || (st = check_device(sink, "sink"))) return st;
+    return launched(bin1::launch_stream_read(buf, bytes, sink, grid, unroll, static_cast<hipStream_t>(stream)),
+                    "bin1_stream_read");
+}
+
+int bin1_kernel_variant(int op, int M, int K, int count, const int *N, char *name, int len)
+{
+    if (!N || !name) return fail(BIN1_ERR_NULL, "N and name must be non-NULL");
+    if (len < 1) return fail(BIN1_ERR_SHAPE, "len must be >= 1");
+    name[0] = 0;
+    if (op < 0 || op > 3 || count < 1 || count > bin1::kMaxMats || (op >= 2 && count != 1))
+        return fail(BIN1_ERR_SHAPE, "need op 0..3 and count 1..%d (1 for the prefill calls)", bin1::kMaxMats);
+    if (M < 1 || K < 128 || K % 128 != 0)
+        return fail(BIN1_ERR_SHAPE, "need M >= 1, K >= 128, K %% 128 == 0 (got M=%d K=%d)", M, K);
+    for (int i = 0; i < count; ++i)
+        if (N[i] < 1 || N[i] >= (1 << 24) - 64) return fail(BIN1_ERR_SHAPE, "N[%d] out of range (%d)", i, N[i]);
+    // Stand-in addresses, never dereferenced (nothing is launched): distinct, aligned, and not back
+    // to back, as the caller's matrices after any merge.
+    const uint32_t *W[bin1::kMaxMats];
+    const void *S[bin1::kMaxMats];
+    void *Y[bin1::kMaxMats];
+    for (int i = 0; i < bin1::kMaxMats; ++i) {
+        W[i] = reinterpret_cast<const uint32_t *>((uintptr_t)(0x100000000ull * (1 + i)));
+        S[i] = reinterpret_cast<const void *>((uintptr_t)(0x100000000ull * (5 + i)));
+        Y[i] = reinterpret_cast<void *>((uintptr_t)(0x100000000ull * (9 + i)));
+    }
+    const void *X = reinterpret_cast<const void *>((uintptr_t)0x1000000000ull);
+    std::string desc;
+    hipError_t e = hipSuccess;
+    switch (op) {
+    case 0:
+        e = count == 1 ? bin1::launch_gemv(static_cast<const uint16_t *>(X), W[0], static_cast<const uint16_t *>(S[0]),
+                                           static_cast<uint16_t *>(Y[0]), M, K, N[0], nullptr, &desc)
+                       : route_group(false, X, count, W, S, Y, N, M, K, nullptr, &desc);
+        break;
+    case 1:
+        e = count == 1 ? route_t2(X, W[0], S[0], Y[0], M, K, N[0], nullptr, &desc)
+                       : route_group(true, X, count, W, S, Y, N, M, K, nullptr, &desc);
+        break;
+    case 2:
+        e = bin1::launch_prefill(static_cast<const uint16_t *>(X), W[0], static_cast<const uint16_t *>(S[0]),
+                                 static_cast<uint16_t *>(Y[0]), M, K, N[0], nullptr, &desc);
+        break;
+    default:
+        e = bin1::launch_prefill_t2(static_cast<const uint16_t *>(X), W[0], static_cast<const uint16_t *>(S[0]),
+                                    static_cast<uint16_t *>(Y[0]), M, K, N[0], nullptr, &desc);
+        break;
+    }
+    if (e != hipSuccess) return fail(BIN1_ERR_LAUNCH, "bin1_kernel_variant: %s", hipGetErrorString(e));
+    if ((int)desc.size() >= len) return fail(BIN1_ERR_SHAPE, "name buffer too small: need %zu bytes", desc.size() + 1);
+    memcpy(name, desc.c_str(), desc.size() + 1);
+    return ok();
 }
 
 }  // extern "C"

@@ -5,6 +5,8 @@
 // by select/accumulate (no multiplies) and the group scale is applied once per 32-weight
 // word partial sum; accumulation is fp32 ["Bonsai 27B" page, section "Low-bit kernels
 // for hybrid attention"].
+#include <string>
+
 #include "common.hpp"
 #include "kernels.hpp"
 
@@ -60,24 +62,28 @@ __global__ __launch_bounds__(256) void gemv_select_kernel(
 }
 
 hipError_t launch_gemv(const uint16_t *x, const uint32_t *W, const uint16_t *S, uint16_t *y,
-                       int M, int K, int N, hipStream_t st)
+                       int M, int K, int N, hipStream_t st, std::string *desc)
 {
-    if (M > 16) return launch_prefill(x, W, S, y, M, K, N, st);
+    if (M > 16) return launch_prefill(x, W, S, y, M, K, N, st, desc);
     if (M == 1 && K <= mx_max_k()) {
         MxSet set{};
         set.W[0] = W; set.S[0] = S; set.y[0] = y; set.N[0] = N;
         set.tile_end[0] = (N + 15) / 16;
         set.count = 1;
-        return launch_gemv_mx(x, set, K, st);
+        return launch_gemv_mx(x, set, K, st, desc);
     }
     if (M >= 2) {
         MxSet set{};
         set.W[0] = W; set.S[0] = S; set.y[0] = y; set.N[0] = N;
         set.count = 1;
-        return launch_gemv_smallm(x, set, M, K, st);
+        return launch_gemv_smallm(x, set, M, K, st, desc);
     }
     // M == 1 with K past the block-scaled kernel's register budget: select/accumulate
     dim3 grid((N + 3) / 4), block(256);
+    if (desc) {                                        // describe the launch instead of making it
+        desc->append(desc->empty() ? "" : ";").append("gemv_select<1> grid=" + std::to_string(grid.x));
+        return hipSuccess;
+    }
     hipLaunchKernelGGL(gemv_select_kernel<1>, grid, block, 0, st, x, W, S, y, M, K, N);
     return hipGetLastError();
 }

@@ -31,6 +31,8 @@
 //  * Segment sigma (two per pair p, h = sigma % 2) is what one chain of four MFMAs covers:
 //    MFMA K-block G of segment sigma is scale group gamma = 8p + 2G + h.
 #include <algorithm>
+#include <cstdio>
+#include <string>
 
 #include "common.hpp"
 #include "kernels.hpp"
@@ -378,13 +380,8 @@ constexpr size_t shm_bytes(int K, int rows_per_wg, int NW)
 }
 
 template <int SP, int P, int R, bool ODD, bool T2, int NW, bool TWO>
-hipError_t launch_mx_t(const uint16_t *x, const MxSet &set0, int K, hipStream_t st)
+hipError_t launch_mx_t(const uint16_t *x, const MxSet &set0, int K, hipStream_t st, std::string *desc)
 {
-    static const hipError_t attr = hipFuncSetAttribute(
-        reinterpret_cast<const void *>(&gemv_mx_kernel<SP, P, R, ODD, T2, NW, TWO>),
-        hipFuncAttributeMaxDynamicSharedMemorySize,
-        (int)std::min<size_t>(shm_bytes(kMaxPairs * 1024, kMaxTileRows, NW), kMaxLds));
-    if (attr != hipSuccess) return attr;
     MxSet set = set0;
     int tiles = 0;
     for (int i = 0; i < set.count; ++i) {
@@ -401,6 +398,18 @@ hipError_t launch_mx_t(const uint16_t *x, const MxSet &set0, int K, hipStream_t 
     const int grid = tiles < cap ? tiles : (need > cap ? need : cap);
     const int rows_per_wg = (tiles + grid - 1) / grid * 16 * R;
     const bool two = set.count == 2;
+    if (desc) {                                        // describe the launch instead of making it
+        char buf[128];
+        snprintf(buf, sizeof buf, "gemv_mx<%d,%d,%d,%d,%d,%d,%d> grid=%d", SP, P, R, (int)ODD, (int)T2, NW,
+                 (int)TWO, grid);
+        desc->append(desc->empty() ? "" : ";").append(buf);
+        return hipSuccess;
+    }
+    static const hipError_t attr = hipFuncSetAttribute(
+        reinterpret_cast<const void *>(&gemv_mx_kernel<SP, P, R, ODD, T2, NW, TWO>),
+        hipFuncAttributeMaxDynamicSharedMemorySize,
+        (int)std::min<size_t>(shm_bytes(kMaxPairs * 1024, kMaxTileRows, NW), kMaxLds));
+    if (attr != hipSuccess) return attr;
     hipLaunchKernelGGL((gemv_mx_kernel<SP, P, R, ODD, T2, NW, TWO>), dim3(grid), dim3(64 * NW),
                        shm_bytes(K, rows_per_wg, NW), st, x, K | (tiles / grid) << 16, (tiles % grid) | grid << 16,
                        set.W[0], set.S[0], two ? set.W[1] : nullptr, two ? set.S[1] : nullptr, set.N[0],
@@ -410,14 +419,14 @@ hipError_t launch_mx_t(const uint16_t *x, const MxSet &set0, int K, hipStream_t 
 
 // Launches of at most two matrices take their whole tile table from scalar arguments.
 template <int SP, int P, int R, bool ODD, bool T2, int NW = 4>
-hipError_t launch_mx(const uint16_t *x, const MxSet &set, int K, hipStream_t st)
+hipError_t launch_mx(const uint16_t *x, const MxSet &set, int K, hipStream_t st, std::string *desc)
 {
-    return set.count <= 2 ? launch_mx_t<SP, P, R, ODD, T2, NW, true>(x, set, K, st)
-                          : launch_mx_t<SP, P, R, ODD, T2, NW, false>(x, set, K, st);
+    return set.count <= 2 ? launch_mx_t<SP, P, R, ODD, T2, NW, true>(x, set, K, st, desc)
+                          : launch_mx_t<SP, P, R, ODD, T2, NW, false>(x, set, K, st, desc);
 }
 
 template <bool ODD, bool T2>
-hipError_t dispatch_mx(const uint16_t *x, const MxSet &set, int K, hipStream_t st)
+hipError_t dispatch_mx(const uint16_t *x, const MxSet &set, int K, hipStream_t st, std::string *desc)
 {
     const int SP = (((K + 1023) >> 10) + 3) / 4;        // pairs per wave
     // One tile per workgroup (the grid covers all tiles): a one-slot ring, so that no dead
@@ -434,24 +443,24 @@ hipError_t dispatch_mx(const uint16_t *x, const MxSet &set, int K, hipStream_t s
     const int cap = SP == 1 ? 3 * 256 : SP == 2 ? 2 * 256 : 256;
     const bool one16 = t16 <= cap, one = t32 <= cap, few16 = t16 <= 3 * cap;
     switch (SP) {
-    case 1: return one16 ? launch_mx<1, 1, 1, ODD, T2>(x, set, K, st)
-                 : one   ? launch_mx<1, 1, 2, ODD, T2>(x, set, K, st)
-                 : few16 ? launch_mx<1, 3, 1, ODD, T2>(x, set, K, st) : launch_mx<1, 2, 2, ODD, T2>(x, set, K, st);
+    case 1: return one16 ? launch_mx<1, 1, 1, ODD, T2>(x, set, K, st, desc)
+                 : one   ? launch_mx<1, 1, 2, ODD, T2>(x, set, K, st, desc)
+                 : few16 ? launch_mx<1, 3, 1, ODD, T2>(x, set, K, st, desc) : launch_mx<1, 2, 2, ODD, T2>(x, set, K, st, desc);
     // One 16-row tile per workgroup: as many waves as pairs (up to 16), one pair each, so no wave
     // carries a second pair on the critical path (the wider workgroups fit fewer per CU).
-    case 2: return one16 ? launch_mx<1, 1, 1, ODD, T2, 8>(x, set, K, st)
-                 : one   ? launch_mx<2, 1, 2, ODD, T2>(x, set, K, st)
-                 : few16 ? launch_mx<2, 2, 1, ODD, T2>(x, set, K, st) : launch_mx<2, 2, 2, ODD, T2>(x, set, K, st);
-    case 3: return one16 ? launch_mx<1, 1, 1, ODD, T2, 12>(x, set, K, st)
-                 : one   ? launch_mx<3, 1, 2, ODD, T2>(x, set, K, st) : launch_mx<3, 2, 2, ODD, T2>(x, set, K, st);
+    case 2: return one16 ? launch_mx<1, 1, 1, ODD, T2, 8>(x, set, K, st, desc)
+                 : one   ? launch_mx<2, 1, 2, ODD, T2>(x, set, K, st, desc)
+                 : few16 ? launch_mx<2, 2, 1, ODD, T2>(x, set, K, st, desc) : launch_mx<2, 2, 2, ODD, T2>(x, set, K, st, desc);
+    case 3: return one16 ? launch_mx<1, 1, 1, ODD, T2, 12>(x, set, K, st, desc)
+                 : one   ? launch_mx<3, 1, 2, ODD, T2>(x, set, K, st, desc) : launch_mx<3, 2, 2, ODD, T2>(x, set, K, st, desc);
     // (ternary rows are twice as many bytes: 16-row tiles keep the ring in registers)
     case 4:
-        if (one16) return launch_mx<1, 1, 1, ODD, T2, 16>(x, set, K, st);
-        if constexpr (T2) return launch_mx<4, 1, 1, ODD, T2>(x, set, K, st);
-        else return launch_mx<4, 1, 2, ODD, T2>(x, set, K, st);
+        if (one16) return launch_mx<1, 1, 1, ODD, T2, 16>(x, set, K, st, desc);
+        if constexpr (T2) return launch_mx<4, 1, 1, ODD, T2>(x, set, K, st, desc);
+        else return launch_mx<4, 1, 2, ODD, T2>(x, set, K, st, desc);
     default:
-        if constexpr (T2) return launch_mx<5, 1, 1, ODD, T2>(x, set, K, st);
-        else return launch_mx<5, 1, 2, ODD, T2>(x, set, K, st);
+        if constexpr (T2) return launch_mx<5, 1, 1, ODD, T2>(x, set, K, st, desc);
+        else return launch_mx<5, 1, 2, ODD, T2>(x, set, K, st, desc);
     }
 }
 
@@ -459,14 +468,14 @@ hipError_t dispatch_mx(const uint16_t *x, const MxSet &set, int K, hipStream_t s
 
 int mx_max_k() { return kMaxPairs * 1024; }
 
-hipError_t launch_gemv_mx(const uint16_t *x, const MxSet &set, int K, hipStream_t st)
+hipError_t launch_gemv_mx(const uint16_t *x, const MxSet &set, int K, hipStream_t st, std::string *desc)
 {
-    return ((K >> 7) & 1) ? dispatch_mx<true, false>(x, set, K, st) : dispatch_mx<false, false>(x, set, K, st);
+    return ((K >> 7) & 1) ? dispatch_mx<true, false>(x, set, K, st, desc) : dispatch_mx<false, false>(x, set, K, st, desc);
 }
 
-hipError_t launch_gemv_mx_t2(const uint16_t *x, const MxSet &set, int K, hipStream_t st)
+hipError_t launch_gemv_mx_t2(const uint16_t *x, const MxSet &set, int K, hipStream_t st, std::string *desc)
 {
-    return ((K >> 7) & 1) ? dispatch_mx<true, true>(x, set, K, st) : dispatch_mx<false, true>(x, set, K, st);
+    return ((K >> 7) & 1) ? dispatch_mx<true, true>(x, set, K, st, desc) : dispatch_mx<false, true>(x, set, K, st, desc);
 }
 
 }  // namespace bin1

@@ -20,6 +20,9 @@
 // interleaves its A operands once per chunk and reuses them for every tile of the batch.
 // Read straight from memory, every A load would touch 64 cache lines.  The merge table
 // reuses the same LDS once the batch's last chunk is done.
+#include <cstdio>
+#include <string>
+
 #include "common.hpp"
 #include "kernels.hpp"
 
@@ -250,9 +253,15 @@ void gemv_smallm_kernel(const uint16_t *__restrict__ x, int M, int K, int tq, in
 }
 
 template <int TB, int D>
-hipError_t launch_sm(const uint16_t *x, const MxSet &set, int M, int K, int tiles, hipStream_t st)
+hipError_t launch_sm(const uint16_t *x, const MxSet &set, int M, int K, int tiles, hipStream_t st, std::string *desc)
 {
     static_assert(TB * 256 * kWaves * 4 <= kXBytes, "merge table fits the staging area");
+    if (desc) {                                        // describe the launch instead of making it
+        char buf[96];
+        snprintf(buf, sizeof buf, "gemv_smallm<%d,%d> grid=%d", TB, D, (tiles + TB - 1) / TB);
+        desc->append(desc->empty() ? "" : ";").append(buf);
+        return hipSuccess;
+    }
     static const hipError_t attr = hipFuncSetAttribute(reinterpret_cast<const void *>(&gemv_smallm_kernel<TB, D>),
                                                        hipFuncAttributeMaxDynamicSharedMemorySize, kXBytes);
     if (attr != hipSuccess) return attr;
@@ -264,7 +273,7 @@ hipError_t launch_sm(const uint16_t *x, const MxSet &set, int M, int K, int tile
 
 }  // namespace
 
-hipError_t launch_gemv_smallm(const uint16_t *x, const MxSet &set0, int M, int K, hipStream_t st)
+hipError_t launch_gemv_smallm(const uint16_t *x, const MxSet &set0, int M, int K, hipStream_t st, std::string *desc)
 {
     MxSet set = set0;
     int tiles = 0;
@@ -276,13 +285,13 @@ hipError_t launch_gemv_smallm(const uint16_t *x, const MxSet &set0, int M, int K
     // grows past 256 beyond that); with several K chunks, more chunks per tile are in flight
     const int per = (tiles + 255) / 256, nchunk = (K + kChunkK - 1) / kChunkK;
     if (nchunk == 1) {
-        if (per <= 2) return launch_sm<2, 0>(x, set, M, K, tiles, st);
-        if (per <= 4) return launch_sm<4, 0>(x, set, M, K, tiles, st);
-        return launch_sm<6, 0>(x, set, M, K, tiles, st);
+        if (per <= 2) return launch_sm<2, 0>(x, set, M, K, tiles, st, desc);
+        if (per <= 4) return launch_sm<4, 0>(x, set, M, K, tiles, st, desc);
+        return launch_sm<6, 0>(x, set, M, K, tiles, st, desc);
     }
-    if (per <= 1) return launch_sm<1, 4>(x, set, M, K, tiles, st);
-    if (per <= 2) return launch_sm<2, 3>(x, set, M, K, tiles, st);
-    return launch_sm<4, 2>(x, set, M, K, tiles, st);
+    if (per <= 1) return launch_sm<1, 4>(x, set, M, K, tiles, st, desc);
+    if (per <= 2) return launch_sm<2, 3>(x, set, M, K, tiles, st, desc);
+    return launch_sm<4, 2>(x, set, M, K, tiles, st, desc);
 }
 
 }  // namespace bin1

@@ -5,8 +5,14 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <string>
+
 namespace bin1 {
 
+// Every product launcher takes an optional `desc`: when it is given, nothing is launched and the
+// name of the kernel variant and its grid that the call would launch are appended to it instead
+// (the library's variant query runs the same dispatch code as the launches).
+//
 // Up to kMaxMats products that read the same activation vector (e.g. q/k/v or gate/up),
 // decoded in one launch.  tile_end[] is filled in by the launcher (cumulative row tiles).
 constexpr int kMaxMats = 4;
@@ -59,20 +65,22 @@ hipError_t launch_gemv_chain(ChainHeader *hdr, int *done, const ChainStage *tabl
 
 // Largest K the block-scaled decode kernel takes (longer rows use the select kernel).
 int mx_max_k();
-hipError_t launch_gemv_mx(const uint16_t *x, const MxSet &set, int K, hipStream_t st);
+hipError_t launch_gemv_mx(const uint16_t *x, const MxSet &set, int K, hipStream_t st, std::string *desc = nullptr);
 // The same product for ternary weights in 2-bit slots (W pointers of the set: uint32 [N][K/16]).
-hipError_t launch_gemv_mx_t2(const uint16_t *x, const MxSet &set, int K, hipStream_t st);
+hipError_t launch_gemv_mx_t2(const uint16_t *x, const MxSet &set, int K, hipStream_t st,
+                             std::string *desc = nullptr);
 
 hipError_t launch_gemv(const uint16_t *x, const uint32_t *W, const uint16_t *S, uint16_t *y,
-                       int M, int K, int N, hipStream_t st);
+                       int M, int K, int N, hipStream_t st, std::string *desc = nullptr);
 // Small-batch product (2 <= M <= 16) on fp16 MFMA with the tokens as the A rows.
 // 2 <= M <= 16 tokens, 1..4 products sharing x (tile_end filled in by the launcher).
-hipError_t launch_gemv_smallm(const uint16_t *x, const MxSet &set, int M, int K, hipStream_t st);
+hipError_t launch_gemv_smallm(const uint16_t *x, const MxSet &set, int M, int K, hipStream_t st,
+                              std::string *desc = nullptr);
 hipError_t launch_prefill(const uint16_t *x, const uint32_t *W, const uint16_t *S, uint16_t *y,
-                          int M, int K, int N, hipStream_t st);
+                          int M, int K, int N, hipStream_t st, std::string *desc = nullptr);
 // Ternary weights in 2-bit slots: T uint32 [N][K/16].
 hipError_t launch_prefill_t2(const uint16_t *x, const uint32_t *T, const uint16_t *S, uint16_t *y,
-                             int M, int K, int N, hipStream_t st);
+                             int M, int K, int N, hipStream_t st, std::string *desc = nullptr);
 hipError_t launch_pm1(const uint32_t *A, const uint32_t *W, int32_t *y, int M, int K, int N,
                       hipStream_t st);
 hipError_t launch_xor_bits(uint32_t *const *Wtab, const int32_t *Ktab, const int32_t *Ntab, int nmat,
@@ -83,5 +91,8 @@ hipError_t launch_xor_patch(uint32_t *W, const int32_t *rows, int nrows, int K, 
 hipError_t launch_xor_patch_multi(uint32_t *const *Wtab, const int32_t *Ktab, const int32_t *Ntab,
                                   int nmat, const int32_t *entries, int nentries, int32_t *bad,
                                   hipStream_t st);
+
+// Streaming read of `bytes` (multiple of 16) into a per-wave digest sink[4 * grid].
+hipError_t launch_stream_read(const void *buf, size_t bytes, uint32_t *sink, int grid, int unroll, hipStream_t st);
 
 }  // namespace bin1

@@ -8,8 +8,17 @@
 
 namespace bin1 {
 
-// One workgroup per patch entry; each thread complements 16-byte chunks of the row.
-// Row bytes are K/8 = 16 * (K/128), so a row is a whole number of 16-byte chunks.
+// One workgroup per patch entry; each thread complements 8-byte words of the row with atomic
+// XORs (no value returned, so they are issued and not waited on).  Complementing is an XOR, so
+// entries commute: a row listed an even number of times in one call ends unchanged and an odd
+// number of times complemented, whatever the order the workgroups run in.
+__device__ __forceinline__ void complement_row(uint32_t *row32, int K)
+{
+    unsigned long long *row = reinterpret_cast<unsigned long long *>(row32);
+    const int words = K >> 6;                              // K / 64 eight-byte words
+    for (int c = threadIdx.x; c < words; c += blockDim.x) atomicXor(row + c, ~0ull);
+}
+
 __global__ __launch_bounds__(64) void xor_patch_kernel(uint32_t *__restrict__ W,
                                                         const int32_t *__restrict__ rows,
                                                         int K, int N, int32_t *bad)
@@ -19,13 +28,7 @@ __global__ __launch_bounds__(64) void xor_patch_kernel(uint32_t *__restrict__ W,
         if (threadIdx.x == 0 && bad) atomicAdd(bad, 1);
         return;
     }
-    const int chunks = K >> 7;
-    uint4 *row = reinterpret_cast<uint4 *>(W + (size_t)r * (K >> 5));
-    for (int c = threadIdx.x; c < chunks; c += blockDim.x) {
-        uint4 v = row[c];
-        v.x = ~v.x; v.y = ~v.y; v.z = ~v.z; v.w = ~v.w;
-        row[c] = v;
-    }
+    complement_row(W + (size_t)r * (K >> 5), K);
 }
 
 __global__ __launch_bounds__(64) void xor_patch_multi_kernel(
@@ -45,13 +48,7 @@ __global__ __launch_bounds__(64) void xor_patch_multi_kernel(
         if (threadIdx.x == 0 && bad) atomicAdd(bad, 1);
         return;
     }
-    const int chunks = K >> 7;
-    uint4 *row = reinterpret_cast<uint4 *>(Wtab[id] + (size_t)r * (K >> 5));
-    for (int c = threadIdx.x; c < chunks; c += blockDim.x) {
-        uint4 v = row[c];
-        v.x = ~v.x; v.y = ~v.y; v.z = ~v.z; v.w = ~v.w;
-        row[c] = v;
-    }
+    complement_row(Wtab[id] + (size_t)r * (K >> 5), K);
 }
 
 // Bit-granular patch ["LocalLLaMA ... XOR patch 'Bankai'" page, experiments section: random

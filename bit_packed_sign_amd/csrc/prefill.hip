@@ -25,6 +25,8 @@
 #include "common.hpp"
 #include "kernels.hpp"
 
+#include <cstdio>
+#include <string>
 #include <type_traits>
 
 namespace bin1 {
@@ -287,9 +289,16 @@ void prefill_kernel(const uint16_t *__restrict__ x, const uint32_t *__restrict__
 namespace {
 template <int BM, int WM, int WN, int WPE, bool T2>
 hipError_t launch_prefill_t(const uint16_t *x, const uint32_t *W, const uint16_t *S, uint16_t *y, int M, int K,
-                            int N, hipStream_t st)
+                            int N, hipStream_t st, std::string *desc)
 {
     constexpr int shm = 2 * BM * LDK * 2;
+    if (desc) {                                        // describe the launch instead of making it
+        char buf[96];
+        snprintf(buf, sizeof buf, "prefill<%d,%d,%d,%d,%d> grid=%d", BM, WM, WN, WPE, (int)T2,
+                 ((M + BM - 1) / BM) * ((N + BN - 1) / BN));
+        desc->append(desc->empty() ? "" : ";").append(buf);
+        return hipSuccess;
+    }
     static const hipError_t attr = hipFuncSetAttribute(
         reinterpret_cast<const void *>(&prefill_kernel<BM, WM, WN, WPE, T2>), hipFuncAttributeMaxDynamicSharedMemorySize,
         shm);
@@ -309,17 +318,17 @@ hipError_t launch_prefill_t(const uint16_t *x, const uint32_t *W, const uint16_t
 static bool prefill_small_tiles(int M, int N) { return (long long)((M + 255) / 256) * ((N + 191) / 192) < 512; }
 
 hipError_t launch_prefill(const uint16_t *x, const uint32_t *W, const uint16_t *S, uint16_t *y,
-                          int M, int K, int N, hipStream_t st)
+                          int M, int K, int N, hipStream_t st, std::string *desc)
 {
-    if (prefill_small_tiles(M, N)) return launch_prefill_t<128, 2, 2, 2, false>(x, W, S, y, M, K, N, st);
-    return launch_prefill_t<256, 2, 2, 1, false>(x, W, S, y, M, K, N, st);
+    if (prefill_small_tiles(M, N)) return launch_prefill_t<128, 2, 2, 2, false>(x, W, S, y, M, K, N, st, desc);
+    return launch_prefill_t<256, 2, 2, 1, false>(x, W, S, y, M, K, N, st, desc);
 }
 
 hipError_t launch_prefill_t2(const uint16_t *x, const uint32_t *T, const uint16_t *S, uint16_t *y,
-                             int M, int K, int N, hipStream_t st)
+                             int M, int K, int N, hipStream_t st, std::string *desc)
 {
-    if (prefill_small_tiles(M, N)) return launch_prefill_t<128, 2, 2, 2, true>(x, T, S, y, M, K, N, st);
-    return launch_prefill_t<256, 2, 2, 1, true>(x, T, S, y, M, K, N, st);
+    if (prefill_small_tiles(M, N)) return launch_prefill_t<128, 2, 2, 2, true>(x, T, S, y, M, K, N, st, desc);
+    return launch_prefill_t<256, 2, 2, 1, true>(x, T, S, y, M, K, N, st, desc);
 }
 
 }  // namespace bin1

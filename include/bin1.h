@@ -130,8 +130,10 @@ int bin1_gemv_pm1(const uint32_t *Abits, const uint32_t *Wbits, int32_t *y,
 /* XOR row patch, in place: for each entry r of rowlist (device int32[nrows]) every
  * word of row r of Wbits ([N][K/32]) is complemented, i.e. all K signs of output row
  * r are flipped (y[:, r] -> -y[:, r]); scales are untouched.  Calling it again with
- * the same list removes the patch.  Entries must be distinct (duplicates within one
- * call race); entries outside [0, N) are skipped and, if bad_rows (device int32*,
+ * the same list removes the patch.  The complement is applied as atomic XORs, so entries
+ * commute: a row listed an even number of times in one call ends unchanged, an odd number
+ * of times complemented (a patch's rows are normally distinct; repeats are well defined,
+ * not an error).  Entries outside [0, N) are skipped and, if bad_rows (device int32*,
  * may be NULL) is given, counted into *bad_rows by atomic add (the caller zeroes it).
  * nrows == 0 is a no-op.  Order the call on the same stream as the products that
  * read Wbits.  ["LocalLLaMA ... XOR patch 'Bankai'", section "Key points"] */
@@ -142,8 +144,9 @@ int bin1_xor_patch_apply(uint32_t *Wbits, const int32_t *rowlist, int nrows,
  * Wtab (device uint32_t*[nmat]), Ktab and Ntab (device int32[nmat]) describe the
  * matrices; entries (device int32[nentries][2]) holds (matrix id, row) pairs.  Entries
  * with a matrix id outside [0, nmat), a row outside [0, N_id), or a K_id that is not a
- * positive multiple of 128 are skipped and counted into *bad_rows when given.  Entries
- * must be distinct.  nentries == 0 is a no-op. */
+ * positive multiple of 128 are skipped and counted into *bad_rows when given.  As for the
+ * single-matrix call, repeated entries commute (an even count leaves the row unchanged).
+ * nentries == 0 is a no-op. */
 int bin1_xor_patch_apply_multi(uint32_t *const *Wtab, const int32_t *Ktab, const int32_t *Ntab,
                                int nmat, const int32_t *entries, int nentries,
                                int32_t *bad_rows, void *stream);
@@ -221,6 +224,25 @@ int bin1_gemv_chain(const bin1_chain_plan *plan, void *stream);
 
 /* Synchronously read the workspace: *runs = completed runs, *error = 1 if a wait gave up. */
 int bin1_chain_status(const bin1_chain_plan *plan, int *runs, int *error);
+
+/* Measurement helper (does none of the method's arithmetic): reads `bytes` of device memory at
+ * buf once, with 16-byte nontemporal loads spread over `grid` workgroups of 256 threads, `unroll`
+ * loads in flight per thread (4, 8 or 16), and writes one XOR digest per wave into sink (device
+ * uint32 [4 * grid]).  Timing it gives the HBM read rate this GPU sustains, the reference against
+ * which the decode products' bandwidth is judged (decode speed is bounded by bandwidth over weight
+ * bytes: "Bonsai 27B" page, section "Low-bit kernels for hybrid attention").  Requires buf 16-byte
+ * aligned, bytes a positive multiple of 16, 1 <= grid <= 65536, and sink not overlapping buf. */
+int bin1_stream_read(const void *buf, size_t bytes, uint32_t *sink, int grid, int unroll, void *stream);
+
+/* Diagnostic: the kernel variant(s) and grid that a product call would launch for these shapes,
+ * from the same dispatch code the calls run (nothing is launched; no device is needed).
+ * op: 0 = bin1_gemv (count == 1) or bin1_gemv_group, 1 = bin1_gemv_t2 or bin1_gemv_group_t2,
+ * 2 = bin1_gemm_prefill, 3 = bin1_gemm_prefill_t2 (count == 1 for 2 and 3).  N: host int[count],
+ * the row counts as the call would launch them (matrices a group call runs as one taller matrix
+ * are given as one).  Writes a NUL-terminated text such as "gemv_mx<1,1,1,0,0,4,1> grid=384" into
+ * name (len bytes; launches separated by ';').  Requires M >= 1, K >= 128, K % 128 == 0 and
+ * 1 <= N[i] < 2^24 - 64; BIN1_ERR_SHAPE also if len is too small. */
+int bin1_kernel_variant(int op, int M, int K, int count, const int *N, char *name, int len);
 
 /* Static description of a status code. */
 const char *bin1_status_string(int status);

@@ -88,6 +88,17 @@ def test_group_validation(L):
     S = arr(FAKE * 12, FAKE * 16)
     Y = arr(FAKE * 8 + 16, FAKE * 20)
     assert L.bin1_gemv_group(FAKE, 2, W, S, Y, n, 1, 128, None) == -4
+    # Back-to-back matrices (weights, scales and outputs of matrix 1 each right after matrix 0's,
+    # which a batch-1 call runs as one taller matrix) whose second output covers the first
+    # matrix's weights: each output is clear of its own inputs, so only the check over the
+    # caller's whole list (made before the merge) sees the overlap.
+    n64 = (ctypes.c_int * 2)(64, 64)
+    y0 = 0x1000000
+    W0 = y0 + 128                        # y1 = y0 + 64 halves = W0
+    Wm = arr(W0, W0 + 64 * 16)
+    Sm = arr(0x2000000, 0x2000000 + 128)
+    Ym = arr(y0, y0 + 128)
+    assert L.bin1_gemv_group(0x3000000, 2, Wm, Sm, Ym, n64, 1, 128, None) == -4
     # every product empty: nothing to do
     assert L.bin1_gemv_group(None, 2, arr(None, None), arr(None, None), arr(None, None), n, 0, 128, None) == 0
     z = (ctypes.c_int * 2)(0, 0)

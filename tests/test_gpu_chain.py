@@ -1,14 +1,14 @@
 """GPU parity of the decode-step chain (bin1_chain_prepare / bin1_gemv_chain) against the
 fp64 oracle: every stage of a chain, each kernel variant, a chain whose stages feed each other,
 replays (eager and from a captured graph), the bounded-wait failure path, and the 8B decode
-step at full size with sampled outputs."""
+step at full size with every output checked."""
 import numpy as np
 import pytest
 import torch
 
 import bit_packed_sign_amd as b1
 from bit_packed_sign_amd import synth
-from parity import TOL, dev_tensors, norm_err, sample_rows
+from parity import TOL, dev_tensors, norm_err
 
 pytestmark = pytest.mark.gpu
 
@@ -115,8 +115,9 @@ def test_chain_replays_bit_identical_and_in_graph(orc, dev):
 
 def test_chain_stages_feed_each_other(orc, dev):
     """x of stage s+1 is an output of stage s, so a stage that started before its predecessor
-    finished would read the NaN fill.  The oracle runs the same chain on its own outputs,
-    rounded to fp16 as the library's outputs are."""
+    finished would read the NaN fill (and give non-finite outputs).  Each stage is checked on its
+    own: the oracle takes the fp16 activations the GPU actually fed that stage (the previous
+    stage's output as stored), so every stage meets the single-product bar."""
     dims = [(1024, [2048, 512, 512]), (2048, [4096]), (4096, [1280, 3000]), (1280, [12288]),
             (12288, [1024]), (1024, [17, 300, 5000, 256])]
     mats = [[_mat(9000 + 10 * s + i, K, N) for i, N in enumerate(Ns)] for s, (K, Ns) in enumerate(dims)]
@@ -128,23 +129,21 @@ def test_chain_stages_feed_each_other(orc, dev):
         stages.append((xd, [dev_tensors(dev, W=W)[0] for W, _ in mats[s]],
                        [dev_tensors(dev, S=S)[0] for _, S in mats[s]], ys[s]))
     plan = b1.ChainPlan(stages)
-    # oracle chain
-    refs, x = [], x0
-    for s in range(len(dims)):
-        out = [orc.gemv(x, W, S) for W, S in mats[s]]
-        refs.append(out)
-        x = out[0][0].astype(np.float16)
     for rep in range(2):
         for row in ys:
             for y in row:
                 y.fill_(float("nan"))
         plan.run()
         torch.cuda.synchronize()
+        x = x0
         for s in range(len(dims)):
-            for i, (ref, nrm) in enumerate(refs[s]):
-                # each earlier stage's fp16 rounding and product error carries forward once
-                e = norm_err(ys[s][i], ref, nrm)
-                assert e <= TOL * (s + 1), f"run {rep} stage {s} matrix {i}: {e}"
+            for i, (W, S) in enumerate(mats[s]):
+                y = ys[s][i].cpu().numpy()
+                assert np.all(np.isfinite(y)), f"run {rep} stage {s} matrix {i}: read an unfinished input"
+                ref, nrm = orc.gemv(x, W, S)
+                e = norm_err(y, ref, nrm)
+                assert e <= TOL, f"run {rep} stage {s} matrix {i}: {e}"
+            x = ys[s][0].cpu().numpy()                # what stage s + 1 read
     assert plan.status() == (2, 0)
 
 
@@ -192,9 +191,9 @@ def test_chain_rejects_bad_plans(dev):
         b1.ChainPlan([(torch.zeros((2, K), dtype=torch.float16, device=dev), [Wd], [Sd], [y])])
 
 
-def test_chain_decode_8b_full_size_sampled(orc, dev):
-    """The whole 8B decode step (145 stages, 253 products) as one chain, in the
-    configuration the benchmark times; sampled outputs of every product checked."""
+def test_chain_decode_8b_every_output(orc, dev):
+    """The whole 8B decode step (145 stages, 253 products) as one chain, in the configuration
+    the benchmark times; every output of every product checked against the oracle."""
     wl = synth.decode_8b()
     stages, checks = [], []
     gi = 0
@@ -208,19 +207,15 @@ def test_chain_decode_8b_full_size_sampled(orc, dev):
             Wd.append(a)
             Sd.append(b)
             yd.append(torch.full((1, g.N), float("nan"), dtype=torch.float16, device=dev))
-            if gi % 7 == 0 or g.N > 100000:          # a spread of products incl. lm_head
-                checks.append((x, W, S, yd[-1], gi))
+            checks.append((s, yd[-1], gi))
             gi += 1
         stages.append((xd, Wd, Sd, yd))
     plan = b1.ChainPlan(stages)
     plan.run()
     torch.cuda.synchronize()
     assert plan.status() == (1, 0)
-    for row in stages:
-        for y in row[3]:
-            assert bool(torch.isfinite(y).all())
-    for x, W, S, y, gi in checks:
-        rows = sample_rows(synth.rng_for(0, synth.WL_TEST, 7800 + gi), W.shape[0], k=64, edge=16)
-        ref, nrm = orc.gemv_rows(x, W, S, rows)
-        e = norm_err(y.float().cpu().numpy()[:, rows], ref, nrm)
+    for s, y, gi in checks:
+        W, S = synth.gemv_tensors(0, wl, gi)
+        ref, nrm = orc.gemv(synth.stage_activations(0, wl, s), W, S)
+        e = norm_err(y, ref, nrm)
         assert e <= TOL, f"product {gi}: {e}"

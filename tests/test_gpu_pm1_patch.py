@@ -70,8 +70,56 @@ def test_patch_out_of_range_and_empty(orc, dev):
     assert int(bad.item()) == nbad == 3
     b1.xor_patch_apply(Wd, torch.zeros(0, dtype=torch.int32, device=dev))
     assert np.array_equal(Wd.cpu().numpy().view(np.uint32), expect)
-    with pytest.raises(ValueError):
-        b1.xor_patch_apply(Wd, torch.tensor([1, 1], dtype=torch.int32, device=dev))
+    with pytest.raises(ValueError):                  # the opt-in host check of repeated rows
+        b1.xor_patch_apply(Wd, torch.tensor([1, 1], dtype=torch.int32, device=dev), check_distinct=True)
+
+
+def test_patch_repeated_rows_commute(orc, dev):
+    """Rows listed several times in one call: each listing is one complement, applied as atomic
+    XORs, so an even count leaves the row unchanged and an odd count complements it -- the same
+    as the oracle's one-after-another application -- on both patch calls, every run."""
+    K, N = 4096, 64
+    W = synth.sign_words(synth.rng_for(0, synth.WL_TEST, 6150), N, K)
+    rows = np.array([3, 3, 5, 9, 9, 9, 11, 11, 11, 11, 20] * 8, np.int32)   # many workgroups per row
+    expect, _ = orc.xor_patch(W, rows, K)
+    for _ in range(3):
+        Wd = _i32(W).to(dev)
+        b1.xor_patch_apply(Wd, torch.from_numpy(rows).to(dev))
+        assert np.array_equal(Wd.cpu().numpy().view(np.uint32), expect)
+        table = b1.PatchTable([Wd])
+        ent = torch.from_numpy(np.stack([np.zeros_like(rows), rows], axis=1)).to(dev)
+        b1.xor_patch_apply_multi(table, ent)
+        assert np.array_equal(Wd.cpu().numpy().view(np.uint32), W)
+
+
+def test_patch_in_a_graph(orc, dev):
+    """The patch calls enqueue work only (no host synchronisation), so they can be captured; every
+    replay of apply-then-remove leaves the weights as they were, and one apply matches the oracle."""
+    K, N = 1024, 300
+    W = synth.sign_words(synth.rng_for(0, synth.WL_TEST, 6160), N, K)
+    rows = synth.distinct_rows(synth.rng_for(0, synth.WL_TEST, 6161), N, 40)
+    Wd = _i32(W).to(dev)
+    rd = torch.from_numpy(rows).to(dev)
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        b1.xor_patch_apply(Wd, rd)
+        b1.xor_patch_apply(Wd, rd)
+    torch.cuda.current_stream().wait_stream(s)
+    torch.cuda.synchronize()
+    g1, g2 = torch.cuda.CUDAGraph(), torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g1):
+        b1.xor_patch_apply(Wd, rd)
+    with torch.cuda.graph(g2):
+        b1.xor_patch_apply(Wd, rd)
+    expect, _ = orc.xor_patch(W, rows, K)
+    for _ in range(3):
+        g1.replay()
+        torch.cuda.synchronize()
+        assert np.array_equal(Wd.cpu().numpy().view(np.uint32), expect)
+        g2.replay()
+        torch.cuda.synchronize()
+        assert np.array_equal(Wd.cpu().numpy().view(np.uint32), W)
 
 
 def test_multi_matrix_patch_27b_mlp(orc, dev):

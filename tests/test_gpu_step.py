@@ -1,9 +1,15 @@
-"""GPU parity of the decode steps exactly as the benchmark times them: the 8B step's 145 stages with
-each stage's projections stored back to back (q|k|v and gate|up run as one matrix each), and the
-8B MLP at batch 16 (72 stages on the small-batch kernel), one launch per stage, captured into a
-HIP graph and replayed.  Sampled outputs of a spread of products (the first layers' fused stages
-included, and lm_head) are checked against the fp64 oracle, and every replay must reproduce the
-eager outputs bit for bit.  Concurrent calls on two streams give the same outputs as one stream."""
+"""GPU parity of the decode steps exactly as the benchmark times them (bench.Step): each stage's
+projections stored back to back (q|k|v and gate|up run as one matrix each), one launch per stage,
+captured into a HIP graph and replayed.
+
+* the 8B step (145 stages, 253 products), every output against the fp64 oracle;
+* the 27B step (256 stages, 448 products), every output; its fused q|k|v (15360 x 5120) and
+  gate|up (34816 x 5120) launches are the variants the benchmark runs for it;
+* the ternary 8B step (2-bit slots), every output;
+* the 8B MLP at batch 16 (72 stages on the small-batch kernel), all 16 tokens of every eighth row
+  plus the edge rows of every product.
+Every replay must reproduce the eager outputs bit for bit, with eager work between replays.
+Concurrent calls on two streams give the same outputs as one stream."""
 import numpy as np
 import pytest
 import torch
@@ -11,7 +17,7 @@ import torch
 import bench
 import bit_packed_sign_amd as b1
 from bit_packed_sign_amd import synth
-from parity import TOL, norm_err, sample_rows
+from parity import TOL, norm_err
 
 pytestmark = pytest.mark.gpu
 
@@ -22,34 +28,42 @@ def dev():
     return torch.device("cuda:0")
 
 
-@pytest.mark.parametrize("name,n_gemvs", [("decode_8b", 253), ("mlp_8b_m16", 108)])
-def test_step_graph_full_size_sampled(orc, dev, name, n_gemvs):
-    wl = getattr(synth, name)()
-    step = bench.Step(wl, dev)
+def _rows(N, stride):
+    if stride == 1:
+        return np.arange(N)
+    return np.unique(np.concatenate([np.arange(0, N, stride), np.arange(min(16, N)), np.arange(max(0, N - 16), N)]))
+
+
+def _check_step(orc, dev, wl, ternary, row_stride, expect_variants=None):
+    step = bench.Step(wl, dev, ternary=ternary)
+    if expect_variants:
+        for s, want in expect_variants.items():
+            x, Ws, Ss, ys, _ = step.stages[s]
+            op = "gemv_t2" if ternary else "gemv"
+            got = b1.kernel_variant(op, wl.M, x.shape[1], [sum(W.shape[0] for W in Ws)] if wl.M == 1
+                                    else [W.shape[0] for W in Ws])
+            assert got.split(" ")[0] == want, (s, got, want)
     outs = [y for _, _, _, ys, _ in step.stages for y in ys]
     for y in outs:
         y.fill_(float("nan"))
     step.run_eager()
     torch.cuda.synchronize()
     eager = [y.clone() for y in outs]
-    for y in eager:
-        assert bool(torch.isfinite(y).all())
-
+    gen = synth.ternary_gemv_tensors if ternary else synth.gemv_tensors
+    ref_fn = orc.gemv_t2 if ternary else orc.gemv
     gi = 0
-    checked = 0
+    worst = 0.0
     for s, stage in enumerate(wl.stages):
         x = synth.stage_activations(0, wl, s)
         for g in stage.gemvs:
-            if gi % 5 == 0 or s % 4 in (0, 2) and s < 8 or g.N > 100000:
-                W, S = synth.gemv_tensors(0, wl, gi)
-                rows = sample_rows(synth.rng_for(0, synth.WL_TEST, 8800 + gi), g.N, k=32 if wl.M > 1 else 48, edge=16)
-                ref, nrm = orc.gemv_rows(x, W, S, rows)
-                e = norm_err(eager[gi].float().cpu().numpy()[:, rows], ref, nrm)
-                assert e <= TOL, f"stage {s} product {gi}: {e}"
-                checked += 1
+            W, S = gen(0, wl, gi)
+            rows = _rows(g.N, row_stride)
+            ref, nrm = ref_fn(x, W[rows], S[rows])
+            e = norm_err(eager[gi].float().cpu().numpy()[:, rows], ref, nrm)
+            assert e <= TOL, f"stage {s} product {gi} ({g.name}): {e}"
+            worst = max(worst, e)
             gi += 1
-    assert gi == n_gemvs and checked >= 20
-
+    assert gi == len(wl.gemvs)
     step.capture()
     for rep in range(3):
         for y in outs:                          # eager work between replays
@@ -59,6 +73,30 @@ def test_step_graph_full_size_sampled(orc, dev, name, n_gemvs):
         torch.cuda.synchronize()
         for i, (a, y) in enumerate(zip(eager, outs)):
             assert torch.equal(a, y), f"graph replay {rep}: product {i} differs"
+    return worst
+
+
+def test_step_8b_every_output(orc, dev):
+    _check_step(orc, dev, synth.decode_8b(), False, 1,
+                {0: "gemv_mx<1,1,1,0,0,4,1>", 1: "gemv_mx<1,1,1,0,0,4,1>", 2: "gemv_mx<1,1,2,0,0,4,1>",
+                 3: "gemv_mx<1,1,1,0,0,12,1>", 144: "gemv_mx<1,2,2,0,0,4,1>"})
+
+
+def test_step_27b_every_output(orc, dev):
+    _check_step(orc, dev, synth.decode_27b(), False, 1,
+                {0: "gemv_mx<2,1,2,0,0,4,1>", 1: "gemv_mx<1,1,1,0,0,8,1>", 2: "gemv_mx<2,2,2,0,0,4,1>",
+                 3: "gemv_mx<5,1,2,0,0,4,1>"})
+
+
+def test_step_ternary_8b_every_output(orc, dev):
+    _check_step(orc, dev, synth.decode_8b(), True, 1,
+                {0: "gemv_mx<1,1,1,0,1,4,1>", 2: "gemv_mx<1,1,2,0,1,4,1>", 3: "gemv_mx<1,1,1,0,1,12,1>",
+                 144: "gemv_mx<1,2,2,0,1,4,1>"})
+
+
+def test_step_mlp16_every_product(orc, dev):
+    _check_step(orc, dev, synth.mlp_8b_m16(), False, 8,
+                {0: "gemv_smallm<6,0>", 1: "gemv_smallm<1,4>"})
 
 
 def test_concurrent_streams_match_one_stream(dev):

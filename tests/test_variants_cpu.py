@@ -1,0 +1,58 @@
+"""The variant query (bin1_kernel_variant) names, for every shape of tests/variants.py, the kernel
+variant the dispatch code picks; the GPU tests then run exactly those shapes against the oracle.
+Here (no GPU) the table is checked against the query, and the table is checked to reach every
+branch of the dispatch."""
+import pytest
+
+from variants import ALL_CASES, DECODE_CASES, DECODE_T2_CASES, case_id
+
+
+@pytest.fixture(scope="module")
+def b1():
+    import bit_packed_sign_amd as b1
+    from bit_packed_sign_amd import binding, build
+    import os
+    if not os.path.exists(binding.LIB_PATH):
+        build.build()
+    return b1
+
+
+@pytest.mark.parametrize("case", ALL_CASES, ids=case_id)
+def test_query_names_the_expected_variant(b1, case):
+    op, M, K, Ns, expect, _ = case
+    got = b1.kernel_variant(op, M, K, Ns)
+    assert got.split(" ")[0] == expect, (got, expect)
+    assert ";" not in got                      # one launch for the whole call
+
+
+def test_every_decode_branch_is_reached():
+    """Each (pairs per wave, ring slots, rows per tile, waves) branch of the batch-1 kernel occurs
+    with even and odd K / 128, with a partial last pair, and with one/two and three/four matrices."""
+    for cases in (DECODE_CASES, DECODE_T2_CASES):
+        seen = {}
+        for op, M, K, Ns, exp, kind in cases:
+            core = exp.split("<")[1].rstrip(">").split(",")
+            branch = tuple(core[i] for i in (0, 1, 2, 5))   # SP, P, R, NW
+            seen.setdefault(branch, set()).add((kind, core[3], core[6]))
+        expected_branches = 4 + 4 + 3 + 2 + 1
+        assert len(seen) == expected_branches, sorted(seen)
+        for branch, kinds in seen.items():
+            assert {k for k, _, _ in kinds} == {"even", "odd", "part"}, (branch, kinds)
+            assert {o for _, o, _ in kinds} == {"0", "1"}, (branch, kinds)
+    # matrices past the scalar tile table occur in every pairs-per-wave class
+    for cases in (DECODE_CASES, DECODE_T2_CASES):
+        classes = {((c[2] + 1023) // 1024 + 3) // 4 for c in cases if c[4].endswith(",0>")}
+        nws = {c[4].split(",")[5] for c in cases if c[4].endswith(",0>")}
+        assert classes == {1, 2, 3, 4, 5} and nws >= {"4", "12"}
+
+
+def test_query_rejects_bad_arguments(b1):
+    from bit_packed_sign_amd.binding import Bin1Error
+    with pytest.raises(Bin1Error):
+        b1.kernel_variant("gemv", 1, 100, [10])               # K % 128 != 0
+    with pytest.raises(Bin1Error):
+        b1.kernel_variant("gemv", 0, 128, [10])               # M < 1
+    with pytest.raises(Bin1Error):
+        b1.kernel_variant("prefill", 4, 128, [10, 20])        # prefill takes one matrix
+    with pytest.raises(Bin1Error):
+        b1.kernel_variant("gemv", 1, 128, [1, 2, 3, 4, 5])    # at most four matrices

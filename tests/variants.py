@@ -1,0 +1,89 @@
+"""Shapes that reach every branch of the product dispatch (test infrastructure).
+
+Each case is (op, M, K, Ns, expected variant): ``op`` as in ``bit_packed_sign_amd.kernel_variant``
+("gemv" covers bin1_gemv and bin1_gemv_group, "gemv_t2" their ternary forms), ``Ns`` the row
+counts of the matrices of one call, and the expected text the variant query returns for them.
+The shapes are derived from the dispatch thresholds of the batch-1 decode kernel (tiles of 16
+rows against the workgroups that fit 256 compute units at one, two or more 1024-wide pairs per
+wave), of the small-batch kernel (tiles per workgroup, 4096-wide K chunks) and of the prefill
+kernel (256-row tiles only when they fill the GPU twice over).  Every decode branch appears with
+an even and an odd number of scale groups per row (K / 128 odd: the scale pair of a lane is read
+as two halves), with a last 1024-wide pair that is only partly inside K, and with three or four
+matrices (no scalar tile table) as well as one or two.
+"""
+
+# K values: EVEN = K / 128 even and K a whole number of 1024-wide pairs; ODD = K / 128 odd;
+# PART = the last pair partly inside K
+SP_K = {
+    1: {"even": 4096, "odd": 3968, "part": 3200},
+    2: {"even": 8192, "odd": 4224, "part": 6400},
+    3: {"even": 12288, "odd": 8320, "part": 10496},
+    4: {"even": 16384, "odd": 12416, "part": 14592},
+    5: {"even": 20480, "odd": 16512, "part": 18688},
+}
+
+
+def _mx(sp, p, r, odd, t2, nw, two):
+    return f"gemv_mx<{sp},{p},{r},{int(odd)},{int(t2)},{nw},{int(two)}>"
+
+
+def _decode_cases(t2):
+    op = "gemv_t2" if t2 else "gemv"
+    cases = []
+    for kind, K in [(k, v) for sp in SP_K for k, v in SP_K[sp].items()]:
+        sp = ((K + 1023) // 1024 + 3) // 4
+        odd = (K // 128) % 2 == 1
+        # (Ns, expected (SP, P, R, NW)) per branch of this pairs-per-wave class
+        if sp == 1:
+            branches = [([100], (1, 1, 1, 4)), ([20000], (1, 1, 2, 4)), ([30000], (1, 3, 1, 4)),
+                        ([40000], (1, 2, 2, 4)), ([100, 200, 300], (1, 1, 1, 4)),
+                        ([10000, 10000, 10000], (1, 3, 1, 4))]
+        elif sp == 2:
+            branches = [([1000], (1, 1, 1, 8)), ([10000], (2, 1, 2, 4)), ([20000], (2, 2, 1, 4)),
+                        ([30000], (2, 2, 2, 4)), ([3000, 3000, 3000], (2, 1, 2, 4))]
+        elif sp == 3:
+            branches = [([1000], (1, 1, 1, 12)), ([6000], (3, 1, 2, 4)), ([10000], (3, 2, 2, 4)),
+                        ([500, 600, 700, 800], (1, 1, 1, 12))]
+        elif sp == 4:
+            branches = [([1000], (1, 1, 1, 16)), ([6000], (4, 1, 1 if t2 else 2, 4)),
+                        ([2000, 2000, 2000], (4, 1, 1 if t2 else 2, 4))]
+        else:
+            branches = [([1000], (5, 1, 1 if t2 else 2, 4)), ([300, 400, 500], (5, 1, 1 if t2 else 2, 4))]
+        # the even-K class carries every branch; the odd and partial-pair classes every branch too,
+        # but with smaller matrices where a branch allows it
+        for Ns, (s_, p_, r_, nw_) in branches:
+            cases.append((op, 1, K, Ns, _mx(s_, p_, r_, odd, t2, nw_, len(Ns) <= 2), f"{kind}"))
+    return cases
+
+
+DECODE_CASES = _decode_cases(False)
+DECODE_T2_CASES = _decode_cases(True)
+
+# rows past the block-scaled kernel's K range (K > 20480): the select/accumulate kernel
+SELECT_CASES = [("gemv", 1, 20608, [70], "gemv_select<1>", "long")]
+
+# small batch (2 <= M <= 16): tiles per workgroup TB and K chunks in flight D (D = 0: one chunk)
+SMALLM_CASES = [
+    ("gemv", 16, 4096, [4096], "gemv_smallm<2,0>", "tb2"),
+    ("gemv", 5, 4096, [12288], "gemv_smallm<4,0>", "tb4"),
+    ("gemv", 16, 4096, [12288, 12288], "gemv_smallm<6,0>", "tb6"),
+    ("gemv", 16, 12288, [4096], "gemv_smallm<1,4>", "tb1d4"),
+    ("gemv", 2, 8192, [8192], "gemv_smallm<2,3>", "tb2d3"),
+    ("gemv", 8, 8192, [16384], "gemv_smallm<4,2>", "tb4d2"),
+    ("gemv", 3, 3968, [1000, 2000, 3000], "gemv_smallm<2,0>", "group3"),
+]
+
+# prefill: 128-row tiles (two workgroups per CU) unless 256-row tiles fill the GPU twice over
+PREFILL_CASES = [
+    ("prefill", 300, 1024, [777], "prefill<128,2,2,2,0>", "small"),
+    ("prefill", 2048, 1024, [12288], "prefill<256,2,2,1,0>", "large"),
+    ("prefill_t2", 300, 1024, [777], "prefill<128,2,2,2,1>", "small"),
+    ("prefill_t2", 2048, 1024, [12288], "prefill<256,2,2,1,1>", "large"),
+]
+
+ALL_CASES = DECODE_CASES + DECODE_T2_CASES + SELECT_CASES + SMALLM_CASES + PREFILL_CASES
+
+
+def case_id(c):
+    op, M, K, Ns, exp, kind = c
+    return f"{op}-M{M}-K{K}-{'x'.join(map(str, Ns))}"
