@@ -162,6 +162,11 @@ class Step:
             nbytes = sum(round(g.N * g.K * synth.TERNARY_BYTES_PER_WEIGHT) if ternary else g.weight_bytes
                          for g in stage.gemvs)
             self.stages.append((xs, Ws, Ss, ys, nbytes))
+        # one workspace for the split-K small-batch products (stages run one after another)
+        import bit_packed_sign_amd as b1
+        need = max([b1.gemv_workspace_bytes(wl.M, st[0].shape[1], st[1][0].shape[0])
+                    for st in self.stages if len(st[1]) == 1] + [0])
+        self.workspace = torch.empty(need, dtype=torch.uint8, device=device) if need and not ternary else None
         torch.cuda.synchronize()
         self.weight_bytes = sum(st[4] for st in self.stages)
         log(f"[bench] {wl.name}{' (ternary)' if ternary else ''}: {gi} GEMVs in {len(self.stages)} stages, "
@@ -178,7 +183,10 @@ class Step:
             else:
                 b1.gemv_group_t2(x, Ws, Ss, outs=ys)
         elif len(Ws) == 1:
-            b1.gemv(x, Ws[0], Ss[0], out=ys[0])
+            if self.workspace is not None:    # small batch: K split over workgroups where it pays
+                b1.gemv_ws(x, Ws[0], Ss[0], workspace=self.workspace, out=ys[0])
+            else:
+                b1.gemv(x, Ws[0], Ss[0], out=ys[0])
         else:                                 # q/k/v or gate/up: same-input fusion
             b1.gemv_group(x, Ws, Ss, outs=ys)
 

@@ -43,12 +43,14 @@ _SIGS = {
     "bin1_chain_status": [_p, _p, _p],
     "bin1_stream_read": [_p, ctypes.c_size_t, _p, _i, _i, _p],
     "bin1_kernel_variant": [_i, _i, _i, _i, _p, _p, _i],
+    "bin1_gemv_workspace_bytes": [_i, _i, _i],
+    "bin1_gemv_ws": [_p, _p, _p, _p, _i, _i, _i, _p, ctypes.c_size_t, _p],
     "bin1_status_string": [_i],
     "bin1_last_error": [],
     "bin1_abi_version": [],
 }
 _RESTYPE = {"bin1_status_string": ctypes.c_char_p, "bin1_last_error": ctypes.c_char_p,
-            "bin1_chain_workspace_bytes": ctypes.c_size_t}
+            "bin1_chain_workspace_bytes": ctypes.c_size_t, "bin1_gemv_workspace_bytes": ctypes.c_size_t}
 
 
 class _Stage(ctypes.Structure):
@@ -149,6 +151,47 @@ def _product(fn: str, x, Wbits, scales, out, per_word: int = 32):
 def gemv(x: torch.Tensor, Wbits: torch.Tensor, scales: torch.Tensor, out: Optional[torch.Tensor] = None):
     """y[M][N] (fp16) = x[M][K] (fp16) times the 1-bit weights (Wbits [N][K/32], scales [N][K/128])."""
     return _product("bin1_gemv", x, Wbits, scales, out)
+
+
+def gemv_workspace_bytes(M: int, K: int, N: int) -> int:
+    """Bytes of workspace :func:`gemv_ws` uses for this shape (0: it takes no split path)."""
+    return int(lib().bin1_gemv_workspace_bytes(M, K, N))
+
+
+def gemv_ws(x: torch.Tensor, Wbits: torch.Tensor, scales: torch.Tensor, workspace: Optional[torch.Tensor] = None,
+            out: Optional[torch.Tensor] = None):
+    """:func:`gemv` with a device workspace (uint8, at least :func:`gemv_workspace_bytes` bytes,
+    256-byte aligned) that lets long small-batch products split K over workgroups.  The workspace
+    is allocated here when not given."""
+    _need(x, "x", (torch.float16,), 2)
+    _need(Wbits, "Wbits", _BITS, 2)
+    M, K = x.shape
+    N = Wbits.shape[0]
+    need = gemv_workspace_bytes(M, K, N) if M >= 1 and N >= 1 and K % 128 == 0 and K >= 128 else 0
+    if workspace is None and need:
+        workspace = torch.empty(need, dtype=torch.uint8, device=x.device)
+    wp, wb = 0, 0
+    if workspace is not None:
+        _need(workspace, "workspace", (torch.uint8,), 1)
+        wp, wb = workspace.data_ptr(), workspace.numel()
+    return _product_ws("bin1_gemv_ws", x, Wbits, scales, out, wp or None, wb)
+
+
+def _product_ws(fn, x, Wbits, scales, out, wp, wb):
+    _need(scales, "scales", (torch.float16,), 2)
+    M, K = x.shape
+    N = Wbits.shape[0]
+    if Wbits.shape[1] * 32 != K or tuple(scales.shape) != (N, K // 128):
+        raise ValueError(f"shapes: x {tuple(x.shape)}, Wbits {tuple(Wbits.shape)}, scales {tuple(scales.shape)}")
+    if out is None:
+        out = torch.empty((M, N), dtype=torch.float16, device=x.device)
+    else:
+        _need(out, "out", (torch.float16,), 2)
+        if tuple(out.shape) != (M, N):
+            raise ValueError("out has the wrong shape")
+    _call(fn, x.get_device(), x.data_ptr(), Wbits.data_ptr(), scales.data_ptr(), out.data_ptr(), M, K, N,
+          wp, wb, _stream(x))
+    return out
 
 
 def gemv_t2(x: torch.Tensor, Tbits: torch.Tensor, scales: torch.Tensor, out: Optional[torch.Tensor] = None):
@@ -399,12 +442,12 @@ def stream_read(buf: torch.Tensor, sink: Optional[torch.Tensor] = None, grid: in
     return sink
 
 
-_VARIANT_OPS = {"gemv": 0, "gemv_t2": 1, "prefill": 2, "prefill_t2": 3}
+_VARIANT_OPS = {"gemv": 0, "gemv_t2": 1, "prefill": 2, "prefill_t2": 3, "gemv_ws": 4}
 
 
 def kernel_variant(op: str, M: int, K: int, N) -> str:
     """The kernel variant(s) and grid a product call would launch (no GPU needed).  ``op``: "gemv"
-    (bin1_gemv / bin1_gemv_group), "gemv_t2", "prefill" or "prefill_t2"; ``N``: an int or the list
+    (bin1_gemv / bin1_gemv_group), "gemv_t2", "prefill", "prefill_t2" or "gemv_ws"; ``N``: an int or the list
     of row counts of a group call, as it would launch them."""
     Ns = [int(N)] if isinstance(N, (int, np.integer)) else [int(n) for n in N]
     buf = ctypes.create_string_buffer(1024)

@@ -135,6 +135,50 @@ int check_product(const void *x, const void *W, const void *S, const void *y, in
 
 }  // namespace
 
+namespace bin1 {
+
+int set_error(int status, const char *what) { return fail(status, "%s", what); }
+
+// bin1_gemv with a scratch area for the split-K path.  caller_ws: the scratch is the caller's
+// (validated like the other pointers); otherwise it is the library's own static array.
+int gemv_scratch(const char *fn, const void *x, const uint32_t *Wbits, const void *scales, void *y, int M, int K,
+                 int N, void *ws, size_t ws_bytes, bool caller_ws, void *stream)
+{
+    int st = check_product_host(x, Wbits, scales, y, M, K, N);
+    if (st) return st == kEmpty ? ok() : st;
+    const size_t need = smallm_split_bytes(M, K, N);
+    const hipStream_t s = static_cast<hipStream_t>(stream);
+    if (need == 0) {
+        if ((st = check_product_device(x, Wbits, scales, y))) return st;
+        return launched(launch_gemv(static_cast<const uint16_t *>(x), Wbits, static_cast<const uint16_t *>(scales),
+                                    static_cast<uint16_t *>(y), M, K, N, s),
+                        fn);
+    }
+    if (!ws) return fail(BIN1_ERR_NULL, "%s: this shape needs %zu bytes of workspace", fn, need);
+    if (ws_bytes < need)
+        return fail(BIN1_ERR_SHAPE, "%s: workspace of %zu bytes, this shape needs %zu", fn, ws_bytes, need);
+    if (reinterpret_cast<uintptr_t>(ws) & 255u) return fail(BIN1_ERR_ALIGN, "%s: workspace must be 256-byte aligned", fn);
+    if (caller_ws) {
+        const size_t xb = (size_t)M * K * 2, wb = (size_t)N * (K / 8), sb = (size_t)N * (K / 128) * 2,
+                     yb = (size_t)M * N * 2;
+        if (overlap(ws, need, x, xb) || overlap(ws, need, Wbits, wb) || overlap(ws, need, scales, sb) ||
+            overlap(ws, need, y, yb))
+            return fail(BIN1_ERR_ALIAS, "%s: the workspace overlaps an input or the output", fn);
+    }
+    if ((st = check_product_device(x, Wbits, scales, y)) || (caller_ws && (st = check_device(ws, "workspace"))))
+        return st;
+    MxSet set{};
+    set.W[0] = Wbits;
+    set.S[0] = static_cast<const uint16_t *>(scales);
+    set.y[0] = static_cast<uint16_t *>(y);
+    set.N[0] = N;
+    set.count = 1;
+    return launched(launch_gemv_smallm(static_cast<const uint16_t *>(x), set, M, K, s, nullptr, static_cast<float *>(ws)),
+                    fn);
+}
+
+}  // namespace bin1
+
 extern "C" {
 
 int bin1_abi_version(void) { return BIN1_ABI_VERSION; }
@@ -609,8 +653,8 @@ int bin1_kernel_variant(int op, int M, int K, int count, const int *N, char *nam
     if (!N || !name) return fail(BIN1_ERR_NULL, "N and name must be non-NULL");
     if (len < 1) return fail(BIN1_ERR_SHAPE, "len must be >= 1");
     name[0] = 0;
-    if (op < 0 || op > 3 || count < 1 || count > bin1::kMaxMats || (op >= 2 && count != 1))
-        return fail(BIN1_ERR_SHAPE, "need op 0..3 and count 1..%d (1 for the prefill calls)", bin1::kMaxMats);
+    if (op < 0 || op > 4 || count < 1 || count > bin1::kMaxMats || (op >= 2 && count != 1))
+        return fail(BIN1_ERR_SHAPE, "need op 0..4 and count 1..%d (1 for ops 2..4)", bin1::kMaxMats);
     if (M < 1 || K < 128 || K % 128 != 0)
         return fail(BIN1_ERR_SHAPE, "need M >= 1, K >= 128, K %% 128 == 0 (got M=%d K=%d)", M, K);
     for (int i = 0; i < count; ++i)
@@ -642,15 +686,42 @@ int bin1_kernel_variant(int op, int M, int K, int count, const int *N, char *nam
         e = bin1::launch_prefill(static_cast<const uint16_t *>(X), W[0], static_cast<const uint16_t *>(S[0]),
                                  static_cast<uint16_t *>(Y[0]), M, K, N[0], nullptr, &desc);
         break;
-    default:
+    case 3:
         e = bin1::launch_prefill_t2(static_cast<const uint16_t *>(X), W[0], static_cast<const uint16_t *>(S[0]),
                                     static_cast<uint16_t *>(Y[0]), M, K, N[0], nullptr, &desc);
+        break;
+    default:                                          // bin1_gemv_ws with a large enough workspace
+        if (bin1::smallm_split_bytes(M, K, N[0]) == 0) {
+            e = bin1::launch_gemv(static_cast<const uint16_t *>(X), W[0], static_cast<const uint16_t *>(S[0]),
+                                  static_cast<uint16_t *>(Y[0]), M, K, N[0], nullptr, &desc);
+        } else {
+            bin1::MxSet set{};
+            set.W[0] = W[0];
+            set.S[0] = static_cast<const uint16_t *>(S[0]);
+            set.y[0] = static_cast<uint16_t *>(Y[0]);
+            set.N[0] = N[0];
+            set.count = 1;
+            e = bin1::launch_gemv_smallm(static_cast<const uint16_t *>(X), set, M, K, nullptr, &desc,
+                                         reinterpret_cast<float *>((uintptr_t)0x2000000000ull));
+        }
         break;
     }
     if (e != hipSuccess) return fail(BIN1_ERR_LAUNCH, "bin1_kernel_variant: %s", hipGetErrorString(e));
     if ((int)desc.size() >= len) return fail(BIN1_ERR_SHAPE, "name buffer too small: need %zu bytes", desc.size() + 1);
     memcpy(name, desc.c_str(), desc.size() + 1);
     return ok();
+}
+
+size_t bin1_gemv_workspace_bytes(int M, int K, int N)
+{
+    if (M < 1 || N < 1 || K < 128 || K % 128 != 0) return 0;
+    return bin1::smallm_split_bytes(M, K, N);
+}
+
+int bin1_gemv_ws(const void *x, const uint32_t *Wbits, const void *scales, void *y, int M, int K, int N,
+                 void *workspace, size_t workspace_bytes, void *stream)
+{
+    return bin1::gemv_scratch("bin1_gemv_ws", x, Wbits, scales, y, M, K, N, workspace, workspace_bytes, true, stream);
 }
 
 }  // extern "C"

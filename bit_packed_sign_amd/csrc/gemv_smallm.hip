@@ -91,9 +91,10 @@ struct SmTile {     // one tile of the workgroup, resolved once
 // zeros and are never stored.  D = 0 is the one-chunk case (K <= 4096): no prefetch, no
 // refills.  Loads are never issued under a branch (the compiler would then wait for every
 // load in flight where the paths meet).
-template <int TB, int D>
+template <int TB, int D, bool SPLIT>
 __global__ __launch_bounds__(64 * kWaves) __attribute__((amdgpu_waves_per_eu(2, 2)))
-void gemv_smallm_kernel(const uint16_t *__restrict__ x, int M, int K, int tq, int tr, int G, MxSet set)
+void gemv_smallm_kernel(const uint16_t *__restrict__ x, int M, int K, int tq, int tr, int G, MxSet set,
+                        float *__restrict__ part)
 {
     extern __shared__ __attribute__((aligned(16))) uint16_t xs[];   // staged chunk [16][kXRow]
     float *red = reinterpret_cast<float *>(xs);                     // then [tile][wave][lane][4]
@@ -104,7 +105,11 @@ void gemv_smallm_kernel(const uint16_t *__restrict__ x, int M, int K, int tq, in
     const int nchunk = (spr + kChunkGroups - 1) / kChunkGroups;
     // the scalars come first in the argument list and arrive preloaded in registers; the tile
     // count is split on the host (tiles = tq * G + tr, G the grid size)
-    const int nb = tq + (blockIdx.x < (unsigned)tr ? 1 : 0);                              // <= TB
+    // SPLIT: workgroup b takes K chunk cw = b / G only, for tile group b % G, and stores fp32
+    // partial sums of that chunk (the reduction over chunks is a second kernel)
+    const int cw = SPLIT ? (int)blockIdx.x / G : 0;
+    const int gid = (int)blockIdx.x - cw * G;
+    const int nb = tq + (gid < tr ? 1 : 0);                                                // <= TB
     const __amdgpu_buffer_rsrc_t rx = rsrc(x, (unsigned)M * (unsigned)K * 2u);
 
     // thread t's share of a chunk: 8 k of every token row; rows past M are outside the buffer
@@ -114,7 +119,7 @@ void gemv_smallm_kernel(const uint16_t *__restrict__ x, int M, int K, int tq, in
     u4v xr[16];
     const int rot = (int)(blockIdx.x & 15);
     auto fetch_x = [&](int c) {
-        const unsigned kc = (unsigned)(c * kChunkK) + 8u * threadIdx.x;
+        const unsigned kc = (unsigned)((c + cw) * kChunkK) + 8u * threadIdx.x;
         const unsigned base = kc < (unsigned)K ? kc * 2u : kOob;
 #pragma unroll
         for (int m = 0; m < 16; ++m)
@@ -127,7 +132,7 @@ void gemv_smallm_kernel(const uint16_t *__restrict__ x, int M, int K, int tq, in
     // then read into scalar registers, so every wave holds them at the cost of a few readlanes
     SmTile tl[TB];
     {
-        const int tile = blockIdx.x + lane * G;
+        const int tile = gid + lane * G;
         const int m1 = set.count > 1 && tile >= set.tile_end[0], m2 = set.count > 2 && tile >= set.tile_end[1],
                   m3 = set.count > 3 && tile >= set.tile_end[2];
         auto sel = [&](auto a0, auto a1, auto a2, auto a3) { return m3 ? a3 : m2 ? a2 : m1 ? a1 : a0; };
@@ -154,8 +159,8 @@ void gemv_smallm_kernel(const uint16_t *__restrict__ x, int M, int K, int tq, in
     // refill past the last chunk) reloads the row's last group, which meets x = 0.
     auto issue = [&](const SmTile &T, int c, SmSlot &sl) {
         const unsigned row = (unsigned)(T.row0 + n);
-        const unsigned gb = (unsigned)min(c * kChunkGroups + 4 * wave + b, spr - 1);
-        const unsigned live = c < nchunk ? (unsigned)T.N : 0u;       // past the last chunk: no range
+        const unsigned gb = (unsigned)min((c + cw) * kChunkGroups + 4 * wave + b, spr - 1);
+        const unsigned live = c + cw < nchunk ? (unsigned)T.N : 0u;  // past the last chunk: no range
         const __amdgpu_buffer_rsrc_t rW = rsrc(T.W, live * (unsigned)wpr * 4u);
         const __amdgpu_buffer_rsrc_t rS = rsrc(T.S, live * (unsigned)spr * 2u);
         // mul24 row products (rows < 2^24) keep the wait counts exact
@@ -248,8 +253,22 @@ void gemv_smallm_kernel(const uint16_t *__restrict__ x, int M, int K, int tq, in
         const float tot = ((v[0] + v[1]) + (v[2] + v[3])) + ((v[4] + v[5]) + (v[6] + v[7]));
         const SmTile &T = (threadIdx.x >> 8) ? tl[t0 + 1 < TB ? t0 + 1 : t0] : tl[t0];
         const int row = T.row0 + rr;
-        if (m < M && row < T.N) T.y[(size_t)m * T.N + row] = f2h_rne(tot);
+        if (m < M && row < T.N) {
+            if constexpr (SPLIT) part[((size_t)cw * M + m) * T.N + row] = tot;
+            else T.y[(size_t)m * T.N + row] = f2h_rne(tot);
+        }
     }
+}
+
+// y[i] = fp16(sum over chunks c = 0, 1, ... of part[c][i]), in that fixed order (i = m * N + n).
+__global__ __launch_bounds__(256) void smallm_reduce_kernel(const float *__restrict__ part, int nchunk, int MN,
+                                                            uint16_t *__restrict__ y)
+{
+    const int i = (int)blockIdx.x * 256 + (int)threadIdx.x;
+    if (i >= MN) return;
+    float acc = part[i];
+    for (int c = 1; c < nchunk; ++c) acc += part[(size_t)c * MN + i];
+    y[i] = f2h_rne(acc);
 }
 
 template <int TB, int D>
@@ -262,18 +281,54 @@ hipError_t launch_sm(const uint16_t *x, const MxSet &set, int M, int K, int tile
         desc->append(desc->empty() ? "" : ";").append(buf);
         return hipSuccess;
     }
-    static const hipError_t attr = hipFuncSetAttribute(reinterpret_cast<const void *>(&gemv_smallm_kernel<TB, D>),
-                                                       hipFuncAttributeMaxDynamicSharedMemorySize, kXBytes);
+    static const hipError_t attr = hipFuncSetAttribute(
+        reinterpret_cast<const void *>(&gemv_smallm_kernel<TB, D, false>), hipFuncAttributeMaxDynamicSharedMemorySize,
+        kXBytes);
     if (attr != hipSuccess) return attr;
     const int grid = (tiles + TB - 1) / TB;
-    hipLaunchKernelGGL((gemv_smallm_kernel<TB, D>), dim3(grid), dim3(64 * kWaves), kXBytes, st, x, M, K,
-                       tiles / grid, tiles % grid, grid, set);
+    hipLaunchKernelGGL((gemv_smallm_kernel<TB, D, false>), dim3(grid), dim3(64 * kWaves), kXBytes, st, x, M, K,
+                       tiles / grid, tiles % grid, grid, set, nullptr);
+    return hipGetLastError();
+}
+
+// K split into its 4096-wide chunks over workgroups: G tile groups per chunk (at most TB tiles of 16
+// rows each), so a workgroup stages one chunk of x instead of all of them; then the reduction.
+template <int TB>
+hipError_t launch_sm_split(const uint16_t *x, const MxSet &set, int M, int K, int tiles, int G, float *part,
+                           hipStream_t st, std::string *desc)
+{
+    static_assert(TB * 256 * kWaves * 4 <= kXBytes, "merge table fits the staging area");
+    const int nchunk = (K + kChunkK - 1) / kChunkK, MN = M * set.N[0];
+    if (desc) {
+        char buf[128];
+        snprintf(buf, sizeof buf, "gemv_smallm_split<%d> grid=%d;smallm_reduce grid=%d", TB, G * nchunk,
+                 (MN + 255) / 256);
+        desc->append(desc->empty() ? "" : ";").append(buf);
+        return hipSuccess;
+    }
+    static const hipError_t attr = hipFuncSetAttribute(
+        reinterpret_cast<const void *>(&gemv_smallm_kernel<TB, 0, true>), hipFuncAttributeMaxDynamicSharedMemorySize,
+        kXBytes);
+    if (attr != hipSuccess) return attr;
+    hipLaunchKernelGGL((gemv_smallm_kernel<TB, 0, true>), dim3(G * nchunk), dim3(64 * kWaves), kXBytes, st, x, M, K,
+                       tiles / G, tiles % G, G, set, part);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    hipLaunchKernelGGL(smallm_reduce_kernel, dim3((MN + 255) / 256), dim3(256), 0, st, part, nchunk, MN, set.y[0]);
     return hipGetLastError();
 }
 
 }  // namespace
 
-hipError_t launch_gemv_smallm(const uint16_t *x, const MxSet &set0, int M, int K, hipStream_t st, std::string *desc)
+size_t smallm_split_bytes(int M, int K, int N)
+{
+    const int nchunk = (K + kChunkK - 1) / kChunkK;
+    if (M < 2 || M > 16 || nchunk < 2 || N < 1) return 0;
+    return ((size_t)nchunk * M * N * 4 + 255) & ~(size_t)255;
+}
+
+hipError_t launch_gemv_smallm(const uint16_t *x, const MxSet &set0, int M, int K, hipStream_t st, std::string *desc,
+                              float *part)
 {
     MxSet set = set0;
     int tiles = 0;
@@ -281,9 +336,25 @@ hipError_t launch_gemv_smallm(const uint16_t *x, const MxSet &set0, int M, int K
         tiles += (set.N[i] + 15) / 16;
         set.tile_end[i] = tiles;
     }
+    const int per = (tiles + 255) / 256, nchunk = (K + kChunkK - 1) / kChunkK;
+    if (part && set.count == 1 && nchunk > 1) {
+        // one chunk per workgroup: as many tile groups per chunk as fill the 256 CUs once (a
+        // workgroup holds a whole chunk of x in LDS, so one fits a CU), at most 8 tiles each
+        int G = 256 / nchunk;
+        if (G < 1) G = 1;
+        if (G > tiles) G = tiles;
+        int tb = (tiles + G - 1) / G;
+        if (tb > 8) {
+            tb = 8;
+            G = (tiles + 7) / 8;
+        }
+        if (tb <= 1) return launch_sm_split<1>(x, set, M, K, tiles, G, part, st, desc);
+        if (tb <= 2) return launch_sm_split<2>(x, set, M, K, tiles, G, part, st, desc);
+        if (tb <= 4) return launch_sm_split<4>(x, set, M, K, tiles, G, part, st, desc);
+        return launch_sm_split<8>(x, set, M, K, tiles, G, part, st, desc);
+    }
     // TB tiles per workgroup: as few as fill the 256 CUs in one round, at most 6 (the grid
     // grows past 256 beyond that); with several K chunks, more chunks per tile are in flight
-    const int per = (tiles + 255) / 256, nchunk = (K + kChunkK - 1) / kChunkK;
     if (nchunk == 1) {
         if (per <= 2) return launch_sm<2, 0>(x, set, M, K, tiles, st, desc);
         if (per <= 4) return launch_sm<4, 0>(x, set, M, K, tiles, st, desc);

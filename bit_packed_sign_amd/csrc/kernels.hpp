@@ -74,8 +74,12 @@ hipError_t launch_gemv(const uint16_t *x, const uint32_t *W, const uint16_t *S, 
                        int M, int K, int N, hipStream_t st, std::string *desc = nullptr);
 // Small-batch product (2 <= M <= 16) on fp16 MFMA with the tokens as the A rows.
 // 2 <= M <= 16 tokens, 1..4 products sharing x (tile_end filled in by the launcher).
+// With `part` (device scratch of smallm_split_bytes(M, K, N[0]) bytes) a one-matrix product with
+// K > 4096 splits K over workgroups: fp32 partial sums per 4096-wide chunk, then a reduction.
 hipError_t launch_gemv_smallm(const uint16_t *x, const MxSet &set, int M, int K, hipStream_t st,
-                              std::string *desc = nullptr);
+                              std::string *desc = nullptr, float *part = nullptr);
+// Scratch bytes of the split-K small-batch product (0 when the shape does not split).
+size_t smallm_split_bytes(int M, int K, int N);
 hipError_t launch_prefill(const uint16_t *x, const uint32_t *W, const uint16_t *S, uint16_t *y,
                           int M, int K, int N, hipStream_t st, std::string *desc = nullptr);
 // Ternary weights in 2-bit slots: T uint32 [N][K/16].
@@ -94,5 +98,12 @@ hipError_t launch_xor_patch_multi(uint32_t *const *Wtab, const int32_t *Ktab, co
 
 // Streaming read of `bytes` (multiple of 16) into a per-wave digest sink[4 * grid].
 hipError_t launch_stream_read(const void *buf, size_t bytes, uint32_t *sink, int grid, int unroll, hipStream_t st);
+
+// Shared by the entry points (defined with the C ABI's validation): the thread-local error text,
+// and bin1_gemv with a scratch area for the split-K path (caller_ws: a caller's workspace, checked
+// like its other pointers; otherwise the library's own static array).
+int set_error(int status, const char *what);
+int gemv_scratch(const char *fn, const void *x, const uint32_t *Wbits, const void *scales, void *y, int M, int K,
+                 int N, void *ws, size_t ws_bytes, bool caller_ws, void *stream);
 
 }  // namespace bin1

@@ -93,6 +93,24 @@ int bin1_gemv_group(const void *x, int count, const uint32_t *const *Wbits,
                     const void *const *scales, void *const *y, const int *N,
                     int M, int K, void *stream);
 
+/* The product of bin1_gemv with a caller-owned scratch area, which lets long small-batch products
+ * split K over workgroups.  With 2 <= M <= 16 tokens every workgroup must bring the activations of
+ * its K range into on-chip memory, and for K > 4096 that dwarfs its share of the weights; with
+ * the workspace each workgroup stages one 4096-wide chunk of x for more rows, stores fp32 partial
+ * sums per chunk in the workspace, and a second kernel adds the chunks in a fixed order (chunk 0,
+ * 1, ...) and rounds once to fp16.  Decode speed is bounded by bandwidth over weight bytes
+ * ["Bonsai 27B" page, section "Low-bit kernels for hybrid attention"]; this keeps the per-CU
+ * activation stream below the weight stream.
+ * workspace: device memory, 256-byte aligned, at least bin1_gemv_workspace_bytes(M, K, N) bytes,
+ * not overlapping x, Wbits, scales or y; it holds nothing between calls (no clearing needed), but
+ * two calls in flight at once must not share it.  When that size is 0 (the shape takes no split
+ * path) workspace may be NULL and the call is bin1_gemv.  Results equal bin1_gemv's within the
+ * parity bar (the summation order differs); errors as bin1_gemv, plus BIN1_ERR_NULL / _SHAPE /
+ * _ALIGN / _ALIAS for a missing, short, misaligned or overlapping workspace. */
+size_t bin1_gemv_workspace_bytes(int M, int K, int N);
+int bin1_gemv_ws(const void *x, const uint32_t *Wbits, const void *scales, void *y, int M, int K, int N,
+                 void *workspace, size_t workspace_bytes, void *stream);
+
 /* Prefill product, same arguments and result as bin1_gemv; tuned for M >= 256 (the
  * pages note that prompt processing is compute-bound: ["Bonsai 27B", section "Low-bit
  * kernels for hybrid attention"]).  Bit tiles are unpacked into LDS as fp16 +-scale
@@ -237,7 +255,8 @@ int bin1_stream_read(const void *buf, size_t bytes, uint32_t *sink, int grid, in
 /* Diagnostic: the kernel variant(s) and grid that a product call would launch for these shapes,
  * from the same dispatch code the calls run (nothing is launched; no device is needed).
  * op: 0 = bin1_gemv (count == 1) or bin1_gemv_group, 1 = bin1_gemv_t2 or bin1_gemv_group_t2,
- * 2 = bin1_gemm_prefill, 3 = bin1_gemm_prefill_t2 (count == 1 for 2 and 3).  N: host int[count],
+ * 2 = bin1_gemm_prefill, 3 = bin1_gemm_prefill_t2, 4 = bin1_gemv_ws given a large enough
+ * workspace (count == 1 for 2, 3 and 4).  N: host int[count],
  * the row counts as the call would launch them (matrices a group call runs as one taller matrix
  * are given as one).  Writes a NUL-terminated text such as "gemv_mx<1,1,1,0,0,4,1> grid=384" into
  * name (len bytes; launches separated by ';').  Requires M >= 1, K >= 128, K % 128 == 0 and

@@ -166,3 +166,23 @@ def test_binding_rejects_cpu_tensors():
         b1.gemv(x, W, S)
     with pytest.raises(ValueError):
         b1.xor_patch_apply(W, torch.zeros(1, dtype=torch.int32))
+
+
+def test_workspace_product_validation(L):
+    """bin1_gemv_ws: the workspace query, and a missing, short, misaligned or overlapping
+    workspace rejected before anything is touched (fake addresses, never dereferenced)."""
+    L.bin1_gemv_workspace_bytes.restype = ctypes.c_size_t
+    need = L.bin1_gemv_workspace_bytes(16, 12288, 4096)
+    assert need == 3 * 16 * 4096 * 4
+    assert L.bin1_gemv_workspace_bytes(1, 12288, 4096) == 0          # batch 1: no split
+    assert L.bin1_gemv_workspace_bytes(16, 4096, 4096) == 0          # one chunk: no split
+    assert L.bin1_gemv_workspace_bytes(16, 100, 4096) == 0           # invalid shape
+    f = L.bin1_gemv_ws
+    x, W, S, y, ws = 0x10000000, 0x20000000, 0x30000000, 0x40000000, 0x50000000
+    assert f(x, W, S, y, 16, 12288, 4096, None, 0, None) == -1
+    assert f(x, W, S, y, 16, 12288, 4096, ws, need - 1, None) == -2
+    assert f(x, W, S, y, 16, 12288, 4096, ws + 16, need, None) == -3
+    assert f(x, W, S, y, 16, 12288, 4096, y - 256, need, None) == -4   # covers y
+    assert f(x, W, S, y, 16, 12288, 4096, W, need, None) == -4         # covers the weights
+    assert f(x, W, S, y, 0, 12288, 4096, None, 0, None) == 0           # no outputs: nothing to do
+

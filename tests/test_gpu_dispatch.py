@@ -54,6 +54,12 @@ def test_dispatch_branch_matches_oracle(orc, dev, case):
     outs = [ybuf[a:a + M * N].view(M, N) for a, N in zip(starts, Ns)]
     if op.startswith("prefill"):
         (b1.gemm_prefill_t2 if t2 else b1.gemm_prefill)(xd, Wd[0], Sd[0], out=outs[0])
+    elif op == "gemv_ws":
+        need = b1.gemv_workspace_bytes(M, K, Ns[0])
+        ws = torch.full((need + 512,), 0xFF, dtype=torch.uint8, device=dev)   # stale bytes: fully overwritten
+        b1.gemv_ws(xd, Wd[0], Sd[0], workspace=ws[256:256 + need] if need else None, out=outs[0])
+        if need:                                # the bytes around the workspace are untouched
+            assert bool((ws[:256] == 0xFF).all()) and bool((ws[256 + need:] == 0xFF).all())
     elif len(Ns) == 1:
         (b1.gemv_t2 if t2 else b1.gemv)(xd, Wd[0], Sd[0], out=outs[0])
     else:

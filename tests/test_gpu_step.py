@@ -6,8 +6,8 @@ captured into a HIP graph and replayed.
 * the 27B step (256 stages, 448 products), every output; its fused q|k|v (15360 x 5120) and
   gate|up (34816 x 5120) launches are the variants the benchmark runs for it;
 * the ternary 8B step (2-bit slots), every output;
-* the 8B MLP at batch 16 (72 stages on the small-batch kernel), all 16 tokens of every eighth row
-  plus the edge rows of every product.
+* the 8B MLP at batch 16 (72 stages on the small-batch kernel; down splits K over workgroups with
+  the step's workspace), all 16 tokens of every eighth row plus the edge rows of every product.
 Every replay must reproduce the eager outputs bit for bit, with eager work between replays.
 Concurrent calls on two streams give the same outputs as one stream."""
 import numpy as np
@@ -39,7 +39,7 @@ def _check_step(orc, dev, wl, ternary, row_stride, expect_variants=None):
     if expect_variants:
         for s, want in expect_variants.items():
             x, Ws, Ss, ys, _ = step.stages[s]
-            op = "gemv_t2" if ternary else "gemv"
+            op = "gemv_t2" if ternary else "gemv_ws" if step.workspace is not None and len(Ws) == 1 else "gemv"
             got = b1.kernel_variant(op, wl.M, x.shape[1], [sum(W.shape[0] for W in Ws)] if wl.M == 1
                                     else [W.shape[0] for W in Ws])
             assert got.split(" ")[0] == want, (s, got, want)
@@ -96,7 +96,7 @@ def test_step_ternary_8b_every_output(orc, dev):
 
 def test_step_mlp16_every_product(orc, dev):
     _check_step(orc, dev, synth.mlp_8b_m16(), False, 8,
-                {0: "gemv_smallm<6,0>", 1: "gemv_smallm<1,4>"})
+                {0: "gemv_smallm<6,0>", 1: "gemv_smallm_split<4>"})
 
 
 def test_concurrent_streams_match_one_stream(dev):

@@ -22,7 +22,10 @@ def test_query_names_the_expected_variant(b1, case):
     op, M, K, Ns, expect, _ = case
     got = b1.kernel_variant(op, M, K, Ns)
     assert got.split(" ")[0] == expect, (got, expect)
-    assert ";" not in got                      # one launch for the whole call
+    if "split" in expect:                       # the partial-sum kernel, then the chunk reduction
+        assert got.count(";") == 1 and got.split(";")[1].startswith("smallm_reduce")
+    else:
+        assert ";" not in got                   # one launch for the whole call
 
 
 def test_every_decode_branch_is_reached():

@@ -81,7 +81,19 @@ PREFILL_CASES = [
     ("prefill_t2", 2048, 1024, [12288], "prefill<256,2,2,1,1>", "large"),
 ]
 
-ALL_CASES = DECODE_CASES + DECODE_T2_CASES + SELECT_CASES + SMALLM_CASES + PREFILL_CASES
+# small batch with a workspace: K split into 4096-wide chunks over workgroups (G tile groups per
+# chunk, TB tiles each) then the chunk reduction; shapes without a split run as bin1_gemv
+WS_CASES = [
+    ("gemv_ws", 16, 12288, [4096], "gemv_smallm_split<4>", "down"),
+    ("gemv_ws", 2, 8192, [300], "gemv_smallm_split<1>", "ragged"),
+    ("gemv_ws", 5, 20480, [5000], "gemv_smallm_split<8>", "tb8"),
+    ("gemv_ws", 16, 17408, [5120], "gemv_smallm_split<8>", "down27b"),
+    ("gemv_ws", 9, 4224, [1000], "gemv_smallm_split<1>", "partial"),
+    ("gemv_ws", 16, 4096, [4096], "gemv_smallm<2,0>", "nosplit"),
+    ("gemv_ws", 1, 12288, [4096], "gemv_mx<1,1,1,0,0,12,1>", "m1"),
+]
+
+ALL_CASES = DECODE_CASES + DECODE_T2_CASES + SELECT_CASES + SMALLM_CASES + PREFILL_CASES + WS_CASES
 
 
 def case_id(c):
