@@ -45,6 +45,7 @@ _SIGS = {
     "bin1_kernel_variant": [_i, _i, _i, _i, _p, _p, _i],
     "bin1_gemv_workspace_bytes": [_i, _i, _i],
     "bin1_gemv_ws": [_p, _p, _p, _p, _i, _i, _i, _p, ctypes.c_size_t, _p],
+    "bin1_gemv_noalloc": [_p, _p, _p, _p, _i, _i, _i, _p],
     "bin1_status_string": [_i],
     "bin1_last_error": [],
     "bin1_abi_version": [],
@@ -175,6 +176,12 @@ def gemv_ws(x: torch.Tensor, Wbits: torch.Tensor, scales: torch.Tensor, workspac
         _need(workspace, "workspace", (torch.uint8,), 1)
         wp, wb = workspace.data_ptr(), workspace.numel()
     return _product_ws("bin1_gemv_ws", x, Wbits, scales, out, wp or None, wb)
+
+
+def gemv_noalloc(x: torch.Tensor, Wbits: torch.Tensor, scales: torch.Tensor, out: Optional[torch.Tensor] = None):
+    """:func:`gemv_ws` on the library's own 4 MiB scratch per GPU (no workspace argument; calls
+    overlapping in time on one GPU race).  Only the output is allocated here, when not given."""
+    return _product("bin1_gemv_noalloc", x, Wbits, scales, out)
 
 
 def _product_ws(fn, x, Wbits, scales, out, wp, wb):

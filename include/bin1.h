@@ -111,6 +111,18 @@ size_t bin1_gemv_workspace_bytes(int M, int K, int N);
 int bin1_gemv_ws(const void *x, const uint32_t *Wbits, const void *scales, void *y, int M, int K, int N,
                  void *workspace, size_t workspace_bytes, void *stream);
 
+/* For callers that cannot allocate device memory (code under HIP graph capture, tight serving
+ * loops, harnesses that forbid hipMalloc): bin1_gemv_ws with the library's own scratch instead of
+ * a caller's workspace.  The scratch is a static device array of 4 MiB that every GPU the library
+ * runs on holds until the process ends; its device address is looked up on the first call on each
+ * device (so make that first call outside a capture).  Shapes whose workspace
+ * (bin1_gemv_workspace_bytes) exceeds 4 MiB return BIN1_ERR_SHAPE before anything is enqueued.
+ * All calls on one GPU share that GPU's array: calls that overlap in time on one GPU (on different
+ * streams without ordering between them) race; calls ordered on one stream do not.  Nothing has to
+ * be cleared between calls.  Results are bit-identical to bin1_gemv_ws on the same inputs. */
+int bin1_gemv_noalloc(const void *x, const uint32_t *Wbits, const void *scales, void *y, int M, int K, int N,
+                      void *stream);
+
 /* Prefill product, same arguments and result as bin1_gemv; tuned for M >= 256 (the
  * pages note that prompt processing is compute-bound: ["Bonsai 27B", section "Low-bit
  * kernels for hybrid attention"]).  Bit tiles are unpacked into LDS as fp16 +-scale
