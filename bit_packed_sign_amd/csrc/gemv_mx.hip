@@ -170,7 +170,7 @@ struct Slot {
     uint16_t s1[R][SP];
 };
 
-template <int SP, int P, int R, bool ODD, bool T2, int NW, bool TWO>
+template <int SP, int P, int R, bool ODD, bool T2, int NW, bool TWO, int TT>
 __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(NW / 4, 4)))
 void gemv_mx_kernel(const uint16_t *__restrict__ x, int Ktq, int trg, const uint32_t *W0, const uint16_t *S0,
                     const uint32_t *W1, const uint16_t *S1, int N0, int N1, MxSet set)
@@ -181,6 +181,12 @@ void gemv_mx_kernel(const uint16_t *__restrict__ x, int Ktq, int trg, const uint
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);      // wave-uniform
     const int n = lane & 15, g = lane >> 4;
+    // TT groups of NWP waves: wave group tt takes the workgroup's tiles tt, tt + TT, ..., and
+    // wave wp of a group the 1024-wide pairs wp, wp + NWP, ... of each; all waves share one
+    // conversion of x to limbs (so a CU converts x once for all its tiles)
+    static_assert(NW % TT == 0 && (NW / TT) % 4 == 0 && (TT == 1 || TWO), "wave groups of 4k waves");
+    constexpr int NWP = NW / TT;
+    const int tt = wave / NWP, wp = wave - tt * NWP;                 // wave-uniform
     constexpr int NT = 64 * NW;                      // threads
     const int npair = (K + 1023) >> 10, nseg = 2 * npair;
     const int wpr = T2 ? K >> 4 : K >> 5, spr = K >> 7;   // words per row: 16 or 32 weights each
@@ -208,7 +214,7 @@ void gemv_mx_kernel(const uint16_t *__restrict__ x, int Ktq, int trg, const uint
             const bool rok = row < N;
 #pragma unroll
             for (int q = 0; q < SP; ++q) {
-                const int gam = 8 * (wave + NW * q) + 2 * g;    // this lane's first group
+                const int gam = 8 * (wp + NWP * q) + 2 * g;     // this lane's first group
                 const bool ok0 = rok && gam < spr, ok1 = rok && gam + 1 < spr;
                 const unsigned ow = (mul24((unsigned)row, (unsigned)wpr) + (unsigned)kGW * gam) * 4u;
                 const unsigned os = (mul24((unsigned)row, (unsigned)spr) + gam) * 2u;
@@ -244,7 +250,7 @@ void gemv_mx_kernel(const uint16_t *__restrict__ x, int Ktq, int trg, const uint
     if constexpr (TWO) {
         tab = tile_tab2<R>(W0, S0, N0, te0, W1, S1, N1, blockIdx.x + lane * grid);
 #pragma unroll
-        for (int p = 0; p < P; ++p) issue(tab, p, ring[p]);
+        for (int p = 0; p < P; ++p) issue(tab, tt + TT * p, ring[p]);
         limbs_fill<NT>(K, lds);
     } else {
         // only the scalars are chosen under the (uniform) branch: one issue after it, so no
@@ -284,8 +290,8 @@ void gemv_mx_kernel(const uint16_t *__restrict__ x, int Ktq, int trg, const uint
     for (int q = 0; q < SP; ++q)
 #pragma unroll
         for (int h = 0; h < 2; ++h) {
-            const int sigma = 2 * (wave + NW * q) + h;
-            const bool v = wave + NW * q < npair;
+            const int sigma = 2 * (wp + NWP * q) + h;
+            const bool v = wp + NWP * q < npair;
             const uint8_t *blk = lds + (v ? sigma : 0) * 4 * kBlk;
 #pragma unroll
             for (int t = 0; t < 4; ++t) A[q][h][t] = load_a(blk + t * kBlk, lo, hi);
@@ -293,19 +299,20 @@ void gemv_mx_kernel(const uint16_t *__restrict__ x, int Ktq, int trg, const uint
         }
 
     // Main loop: no cross-wave synchronisation.  Each wave streams its K-slice of every tile
-    // of this workgroup and parks its partial row sums in LDS; one barrier at the end merges
-    // the four slices and writes y with coalesced stores.
-    for (int it0 = 0; it0 < my_tiles; it0 += P) {
+    // of its group and parks its partial row sums in LDS; one barrier at the end merges the
+    // slices and writes y with coalesced stores.  Local tile j of the group is the workgroup's
+    // tile tt + TT j.
+    for (int j0 = 0; tt + TT * j0 < my_tiles; j0 += P) {
 #pragma unroll
         for (int p = 0; p < P; ++p) {
-            const int it = it0 + p;
+            const int it = tt + TT * (j0 + p);
             if (it >= my_tiles) goto done;            // uniform; the slots left hold dead loads
             float acc[R];
 #pragma unroll
             for (int r = 0; r < R; ++r) acc[r] = 0.f;
 #pragma unroll
             for (int q = 0; q < SP; ++q) {
-                const int pr = wave + NW * q;
+                const int pr = wp + NWP * q;
                 if (pr < npair) {                     // wave-uniform
                     const int gam = 8 * pr + 2 * g;
 #pragma unroll
@@ -314,36 +321,49 @@ void gemv_mx_kernel(const uint16_t *__restrict__ x, int Ktq, int trg, const uint
                         const float s0 = h2f((uint16_t)(sv & 0xFFFFu));
                         const float s1 = ODD ? h2f(ring[p].s1[r][q])
                                              : (gam + 1 < spr ? h2f((uint16_t)(sv >> 16)) : 0.f);
-#pragma unroll
-                        for (int h = 0; h < 2; ++h) {
-                            float4v c = {0.f, 0.f, 0.f, 0.f};
-                            if constexpr (T2) {
-                                // MFMA t takes the group's words 2t and 2t + 1 (32 weights)
-                                const u4v w0 = ring[p].w[r][q][h][0], w1 = ring[p].w[r][q][h][T2 ? 1 : 0];
-                                c = mma_b<0>(A[q][h][0], unpack_t2(w0.x, w0.y), scA[q][h], c);
-                                c = mma_b<1>(A[q][h][1], unpack_t2(w0.z, w0.w), scA[q][h], c);
-                                c = mma_b<2>(A[q][h][2], unpack_t2(w1.x, w1.y), scA[q][h], c);
-                                c = mma_b<3>(A[q][h][3], unpack_t2(w1.z, w1.w), scA[q][h], c);
-                                acc[r] = fmaf(h ? s1 : s0, (c[0] + c[1]) + (c[2] + c[3]), acc[r]);
-                            } else {
-                                const u4v w = ring[p].w[r][q][h][0];
-                                c = mma<0>(A[q][h][0], w.x, scA[q][h], c);
-                                c = mma<1>(A[q][h][1], w.y, scA[q][h], c);
-                                c = mma<2>(A[q][h][2], w.z, scA[q][h], c);
-                                c = mma<3>(A[q][h][3], w.w, scA[q][h], c);
-                                // B held -w, so the group's partial is -(c0+c1+c2+c3)
-                                acc[r] = fmaf(-(h ? s1 : s0), (c[0] + c[1]) + (c[2] + c[3]), acc[r]);
-                            }
+                        // the two segments' chains of four products each, interleaved (independent
+                        // accumulators keep the matrix pipe busy); group partials added in segment order
+                        float4v ca = {0.f, 0.f, 0.f, 0.f}, cb = {0.f, 0.f, 0.f, 0.f};
+                        if constexpr (T2) {
+                            // MFMA t takes the group's words 2t and 2t + 1 (32 weights)
+                            const u4v a0 = ring[p].w[r][q][0][0], a1 = ring[p].w[r][q][0][T2 ? 1 : 0];
+                            const u4v b0 = ring[p].w[r][q][1][0], b1 = ring[p].w[r][q][1][T2 ? 1 : 0];
+                            ca = mma_b<0>(A[q][0][0], unpack_t2(a0.x, a0.y), scA[q][0], ca);
+                            cb = mma_b<0>(A[q][1][0], unpack_t2(b0.x, b0.y), scA[q][1], cb);
+                            ca = mma_b<1>(A[q][0][1], unpack_t2(a0.z, a0.w), scA[q][0], ca);
+                            cb = mma_b<1>(A[q][1][1], unpack_t2(b0.z, b0.w), scA[q][1], cb);
+                            ca = mma_b<2>(A[q][0][2], unpack_t2(a1.x, a1.y), scA[q][0], ca);
+                            cb = mma_b<2>(A[q][1][2], unpack_t2(b1.x, b1.y), scA[q][1], cb);
+                            ca = mma_b<3>(A[q][0][3], unpack_t2(a1.z, a1.w), scA[q][0], ca);
+                            cb = mma_b<3>(A[q][1][3], unpack_t2(b1.z, b1.w), scA[q][1], cb);
+                            acc[r] = fmaf(s0, (ca[0] + ca[1]) + (ca[2] + ca[3]), acc[r]);
+                            acc[r] = fmaf(s1, (cb[0] + cb[1]) + (cb[2] + cb[3]), acc[r]);
+                        } else {
+                            const u4v wa = ring[p].w[r][q][0][0], wb = ring[p].w[r][q][1][0];
+                            ca = mma<0>(A[q][0][0], wa.x, scA[q][0], ca);
+                            cb = mma<0>(A[q][1][0], wb.x, scA[q][1], cb);
+                            ca = mma<1>(A[q][0][1], wa.y, scA[q][0], ca);
+                            cb = mma<1>(A[q][1][1], wb.y, scA[q][1], cb);
+                            ca = mma<2>(A[q][0][2], wa.z, scA[q][0], ca);
+                            cb = mma<2>(A[q][1][2], wb.z, scA[q][1], cb);
+                            ca = mma<3>(A[q][0][3], wa.w, scA[q][0], ca);
+                            cb = mma<3>(A[q][1][3], wb.w, scA[q][1], cb);
+                            // B held -w, so a group's partial is -(c0+c1+c2+c3)
+                            acc[r] = fmaf(-s0, (ca[0] + ca[1]) + (ca[2] + ca[3]), acc[r]);
+                            acc[r] = fmaf(-s1, (cb[0] + cb[1]) + (cb[2] + cb[3]), acc[r]);
                         }
                     }
                 }
             }
-            issue(tab, it + P, ring[p]);
-            float *rb = red + it * (16 * NW * R);     // [tile][16R rows][NW waves]
+            // refill the slot with the group's tile P further on; with a one-slot ring only when
+            // there is one (the branch is uniform, and nothing after it waits on other loads)
+            const int nxt = tt + TT * (j0 + p + P);
+            if (P > 1 || nxt < my_tiles) issue(tab, nxt, ring[p]);
+            float *rb = red + it * (16 * NWP * R);    // [tile][16R rows][NWP waves]
 #pragma unroll
             for (int r = 0; r < R; ++r) {
                 const float v = sum_groups(acc[r]);
-                if (lane < 16) rb[(16 * r + lane) * NW + wave] = v;
+                if (lane < 16) rb[(16 * r + lane) * NWP + wp] = v;
             }
         }
     }
@@ -359,11 +379,11 @@ done:
         const int row = __shfl(tab.row0, it, kWave) + j, N = __shfl(tab.N, it, kWave);
         const unsigned long long yp = ((unsigned long long)(unsigned)__shfl((unsigned)(tab.y >> 32), it, kWave) << 32) |
                                       (unsigned)__shfl((unsigned)tab.y, it, kWave);
-        const float4v pr4 = *reinterpret_cast<const float4v *>(red + e * NW);
+        const float4v pr4 = *reinterpret_cast<const float4v *>(red + e * NWP);
         float tot = (pr4[0] + pr4[1]) + (pr4[2] + pr4[3]);
 #pragma unroll
-        for (int v = 4; v < NW; v += 4) {             // waves 4.. of a wider workgroup
-            const float4v prv = *reinterpret_cast<const float4v *>(red + e * NW + v);
+        for (int v = 4; v < NWP; v += 4) {            // waves 4.. of a wider pair split
+            const float4v prv = *reinterpret_cast<const float4v *>(red + e * NWP + v);
             tot += (prv[0] + prv[1]) + (prv[2] + prv[3]);
         }
         if (row < N) reinterpret_cast<uint16_t *>(yp)[row] = f2h_rne(tot);
@@ -379,9 +399,10 @@ constexpr size_t shm_bytes(int K, int rows_per_wg, int NW)
     return (size_t)(2 * ((K + 1023) >> 10)) * (4 * kBlk + 64) + (size_t)rows_per_wg * NW * 4;
 }
 
-template <int SP, int P, int R, bool ODD, bool T2, int NW, bool TWO>
+template <int SP, int P, int R, bool ODD, bool T2, int NW, bool TWO, int TT>
 hipError_t launch_mx_t(const uint16_t *x, const MxSet &set0, int K, hipStream_t st, std::string *desc)
 {
+    constexpr int NWP = NW / TT;
     MxSet set = set0;
     int tiles = 0;
     for (int i = 0; i < set.count; ++i) {
@@ -389,40 +410,48 @@ hipError_t launch_mx_t(const uint16_t *x, const MxSet &set0, int K, hipStream_t 
         set.tile_end[i] = tiles;
     }
     // Resident workgroups per CU follow the register budget (A operands dominate it: three
-    // fit at one pair per wave, two at two); the grid grows past that only when a workgroup's
-    // rows would overflow the merge table.
-    const int cap = NW == 4 ? (SP == 1 ? 3 * 256 : SP == 2 ? 2 * 256 : 256) : (NW == 8 && SP == 1 ? 2 * 256 : 256);
+    // fit at one pair per wave, two at two); a workgroup of several wave groups fills a CU by
+    // itself.  The grid grows past that only when a workgroup's rows would overflow the merge
+    // table.
+    const int cap = TT > 1 ? 256
+                  : NW == 4 ? (SP == 1 ? 3 * 256 : SP == 2 ? 2 * 256 : 256) : (NW == 8 && SP == 1 ? 2 * 256 : 256);
     // tiles per workgroup: at most what the merge table holds and the one-per-lane tile table
     constexpr int kMaxT = kMaxTileRows / (16 * R) < 64 ? kMaxTileRows / (16 * R) : 64;
-    const int need = (tiles + kMaxT - 1) / kMaxT;
-    const int grid = tiles < cap ? tiles : (need > cap ? need : cap);
+    const int need = (tiles + kMaxT - 1) / kMaxT, units = (tiles + TT - 1) / TT;
+    const int grid = units < cap ? units : (need > cap ? need : cap);
     const int rows_per_wg = (tiles + grid - 1) / grid * 16 * R;
     const bool two = set.count == 2;
     if (desc) {                                        // describe the launch instead of making it
         char buf[128];
-        snprintf(buf, sizeof buf, "gemv_mx<%d,%d,%d,%d,%d,%d,%d> grid=%d", SP, P, R, (int)ODD, (int)T2, NW,
-                 (int)TWO, grid);
+        if (TT > 1)
+            snprintf(buf, sizeof buf, "gemv_mx<%d,%d,%d,%d,%d,%d,%d,%d> grid=%d", SP, P, R, (int)ODD, (int)T2, NW,
+                     (int)TWO, TT, grid);
+        else
+            snprintf(buf, sizeof buf, "gemv_mx<%d,%d,%d,%d,%d,%d,%d> grid=%d", SP, P, R, (int)ODD, (int)T2, NW,
+                     (int)TWO, grid);
         desc->append(desc->empty() ? "" : ";").append(buf);
         return hipSuccess;
     }
     static const hipError_t attr = hipFuncSetAttribute(
-        reinterpret_cast<const void *>(&gemv_mx_kernel<SP, P, R, ODD, T2, NW, TWO>),
+        reinterpret_cast<const void *>(&gemv_mx_kernel<SP, P, R, ODD, T2, NW, TWO, TT>),
         hipFuncAttributeMaxDynamicSharedMemorySize,
-        (int)std::min<size_t>(shm_bytes(kMaxPairs * 1024, kMaxTileRows, NW), kMaxLds));
+        (int)std::min<size_t>(shm_bytes(kMaxPairs * 1024, kMaxTileRows, NWP), kMaxLds));
     if (attr != hipSuccess) return attr;
-    hipLaunchKernelGGL((gemv_mx_kernel<SP, P, R, ODD, T2, NW, TWO>), dim3(grid), dim3(64 * NW),
-                       shm_bytes(K, rows_per_wg, NW), st, x, K | (tiles / grid) << 16, (tiles % grid) | grid << 16,
+    hipLaunchKernelGGL((gemv_mx_kernel<SP, P, R, ODD, T2, NW, TWO, TT>), dim3(grid), dim3(64 * NW),
+                       shm_bytes(K, rows_per_wg, NWP), st, x, K | (tiles / grid) << 16, (tiles % grid) | grid << 16,
                        set.W[0], set.S[0], two ? set.W[1] : nullptr, two ? set.S[1] : nullptr, set.N[0],
                        two ? set.N[1] : 0, set);
     return hipGetLastError();
 }
 
-// Launches of at most two matrices take their whole tile table from scalar arguments.
-template <int SP, int P, int R, bool ODD, bool T2, int NW = 4>
+// Launches of at most two matrices take their whole tile table from scalar arguments; several
+// wave groups per workgroup (TT > 1) need that table, so three or four matrices fall back to one
+// group of NW / TT waves.
+template <int SP, int P, int R, bool ODD, bool T2, int NW = 4, int TT = 1>
 hipError_t launch_mx(const uint16_t *x, const MxSet &set, int K, hipStream_t st, std::string *desc)
 {
-    return set.count <= 2 ? launch_mx_t<SP, P, R, ODD, T2, NW, true>(x, set, K, st, desc)
-                          : launch_mx_t<SP, P, R, ODD, T2, NW, false>(x, set, K, st, desc);
+    if (set.count <= 2) return launch_mx_t<SP, P, R, ODD, T2, NW, true, TT>(x, set, K, st, desc);
+    return launch_mx_t<SP, P, R, ODD, T2, NW / TT, false, 1>(x, set, K, st, desc);
 }
 
 template <bool ODD, bool T2>
@@ -443,9 +472,12 @@ hipError_t dispatch_mx(const uint16_t *x, const MxSet &set, int K, hipStream_t s
     const int cap = SP == 1 ? 3 * 256 : SP == 2 ? 2 * 256 : 256;
     const bool one16 = t16 <= cap, one = t32 <= cap, few16 = t16 <= 3 * cap;
     switch (SP) {
+    // Past one tile per workgroup, one workgroup per CU of three groups of four waves: x is
+    // loaded and converted once per CU instead of once per co-resident workgroup.
     case 1: return one16 ? launch_mx<1, 1, 1, ODD, T2>(x, set, K, st, desc)
-                 : one   ? launch_mx<1, 1, 2, ODD, T2>(x, set, K, st, desc)
-                 : few16 ? launch_mx<1, 3, 1, ODD, T2>(x, set, K, st, desc) : launch_mx<1, 2, 2, ODD, T2>(x, set, K, st, desc);
+                 : one   ? launch_mx<1, 1, 2, ODD, T2, 12, 3>(x, set, K, st, desc)
+                 : few16 ? launch_mx<1, 3, 1, ODD, T2>(x, set, K, st, desc)
+                         : launch_mx<1, 2, 2, ODD, T2, 12, 3>(x, set, K, st, desc);
     // One 16-row tile per workgroup: as many waves as pairs (up to 16), one pair each, so no wave
     // carries a second pair on the critical path (the wider workgroups fit fewer per CU).
     case 2: return one16 ? launch_mx<1, 1, 1, ODD, T2, 8>(x, set, K, st, desc)

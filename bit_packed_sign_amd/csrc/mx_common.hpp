@@ -31,13 +31,18 @@ constexpr int kZero = 512;         // offset of the zero bytes inside a block
 
 // fp4 (e2m1) expansion of one word: nibble q of register v = 0x2 | bit(4q+v) << 3,
 // i.e. -1.0 for a set bit and +1.0 for a clear one (the sign is undone by the caller).
+// Each register is one shift and one v_and_or_b32 (gfx9 encodes no literal in a three-operand
+// instruction, and reads at most one scalar register: the mask comes from a scalar register, the
+// +1.0 pattern from a vector one).
 __device__ __forceinline__ int8v unpack_fp4(uint32_t w)
 {
+    const uint32_t sign = __builtin_amdgcn_readfirstlane(0x88888888u);
+    const uint32_t one = 0x22222222u;
     int8v b;
-    b[0] = (int)(((w << 3) & 0x88888888u) | 0x22222222u);
-    b[1] = (int)(((w << 2) & 0x88888888u) | 0x22222222u);
-    b[2] = (int)(((w << 1) & 0x88888888u) | 0x22222222u);
-    b[3] = (int)((w & 0x88888888u) | 0x22222222u);
+    asm("v_and_or_b32 %0, %1, %2, %3" : "=v"(b[0]) : "v"(w << 3), "s"(sign), "v"(one));
+    asm("v_and_or_b32 %0, %1, %2, %3" : "=v"(b[1]) : "v"(w << 2), "s"(sign), "v"(one));
+    asm("v_and_or_b32 %0, %1, %2, %3" : "=v"(b[2]) : "v"(w << 1), "s"(sign), "v"(one));
+    asm("v_and_or_b32 %0, %1, %2, %3" : "=v"(b[3]) : "v"(w), "s"(sign), "v"(one));
     b[4] = b[5] = b[6] = b[7] = 0;
     return b;
 }

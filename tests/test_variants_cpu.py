@@ -37,7 +37,7 @@ def test_every_decode_branch_is_reached():
             core = exp.split("<")[1].rstrip(">").split(",")
             branch = tuple(core[i] for i in (0, 1, 2, 5))   # SP, P, R, NW
             seen.setdefault(branch, set()).add((kind, core[3], core[6]))
-        expected_branches = 4 + 4 + 3 + 2 + 1
+        expected_branches = 6 + 4 + 3 + 2 + 1          # SP 1: the two three-or-four-matrix fallbacks too
         assert len(seen) == expected_branches, sorted(seen)
         for branch, kinds in seen.items():
             assert {k for k, _, _ in kinds} == {"even", "odd", "part"}, (branch, kinds)

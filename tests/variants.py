@@ -23,8 +23,9 @@ SP_K = {
 }
 
 
-def _mx(sp, p, r, odd, t2, nw, two):
-    return f"gemv_mx<{sp},{p},{r},{int(odd)},{int(t2)},{nw},{int(two)}>"
+def _mx(sp, p, r, odd, t2, nw, two, tt=1):
+    tail = f",{tt}" if tt > 1 else ""
+    return f"gemv_mx<{sp},{p},{r},{int(odd)},{int(t2)},{nw},{int(two)}{tail}>"
 
 
 def _decode_cases(t2):
@@ -35,9 +36,11 @@ def _decode_cases(t2):
         odd = (K // 128) % 2 == 1
         # (Ns, expected (SP, P, R, NW)) per branch of this pairs-per-wave class
         if sp == 1:
-            branches = [([100], (1, 1, 1, 4)), ([20000], (1, 1, 2, 4)), ([30000], (1, 3, 1, 4)),
-                        ([40000], (1, 2, 2, 4)), ([100, 200, 300], (1, 1, 1, 4)),
-                        ([10000, 10000, 10000], (1, 3, 1, 4))]
+            # past one tile per workgroup, three groups of four waves per workgroup (TT = 3)
+            branches = [([100], (1, 1, 1, 4)), ([20000], (1, 1, 2, 12, 3)), ([30000], (1, 3, 1, 4)),
+                        ([40000], (1, 2, 2, 12, 3)), ([100, 200, 300], (1, 1, 1, 4)),
+                        ([10000, 10000, 10000], (1, 3, 1, 4)), ([7000, 7000, 7000], (1, 1, 2, 4)),
+                        ([15000, 15000, 15000], (1, 2, 2, 4))]
         elif sp == 2:
             branches = [([1000], (1, 1, 1, 8)), ([10000], (2, 1, 2, 4)), ([20000], (2, 2, 1, 4)),
                         ([30000], (2, 2, 2, 4)), ([3000, 3000, 3000], (2, 1, 2, 4))]
@@ -51,8 +54,10 @@ def _decode_cases(t2):
             branches = [([1000], (5, 1, 1 if t2 else 2, 4)), ([300, 400, 500], (5, 1, 1 if t2 else 2, 4))]
         # the even-K class carries every branch; the odd and partial-pair classes every branch too,
         # but with smaller matrices where a branch allows it
-        for Ns, (s_, p_, r_, nw_) in branches:
-            cases.append((op, 1, K, Ns, _mx(s_, p_, r_, odd, t2, nw_, len(Ns) <= 2), f"{kind}"))
+        for Ns, br in branches:
+            s_, p_, r_, nw_ = br[:4]
+            tt = br[4] if len(br) > 4 else 1
+            cases.append((op, 1, K, Ns, _mx(s_, p_, r_, odd, t2, nw_, len(Ns) <= 2, tt), f"{kind}"))
     return cases
 
 
@@ -91,6 +96,7 @@ WS_CASES = [
     ("gemv_ws", 9, 4224, [1000], "gemv_smallm_split<1>", "partial"),
     ("gemv_ws", 16, 4096, [4096], "gemv_smallm<2,0>", "nosplit"),
     ("gemv_ws", 1, 12288, [4096], "gemv_mx<1,1,1,0,0,12,1>", "m1"),
+    ("gemv_ws", 1, 4096, [151936], "gemv_mx<1,2,2,0,0,12,1,3>", "lmhead"),
 ]
 
 ALL_CASES = DECODE_CASES + DECODE_T2_CASES + SELECT_CASES + SMALLM_CASES + PREFILL_CASES + WS_CASES
