@@ -92,17 +92,59 @@ def graph_launch_floor_us(device, n, reps=20):
     return e0.elapsed_time(e1) * 1e3 / reps / n
 
 
-def stream_read_gbs(device, nbytes=2 << 30, reps=10):
-    """A reference read rate for this GPU's HBM: torch's row sums over a 2 GiB fp32 tensor in
-    8192-wide rows (reads every byte once, writes 1/8192 of it); of the plain torch reductions
-    and copies tried on this GPU it reads fastest."""
+def stream_read(device, nbytes=4 << 30, reps=10):
+    """This GPU's HBM read ceiling, measured with the library's plain streaming-read kernel
+    (bin1_stream_read: 16-byte nontemporal loads, each byte read once) over a 4 GiB buffer, the
+    best of a sweep of grid sizes and loads in flight per thread; torch's row sums over the
+    same bytes are reported beside it for context."""
     import torch
-    t = torch.ones(nbytes // 4, dtype=torch.float32, device=device).view(-1, 8192)
+    import bit_packed_sign_amd as b1
+    buf = torch.empty(nbytes, dtype=torch.uint8, device=device)
+    buf.fill_(1)
+    best = (0.0, 0, 0)
+    sweep = {}
+    for grid in (4096, 8192, 16384):
+        sink = torch.empty(4 * grid, dtype=torch.int32, device=device)
+        for unroll in (8, 16):
+            ms = time_fn(lambda: b1.stream_read(buf, sink, grid, unroll), reps)
+            gbs = nbytes / (ms * 1e-3) / 1e9
+            sweep[f"{grid}x{unroll}"] = round(gbs, 1)
+            if gbs > best[0]:
+                best = (gbs, grid, unroll)
+    t = buf.view(torch.float32).view(-1, 8192)
     out = torch.empty(t.shape[0], dtype=torch.float32, device=device)
     ms = time_fn(lambda: torch.sum(t, dim=1, out=out), reps)
-    del t
+    torch_gbs = nbytes / (ms * 1e-3) / 1e9
+    del buf, t
     torch.cuda.empty_cache()
-    return nbytes / (ms * 1e-3) / 1e9
+    return {"gbs": round(best[0], 1), "grid": best[1], "loads_in_flight_per_thread": best[2],
+            "bytes": nbytes, "sweep_gbs": sweep, "torch_row_sum_gbs": round(torch_gbs, 1),
+            "kernel": "bin1_stream_read (16-byte nontemporal loads, a contiguous 16*grid*256-byte front per round)"}
+
+
+def gpu_info():
+    """ROCm version, device name and clocks as the tools report them (None where they do not)."""
+    import subprocess
+    import torch
+    info = {"device": torch.cuda.get_device_properties(0).name, "hip": torch.version.hip, "rocm": None,
+            "sclk_mhz": None, "mclk_mhz": None}
+    try:
+        with open("/opt/rocm/.info/version") as f:
+            info["rocm"] = f.read().strip()
+    except OSError:
+        pass
+    try:
+        r = subprocess.run(["rocm-smi", "--showclocks", "--json"], capture_output=True, text=True, timeout=20)
+        rec = next(iter(json.loads(r.stdout).values()))
+        for k, v in rec.items():
+            kl = k.lower()
+            if "sclk" in kl and info["sclk_mhz"] is None:
+                info["sclk_mhz"] = v
+            elif "mclk" in kl and info["mclk_mhz"] is None:
+                info["mclk_mhz"] = v
+    except Exception:                          # the tool is optional: report what it gives
+        pass
+    return info
 
 
 # Matrix-core work reaches its steady clock only after some milliseconds of load: the prefill
@@ -309,38 +351,124 @@ def stored_traffic(kernel_key, sources, bytes_per_launch):
             "copy_scale": rec["copy_scale"], "source": "profiles/traffic.json"}
 
 
-def cpu_baseline(wl):
-    """The fp64 oracle over every output of the whole 8B decode step, on the host cores."""
+def norm_err(y_gpu: np.ndarray, ref: np.ndarray, nrm: np.ndarray) -> float:
+    """Max over outputs of |y_gpu - y_ref| / sum_k |s x| (the parity measure); an output whose
+    normaliser is 0 must be exactly 0 (else the error is reported as infinite)."""
+    y = np.asarray(y_gpu, dtype=np.float64)
+    zero = nrm == 0
+    if np.any(zero) and not np.all(y[zero] == 0):
+        return float("inf")
+    if not np.all(np.isfinite(y)):
+        return float("inf")
+    with np.errstate(divide="ignore", invalid="ignore"):
+        e = np.where(zero, 0.0, np.abs(y - ref) / np.where(zero, 1.0, nrm))
+    return float(e.max()) if e.size else 0.0
+
+
+def step_outputs(step):
+    """Host copies of every product's output of a Step, in workload order."""
+    return [y.float().cpu().numpy() for _, _, _, ys, _ in step.stages for y in ys]
+
+
+def _rows(N, stride):
+    if stride <= 1:
+        return np.arange(N)
+    return np.unique(np.concatenate([np.arange(0, N, stride), np.arange(max(0, N - 8), N)]))
+
+
+def parity_step(wl, outs, stride, ternary=False):
+    """Oracle parity of a Step's outputs: every product, every `stride`-th row (all rows for 1) and
+    the last rows, all tokens.  Returns (max normalised error, outputs checked)."""
+    from bit_packed_sign_amd import synth
+    from oracle import oracle
+    gen = synth.ternary_gemv_tensors if ternary else synth.gemv_tensors
+    ref_fn = oracle.gemv_t2 if ternary else oracle.gemv
+    gi, worst, checked = 0, 0.0, 0
+    for s, stage in enumerate(wl.stages):
+        x = synth.stage_activations(0, wl, s)
+        for g in stage.gemvs:
+            W, S = gen(0, wl, gi)
+            rows = _rows(g.N, stride)
+            ref, nrm = ref_fn(x, W[rows], S[rows])
+            worst = max(worst, norm_err(outs[gi][:, rows], ref, nrm))
+            checked += ref.size
+            gi += 1
+    return worst, checked
+
+
+def cpu_baseline(wl, outs=None):
+    """The fp64 oracle over every output of the whole 8B decode step, on the host cores; when the
+    GPU's outputs are given, their parity against it (every output)."""
     from bit_packed_sign_amd import synth
     from oracle import oracle
     oracle.lib()
-    gi, nbytes, secs = 0, 0, 0.0
+    gi, nbytes, secs, worst = 0, 0, 0.0, 0.0
     for s, stage in enumerate(wl.stages):
         x = synth.stage_activations(0, wl, s)
         for g in stage.gemvs:
             bits, scales = synth.gemv_tensors(0, wl, gi)
             t0 = time.perf_counter()
-            oracle.gemv(x, bits, scales)
+            ref, nrm = oracle.gemv(x, bits, scales)
             secs += time.perf_counter() - t0
             nbytes += g.weight_bytes
+            if outs is not None:
+                worst = max(worst, norm_err(outs[gi], ref, nrm))
             gi += 1
-    return {"value": round(nbytes / secs / 1e9, 4), "unit": "GB/s", "cores": oracle.max_threads(),
+    base = {"value": round(nbytes / secs / 1e9, 4), "unit": "GB/s", "cores": oracle.max_threads(),
             "kind": "oracle",
             "sample": f"the whole 8B decode step: {gi} GEMVs, {nbytes / 1e9:.3f} GB of weights, every output, "
                       f"fp64 dequantise-and-dot with OpenMP over rows; {secs:.1f} s wall",
             "ms_per_step": round(secs * 1e3, 1)}
+    return base, (worst if outs is not None else None)
+
+
+def cpu_one_core():
+    """The same oracle on one host core: the single 4096x4096 GEMV whole, and the first four layers
+    of the 8B step (28 GEMVs) as a sample of it."""
+    from bit_packed_sign_amd import synth
+    from oracle import oracle
+    prev = oracle.max_threads()
+    oracle.set_threads(1)
+    try:
+        wl = synth.single_gemv()
+        bits, scales = synth.gemv_tensors(0, wl, 0)
+        x = synth.stage_activations(0, wl, 0)
+        t0 = time.perf_counter()
+        oracle.gemv(x, bits, scales)
+        c1 = time.perf_counter() - t0
+        wl = synth.decode_8b()
+        gi, nb, secs = 0, 0, 0.0
+        for s, stage in enumerate(wl.stages[:16]):
+            x = synth.stage_activations(0, wl, s)
+            for g in stage.gemvs:
+                bits, scales = synth.gemv_tensors(0, wl, gi)
+                t0 = time.perf_counter()
+                oracle.gemv(x, bits, scales)
+                secs += time.perf_counter() - t0
+                nb += g.weight_bytes
+                gi += 1
+    finally:
+        oracle.set_threads(prev)
+    single = synth.single_gemv().gemvs[0].weight_bytes
+    return {"cores": 1,
+            "single_gemv_4096x4096": {"s": round(c1, 3), "gbs": round(single / c1 / 1e9, 4)},
+            "decode_8b_first_4_layers": {"gemvs": gi, "bytes": nb, "s": round(secs, 2),
+                                         "gbs": round(nb / secs / 1e9, 4),
+                                         "whole_step_s_at_this_rate": round(wl.weight_bytes / (nb / secs), 1)}}
 
 
 # ----------------------------------------------------------------------------------- extras
-def extra_single(dev):
-    """One 4096x4096 GEMV: cache-cold over a pool of copies larger than the 256 MB cache, and
-    cache-hot; plus the 64-row patch applied and removed."""
+def extra_single(dev, check):
+    """One 4096x4096 GEMV over a pool of copies larger than the 256 MB cache: eager launches, and
+    the device time per launch of a replayed graph of one launch per copy; cache-hot; the 64-row
+    patch applied and removed (timed, and checked bit for bit against the oracle)."""
     import torch
     import bit_packed_sign_amd as b1
     from bit_packed_sign_amd import synth
     wl = synth.single_gemv()
     bits, scales = synth.gemv_tensors(0, wl, 0)
-    x = torch.from_numpy(synth.stage_activations(0, wl, 0)).to(dev)
+    xh = synth.stage_activations(0, wl, 0)
+    x = torch.from_numpy(xh).to(dev)
     W0 = torch.from_numpy(bits.view(np.int32)).to(dev)
     S0 = torch.from_numpy(scales).to(dev)
     g = wl.gemvs[0]
@@ -354,34 +482,72 @@ def extra_single(dev):
         i = next(it) % copies
         b1.gemv(x, Ws[i], Ss[i], out=y)
     ms_cold = time_fn(cold, reps=copies)
+    # the same launches captured once: one replay runs every copy once, back to back
+    ys = torch.empty((copies, 4096), dtype=torch.float16, device=dev)
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        for i in range(copies):
+            b1.gemv(x, Ws[i], Ss[i], out=ys[i:i + 1])
+    torch.cuda.current_stream().wait_stream(s)
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        for i in range(copies):
+            b1.gemv(x, Ws[i], Ss[i], out=ys[i:i + 1])
+    ms_graph = time_fn(graph.replay, reps=5) / copies
     ms_hot = time_fn(lambda: b1.gemv(x, W0, S0, out=y), reps=200)
     rows = torch.from_numpy(synth.patch_rows_single()).to(dev)
-    ms_patch = time_fn(lambda: b1.xor_patch_apply(W0, rows), reps=200)
-    del Ws, Ss
-    return {"workload": "4096x4096 GEMV, M=1", "pool_copies": copies,
-            "us_cold": round(ms_cold * 1e3, 2), "gbs_cold": round(g.weight_bytes / ms_cold / 1e6, 1),
-            "us_hot": round(ms_hot * 1e3, 2), "gbs_hot_cache": round(g.weight_bytes / ms_hot / 1e6, 1),
-            "patch_64_rows_us": round(ms_patch * 1e3, 2),
-            "note": "eager launches back to back: each time includes the launch gap"}
+    ms_patch = time_fn(lambda: b1.xor_patch_apply(W0, rows), reps=200)     # an even count: removed again
+    out = {"workload": "4096x4096 GEMV, M=1", "pool_copies": copies,
+           "us_eager_cold": round(ms_cold * 1e3, 2), "gbs_eager_cold": round(g.weight_bytes / ms_cold / 1e6, 1),
+           "us_graph_cold": round(ms_graph * 1e3, 2), "gbs_graph_cold": round(g.weight_bytes / ms_graph / 1e6, 1),
+           "us_eager_hot": round(ms_hot * 1e3, 2), "gbs_eager_hot": round(g.weight_bytes / ms_hot / 1e6, 1),
+           "patch_64_rows_us": round(ms_patch * 1e3, 2),
+           "note": "eager: back-to-back launches, each time includes the host's per-call cost; graph: one "
+                   "replay of one launch per copy, so each launch includes the dependent-launch gap"}
+    if check:
+        from oracle import oracle
+        ref, nrm = oracle.gemv(xh, bits, scales)
+        b1.gemv(x, W0, S0, out=y)
+        errs = [norm_err(y.float().cpu().numpy(), ref, nrm)]
+        errs.append(max(norm_err(ys[i:i + 1].float().cpu().numpy(), ref, nrm) for i in range(0, copies, 57)))
+        rows_h = synth.patch_rows_single()
+        b1.xor_patch_apply(W0, rows)
+        applied = np.array_equal(W0.cpu().numpy().view(np.uint32), oracle.xor_patch(bits, rows_h, 4096)[0])
+        b1.xor_patch_apply(W0, rows)
+        removed = np.array_equal(W0.cpu().numpy().view(np.uint32), bits)
+        out["parity"] = {"max_norm_err": max(errs), "patch_apply_bit_exact": bool(applied),
+                         "patch_remove_bit_exact": bool(removed)}
+    del Ws, Ss, graph
+    return out
 
 
-def extra_step(wl, dev, steps, label, chain=False):
-    st = Step(wl, dev)
+def extra_step(wl, dev, steps, label, chain=False, check_stride=0, ternary=False):
+    st = Step(wl, dev, ternary=ternary)
     st.capture()
     ms = st.timed(max(5, steps // 2), 2)
     out = {"workload": label, "ms_per_step": round(ms, 4),
-           "gbs": round(wl.weight_bytes / ms / 1e6, 1), "tok_s": round(1e3 / ms, 1),
-           "pct_hbm_peak": round(100 * wl.weight_bytes / ms / 1e6 / HBM_PEAK_GBS, 2), "path": "graph"}
+           "gbs": round(st.weight_bytes / ms / 1e6, 1), "tok_s": round(1e3 / ms, 1),
+           "pct_hbm_peak": round(100 * st.weight_bytes / ms / 1e6 / HBM_PEAK_GBS, 2), "path": "graph"}
     if chain:
         c = ChainStep(st)
         msc = c.timed(max(5, steps // 2), 2)
         out["chain"] = {"ms_per_step": round(msc, 4), "gbs": round(wl.weight_bytes / msc / 1e6, 1)}
         del c
+        st.graph.replay()                     # the graph's outputs again (the chain wrote the same)
+        import torch
+        torch.cuda.synchronize()
+    if check_stride:
+        e, n = parity_step(wl, step_outputs(st), check_stride, ternary)
+        out["parity"] = {"max_norm_err": e, "outputs_checked": n,
+                         "rows": "every output" if check_stride == 1 else f"every {check_stride}th row of every product"}
     return st, out
 
 
-def extra_patch27b(st, dev):
-    """2000 distinct (layer, projection, row) flips over the 27B MLP matrices, one launch."""
+def extra_patch27b(st, dev, check):
+    """2000 distinct (layer, projection, row) flips over the 27B MLP matrices, one launch; timed,
+    then applied once and removed once, each checked bit for bit against the oracle's patch."""
     import bit_packed_sign_amd as b1
     import torch
     from bit_packed_sign_amd import synth
@@ -393,12 +559,30 @@ def extra_patch27b(st, dev):
     table = b1.PatchTable(mlp)
     ent_np = synth.patch_entries_27b()
     ent = torch.from_numpy(ent_np).to(dev)
-    ms = time_fn(lambda: b1.xor_patch_apply_multi(table, ent), reps=200)
+    ms = time_fn(lambda: b1.xor_patch_apply_multi(table, ent), reps=200)   # an even count: removed again
     row_bytes = np.array([m.shape[1] * 4 for m in mlp])[ent_np[:, 0]].sum()
-    return {"patch_2000_rows_us": round(ms * 1e3, 2), "patch_bytes_read_and_written": int(2 * row_bytes)}
+    out = {"patch_2000_rows_us": round(ms * 1e3, 2), "patch_bytes_read_and_written": int(2 * row_bytes)}
+    if check:
+        from oracle import oracle
+        wl = synth.decode_27b()
+        b1.xor_patch_apply_multi(table, ent)
+        torch.cuda.synchronize()
+        applied = removed = True
+        hosts = []
+        for mid, m in enumerate(mlp):
+            l, j = divmod(mid, 3)
+            W, _ = synth.gemv_tensors(0, wl, 7 * l + 4 + j)        # gate, up, down of layer l
+            hosts.append(W)
+            want = oracle.xor_patch(W, ent_np[ent_np[:, 0] == mid, 1], W.shape[1] * 32)[0]
+            applied &= bool(torch.equal(m, torch.from_numpy(want.view(np.int32)).to(dev)))
+        b1.xor_patch_apply_multi(table, ent)
+        for m, W in zip(mlp, hosts):
+            removed &= bool(torch.equal(m, torch.from_numpy(W.view(np.int32)).to(dev)))
+        out["patch_parity"] = {"apply_bit_exact": applied, "remove_bit_exact": removed, "matrices_compared": len(mlp)}
+    return out
 
 
-def extra_bits_8b(st, dev):
+def extra_bits_8b(st, dev, check):
     """500K random single-bit flips over the 108 MLP matrices of the 8B batch-16 workload (the
     Bankai robustness experiment's data movement), one launch; each timed call flips them again."""
     import bit_packed_sign_amd as b1
@@ -410,10 +594,21 @@ def extra_bits_8b(st, dev):
         dn = st.stages[2 * l + 1][1]
         mlp += [gu[0], gu[1], dn[0]]
     table = b1.PatchTable(mlp)
-    ent = torch.from_numpy(synth.bit_flip_entries(0, [(m.shape[0], m.shape[1] * 32) for m in mlp],
-                                                  500_000)).to(dev)
-    ms = time_fn(lambda: b1.xor_bits_apply(table, ent), reps=50)
-    return {"bit_flips_500k_us": round(ms * 1e3, 2), "flips_per_s": round(500_000 / (ms * 1e-3), 0)}
+    ent_np = synth.bit_flip_entries(0, [(m.shape[0], m.shape[1] * 32) for m in mlp], 500_000)
+    ent = torch.from_numpy(ent_np).to(dev)
+    ms = time_fn(lambda: b1.xor_bits_apply(table, ent), reps=50)            # an even count: removed again
+    out = {"bit_flips_500k_us": round(ms * 1e3, 2), "flips_per_s": round(500_000 / (ms * 1e-3), 0)}
+    if check:
+        from oracle import oracle
+        wl = synth.mlp_8b_m16()
+        hosts = [synth.gemv_tensors(0, wl, mid)[0] for mid in range(len(mlp))]   # gate, up, down: GEMVs 3l..3l+2
+        b1.xor_bits_apply(table, ent)
+        want, _ = oracle.xor_bits(hosts, ent_np)
+        ok = all(bool(torch.equal(m, torch.from_numpy(w.view(np.int32)).to(dev))) for m, w in zip(mlp, want))
+        b1.xor_bits_apply(table, ent)
+        ok_back = all(bool(torch.equal(m, torch.from_numpy(w.view(np.int32)).to(dev))) for m, w in zip(mlp, hosts))
+        out["bits_parity"] = {"apply_bit_exact": ok, "remove_bit_exact": ok_back}
+    return out
 
 
 def extra_rank27b(st, dev):
@@ -425,19 +620,19 @@ def extra_rank27b(st, dev):
     return {"rank_rows_17408x5120_us": round(ms * 1e3, 1)}
 
 
-def extra_ternary(dev, steps):
+def extra_ternary(dev, steps, check):
     """Ternary g128 (2-bit slots): the 8B decode step (one launch per stage, q/k/v and gate/up
     fused, HIP graph), the lm_head product alone, and the prefill contraction."""
     import torch
     import bit_packed_sign_amd as b1
     from bit_packed_sign_amd import synth
     out = {"bytes_per_weight": synth.TERNARY_BYTES_PER_WEIGHT}
-    st = Step(synth.decode_8b(), dev, ternary=True)
-    st.capture()
-    ms = st.timed(steps, 3)
-    out["decode_8b"] = {"ms_per_step": round(ms, 4), "gbs": round(st.weight_bytes / ms / 1e6, 1),
-                        "tok_s": round(1e3 / ms, 1), "launches": len(st.stages),
-                        "weight_bytes": st.weight_bytes}
+    wl = synth.decode_8b()
+    st, o = extra_step(wl, dev, 2 * steps, "ternary 8B decode step", check_stride=4 if check else 0, ternary=True)
+    out["decode_8b"] = {"ms_per_step": o["ms_per_step"], "gbs": o["gbs"], "tok_s": o["tok_s"],
+                        "launches": len(st.stages), "weight_bytes": st.weight_bytes}
+    if check:
+        out["decode_8b"]["parity"] = o["parity"]
     x, Ws, Ss, ys, nb = st.stages[-1]                 # lm_head 4096 x 151936
     ms = time_fn(lambda: b1.gemv_t2(x, Ws[0], Ss[0], out=ys[0]), reps=20)
     out["lm_head"] = {"us": round(ms * 1e3, 2), "gbs": round(nb / ms / 1e6, 1)}
@@ -445,26 +640,38 @@ def extra_ternary(dev, steps):
     torch.cuda.empty_cache()
     M, K, N = synth.PREFILL_M, synth.PREFILL_K, synth.PREFILL_N
     r = synth.rng_for(0, synth.WL_PREFILL, 1)
-    x = torch.from_numpy(synth.activations(r, M, K)).to(dev)
-    T = torch.from_numpy(synth.ternary_words_fast(r, N, K).view(np.int32)).to(dev)
-    S = torch.from_numpy(synth.group_scales(r, N, K)).to(dev)
+    xh = synth.activations(r, M, K)
+    Th = synth.ternary_words_fast(r, N, K)
+    Sh = synth.group_scales(r, N, K)
+    x = torch.from_numpy(xh).to(dev)
+    T = torch.from_numpy(Th.view(np.int32)).to(dev)
+    S = torch.from_numpy(Sh).to(dev)
     y = torch.empty((M, N), dtype=torch.float16, device=dev)
     ms = time_fn(lambda: b1.gemm_prefill_t2(x, T, S, out=y), reps=50, warm=PREFILL_WARM)
     tf = 2.0 * M * K * N / (ms * 1e-3) / 1e12
     out["prefill"] = {"us": round(ms * 1e3, 2), "tflops": round(tf, 1),
                       "frac_of_fp16_mfma_peak": round(tf / FP16_MFMA_PEAK_TFLOPS, 4)}
+    if check:
+        from oracle import oracle
+        rows = _rows(N, 64)
+        ref, nrm = oracle.gemv_t2(xh, Th[rows], Sh[rows])
+        out["prefill"]["parity"] = {"max_norm_err": norm_err(y.float().cpu().numpy()[:, rows], ref, nrm),
+                                    "rows": "all tokens of every 64th weight row"}
     return out
 
 
-def extra_prefill(dev):
+def extra_prefill(dev, check):
     import torch
     import bit_packed_sign_amd as b1
     from bit_packed_sign_amd import synth
     M, K, N = synth.PREFILL_M, synth.PREFILL_K, synth.PREFILL_N
     r = synth.rng_for(0, synth.WL_PREFILL, 0)
-    x = torch.from_numpy(synth.activations(r, M, K)).to(dev)
-    W = torch.from_numpy(synth.sign_words(r, N, K).view(np.int32)).to(dev)
-    S = torch.from_numpy(synth.group_scales(r, N, K)).to(dev)
+    xh = synth.activations(r, M, K)
+    Wh = synth.sign_words(r, N, K)
+    Sh = synth.group_scales(r, N, K)
+    x = torch.from_numpy(xh).to(dev)
+    W = torch.from_numpy(Wh.view(np.int32)).to(dev)
+    S = torch.from_numpy(Sh).to(dev)
     y = torch.empty((M, N), dtype=torch.float16, device=dev)
     ms = time_fn(lambda: b1.gemm_prefill(x, W, S, out=y), reps=50, warm=PREFILL_WARM)
     tf = 2.0 * M * K * N / (ms * 1e-3) / 1e12
@@ -473,6 +680,17 @@ def extra_prefill(dev):
     y5 = torch.empty((m5, N), dtype=torch.float16, device=dev)
     ms5 = time_fn(lambda: b1.gemm_prefill(x[:m5], W, S, out=y5), reps=50, warm=4 * PREFILL_WARM)
     tf5 = 2.0 * m5 * K * N / (ms5 * 1e-3) / 1e12
+    out = {"workload": "prefill M=2048 K=4096 N=12288", "us": round(ms * 1e3, 2),
+           "tflops": round(tf, 1), "frac_of_fp16_mfma_peak": round(tf / FP16_MFMA_PEAK_TFLOPS, 4),
+           "m512": {"us": round(ms5 * 1e3, 2), "tflops": round(tf5, 1),
+                    "frac_of_fp16_mfma_peak": round(tf5 / FP16_MFMA_PEAK_TFLOPS, 4)}}
+    if check:
+        from oracle import oracle
+        rows = _rows(N, 64)
+        ref, nrm = oracle.gemv(xh, Wh[rows], Sh[rows])
+        out["parity"] = {"max_norm_err": max(norm_err(y.float().cpu().numpy()[:, rows], ref, nrm),
+                                             norm_err(y5.float().cpu().numpy()[:, rows], ref[:m5], nrm[:m5])),
+                         "rows": "all tokens of every 64th weight row, M = 2048 and M = 512"}
     # context only: a dense fp16 GEMM of the same shape through torch (the vendor BLAS), with
     # the weights as a plain fp16 matrix (row-major [K][N] and transposed [N][K])
     del W, S
@@ -483,25 +701,47 @@ def extra_prefill(dev):
     for name, fn in (("b_row_major", lambda: a @ b), ("b_transposed", lambda: a @ bt.t())):
         rms = time_fn(fn, reps=50, warm=PREFILL_WARM)
         ref[name] = {"us": round(rms * 1e3, 2), "tflops": round(2.0 * M * K * N / (rms * 1e-3) / 1e12, 1)}
-    return {"workload": "prefill M=2048 K=4096 N=12288", "us": round(ms * 1e3, 2),
-            "tflops": round(tf, 1), "frac_of_fp16_mfma_peak": round(tf / FP16_MFMA_PEAK_TFLOPS, 4),
-            "m512": {"us": round(ms5 * 1e3, 2), "tflops": round(tf5, 1),
-                     "frac_of_fp16_mfma_peak": round(tf5 / FP16_MFMA_PEAK_TFLOPS, 4)},
-            "dense_fp16_gemm_same_shape_torch": ref}
+    out["dense_fp16_gemm_same_shape_torch"] = ref
+    return out
 
 
-def extra_pm1(dev):
+def extra_pm1(dev, check):
     import torch
     import bit_packed_sign_amd as b1
     from bit_packed_sign_amd import synth
     K, N = 4096, 151936
     r = synth.rng_for(0, synth.WL_TEST, 424242)
-    A = torch.from_numpy(synth.pm1_words(r, 1, K).view(np.int32)).to(dev)
-    W = torch.from_numpy(synth.sign_words(r, N, K).view(np.int32)).to(dev)
+    Ah = synth.pm1_words(r, 1, K)
+    Wh = synth.sign_words(r, N, K)
+    A = torch.from_numpy(Ah.view(np.int32)).to(dev)
+    W = torch.from_numpy(Wh.view(np.int32)).to(dev)
     y = torch.empty((1, N), dtype=torch.int32, device=dev)
     ms = time_fn(lambda: b1.gemv_pm1(A, W, out=y), reps=50)
-    return {"workload": "+-1 popcount product K=4096 N=151936 M=1", "us": round(ms * 1e3, 2),
-            "gbs": round(N * K / 8 / ms / 1e6, 1)}
+    out = {"workload": "+-1 popcount product K=4096 N=151936 M=1", "us": round(ms * 1e3, 2),
+           "gbs": round(N * K / 8 / ms / 1e6, 1)}
+    if check:
+        from oracle import oracle
+        out["parity"] = {"bit_exact": bool(np.array_equal(y.cpu().numpy(), oracle.pm1(Ah, Wh, K)))}
+    return out
+
+
+def extra_small_batch_steps(dev, steps, check):
+    """The 8B decode step (145 stages) at M = 2, 5 and 8 tokens: the verify pass of speculative
+    decoding with 1, 4 and 7 drafted tokens (one launch per stage, HIP graph)."""
+    import torch
+    from bit_packed_sign_amd import synth
+    out = {}
+    for M in (2, 5, 8):
+        wl = synth._decoder(synth.WL_DECODE_8B, f"decode-8b-m{M}", M, 36, 4096, 4096, 1024, 4096, 12288,
+                            lm_vocab=151936)
+        st, o = extra_step(wl, dev, steps, f"8B decode step, M={M}", check_stride=64 if check else 0)
+        out[f"m{M}"] = {"ms_per_step": o["ms_per_step"], "gbs": o["gbs"],
+                        "tokens_per_s": round(M * 1e3 / o["ms_per_step"], 1)}
+        if check:
+            out[f"m{M}"]["parity"] = o["parity"]
+        del st
+        torch.cuda.empty_cache()
+    return out
 
 
 # ------------------------------------------------------------------------------------ main
@@ -519,6 +759,7 @@ def main():
     if args.only:
         run_only(args, dev)
         return
+    check = not args.no_cpu_baseline
 
     wl = synth.decode_8b()
     wbytes = wl.weight_bytes
@@ -526,20 +767,16 @@ def main():
     step.capture()
     ms_graph = step.timed(args.steps, args.warmup)
     log(f"[bench] graph step {ms_graph * 1e3:.1f} us, {wbytes / ms_graph / 1e6:.0f} GB/s")
+    outs_8b = step_outputs(step)              # the timed replays' outputs, for the parity check
     chain = ChainStep(step)
     ms_chain = chain.timed(args.steps, args.warmup)
     log(f"[bench] chain step {ms_chain * 1e3:.1f} us, {wbytes / ms_chain / 1e6:.0f} GB/s")
 
-    # eager per-launch HIP events (on the launch stream) give each stage's share; in the replayed
-    # graph the launches run back to back, so the kernel's average duration there is the step
-    # time over the launches (rocprofv3 kernel traces of the same command agree)
     per = step.per_launch_ms()
     nl = len(step.stages)
     floor_us = graph_launch_floor_us(dev, nl)
     log(f"[bench] graph of {nl} dependent one-workgroup launches: {floor_us:.2f} us per launch")
     pct = step.replay_percentiles_us()
-    read_gbs = stream_read_gbs(dev)
-    log(f"[bench] single replays {pct} us; stream read {read_gbs:.0f} GB/s")
     big = max(range(nl), key=lambda i: step.stages[i][4])
     paths = {
         "graph": {"ms_per_step": round(ms_graph, 5), "gbs": round(wbytes / ms_graph / 1e6, 1),
@@ -572,42 +809,79 @@ def main():
                 "kernel": "gemv_mx_kernel, all 145 launches of the 8B step",
                 "bytes_per_launch": round(wbytes / nl, 1), "avg_launch_us": round(ms_graph * 1e3 / nl, 3),
                 "timing": "HIP events around the timed graph replays on the replay stream; launches run "
-                          "back to back, so the average launch is the step time over 145 launches"}
+                          "back to back, so the average launch is the step time over 145 launches, the "
+                          "dependent-launch gap included (graph_floor_us_per_launch under extra.step_paths "
+                          "is that gap for a one-workgroup kernel)"}
     gbs = wbytes / (ms * 1e-3) / 1e9
     log(f"[bench] headline {head}: {ms * 1e3:.1f} us, {gbs:.0f} GB/s, {1e3 / ms:.0f} tok/s")
     del chain, step
     torch.cuda.empty_cache()
+    stream = stream_read(dev)
+    log(f"[bench] stream read {stream['gbs']:.0f} GB/s (torch row sums {stream['torch_row_sum_gbs']:.0f})")
+    roof["frac_of_stream_read"] = round(achieved / stream["gbs"], 4)
 
     extra = {"step_paths": paths}
+    parity = {}
     if not args.no_extra:
         t0 = time.time()
-        extra["single_gemv"] = extra_single(dev)
+        extra["single_gemv"] = extra_single(dev, check)
         log(f"[bench] single GEMV: {extra['single_gemv']}")
         st, extra["mlp_8b_m16"] = extra_step(synth.mlp_8b_m16(), dev, args.steps,
-                                             "8B MLP batch 16: 36 x (gate/up 4096x12288, down 12288x4096)")
-        extra["mlp_8b_m16"].update(extra_bits_8b(st, dev))
+                                             "8B MLP batch 16: 36 x (gate/up 4096x12288, down 12288x4096)",
+                                             check_stride=16 if check else 0)
+        extra["mlp_8b_m16"].update(extra_bits_8b(st, dev, check))
         log(f"[bench] mlp m16: {extra['mlp_8b_m16']}")
         del st
         torch.cuda.empty_cache()
-        extra["prefill"] = extra_prefill(dev)
+        extra["prefill"] = extra_prefill(dev, check)
         log(f"[bench] prefill: {extra['prefill']}")
         st, extra["decode_27b"] = extra_step(synth.decode_27b(), dev, args.steps,
                                              "27B decode batch 1: 64 x (q/k/v/o 5120x5120, gate/up "
-                                             "5120x17408, down 17408x5120)", chain=True)
-        extra["decode_27b"].update(extra_patch27b(st, dev))
+                                             "5120x17408, down 17408x5120)", chain=True,
+                                             check_stride=4 if check else 0)
+        extra["decode_27b"].update(extra_patch27b(st, dev, check))
         extra["decode_27b"].update(extra_rank27b(st, dev))
         log(f"[bench] 27b: {extra['decode_27b']}")
         del st
         torch.cuda.empty_cache()
-        extra["ternary"] = extra_ternary(dev, args.steps)
+        extra["small_batch_steps"] = extra_small_batch_steps(dev, args.steps, check)
+        log(f"[bench] M = 2, 5, 8: {extra['small_batch_steps']}")
+        extra["ternary"] = extra_ternary(dev, args.steps, check)
         log(f"[bench] ternary: {extra['ternary']}")
-        extra["pm1"] = extra_pm1(dev)
+        extra["pm1"] = extra_pm1(dev, check)
         log(f"[bench] pm1: {extra['pm1']} ({time.time() - t0:.0f} s of extras)")
 
     cpu = None
-    if not args.no_cpu_baseline:
-        cpu = cpu_baseline(wl)
-        log(f"[bench] cpu baseline {cpu['value']:.3f} GB/s on {cpu['cores']} threads")
+    if check:
+        cpu, err_8b = cpu_baseline(wl, outs_8b)
+        log(f"[bench] cpu baseline {cpu['value']:.3f} GB/s on {cpu['cores']} threads; 8B step parity {err_8b:.2e}")
+        cpu["one_core"] = cpu_one_core()
+        log(f"[bench] one core: {cpu['one_core']}")
+        parity["decode_8b_m1"] = {"max_norm_err": err_8b, "outputs": "every output of all 253 products"}
+        if not args.no_extra:
+            e = extra
+            parity["single_gemv_4096"] = e["single_gemv"]["parity"]
+            parity["mlp_8b_m16"] = e["mlp_8b_m16"]["parity"] | {"bit_flips_500k": e["mlp_8b_m16"]["bits_parity"]}
+            parity["prefill_m2048"] = e["prefill"]["parity"]
+            parity["decode_27b_m1"] = e["decode_27b"]["parity"] | {"patch_2000_rows": e["decode_27b"]["patch_parity"]}
+            parity["decode_8b_m2_m5_m8"] = {k: v["parity"] for k, v in e["small_batch_steps"].items()}
+            parity["ternary"] = {"decode_8b": e["ternary"]["decode_8b"]["parity"],
+                                 "prefill": e["ternary"]["prefill"]["parity"]}
+            parity["pm1"] = e["pm1"]["parity"]
+        def walk(d, errs, flags):
+            for k, v in d.items():
+                if isinstance(v, dict):
+                    walk(v, errs, flags)
+                elif k == "max_norm_err":
+                    errs.append(v)
+                elif isinstance(v, bool):
+                    flags.append(v)
+        errs, flags = [], []
+        walk(parity, errs, flags)
+        worst, bits = max(errs), all(flags)
+        parity["summary"] = {"max_norm_err_all_configs": worst, "tolerance": 2e-3,
+                             "all_float_within_tolerance": worst <= 2e-3, "all_integer_bit_exact": bits}
+        log(f"[bench] parity: worst {worst:.2e}, integer work bit-exact {bits}")
     out = {
         "metric": "1-bit decode GEMV weight-GB/s (% of HBM peak) and implied tok/s at 8B shape",
         "value": round(gbs, 1), "unit": "GB/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
@@ -621,11 +895,13 @@ def main():
                    "step_path": head,
                    "weight_bytes_per_step": wbytes, "global_batch": 1, "parallelism": "none (1 GPU)"},
         "pct_hbm_peak": round(100 * gbs / HBM_PEAK_GBS, 2),
-        "pct_of_stream_read": round(100 * gbs / read_gbs, 2),
-        "stream_read_gbs": round(read_gbs, 1),
+        "pct_of_stream_read": round(100 * gbs / stream["gbs"], 2),
+        "stream_read": stream,
         "implied_tok_s": round(1e3 / ms, 1),
         "roofline": roof,
         "cpu_baseline": cpu,
+        "parity": parity or None,
+        "gpu": gpu_info(),
         "extra": extra,
     }
     print(json.dumps(out), flush=True)
@@ -657,22 +933,22 @@ def run_only(args, dev):
         ms = time_fn(lambda: b1.gemv(x, W, S, out=y), reps=args.steps)
         log(f"[bench] lm_head {ms * 1e3:.1f} us")
     elif name == "single":
-        log(f"[bench] {extra_single(dev)}")
+        log(f"[bench] {extra_single(dev, False)}")
     elif name == "mlp16":
         st, o = extra_step(synth.mlp_8b_m16(), dev, args.steps, "mlp16")
         log(f"[bench] {o}")
     elif name == "bits":
         st, _ = extra_step(synth.mlp_8b_m16(), dev, 2, "mlp16")
-        log(f"[bench] {extra_bits_8b(st, dev)}")
+        log(f"[bench] {extra_bits_8b(st, dev, False)}")
     elif name == "prefill":
-        log(f"[bench] {extra_prefill(dev)}")
+        log(f"[bench] {extra_prefill(dev, False)}")
     elif name == "step27b":
         st, o = extra_step(synth.decode_27b(), dev, args.steps, "27b")
-        log(f"[bench] {o} patch {extra_patch27b(st, dev)} rank {extra_rank27b(st, dev)}")
+        log(f"[bench] {o} patch {extra_patch27b(st, dev, False)} rank {extra_rank27b(st, dev)}")
     elif name == "pm1":
-        log(f"[bench] {extra_pm1(dev)}")
+        log(f"[bench] {extra_pm1(dev, False)}")
     elif name == "ternary":
-        log(f"[bench] {extra_ternary(dev, args.steps)}")
+        log(f"[bench] {extra_ternary(dev, args.steps, False)}")
     elif name == "copy":
         # a plain device copy of known size, to scale the HBM traffic counters
         src = torch.empty(256 << 20, dtype=torch.uint8, device=dev).fill_(1)
