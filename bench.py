@@ -277,6 +277,48 @@ class Step:
         t = np.sort([a.elapsed_time(b) * 1e3 for a, b in ev])
         return {f"p{q}": round(float(np.percentile(t, q)), 1) for q in (10, 50, 90)}
 
+    def per_class_graph_us(self, reps=10):
+        """Launches grouped by shape (K and rows per launch): each group's launches of one step,
+        in step order, captured into a graph of their own and replayed; HIP events on the replay
+        stream give the time per launch, the dependent-launch gap included.  A group with a
+        single launch per step (lm_head) is captured 8 times over.  Returns a list of dicts, one
+        per group, in first-stage order."""
+        import torch
+        groups = {}
+        for i, (x, Ws, Ss, ys, nbytes) in enumerate(self.stages):
+            key = (x.shape[1], sum(W.shape[0] for W in Ws))
+            groups.setdefault(key, []).append(i)
+        out = []
+        for (K, N), idx in groups.items():
+            rep = 8 if len(idx) == 1 else 1
+            s = torch.cuda.Stream()
+            s.wait_stream(torch.cuda.current_stream())
+            with torch.cuda.stream(s):
+                for i in idx:
+                    self.run_stage(self.stages[i])
+            torch.cuda.current_stream().wait_stream(s)
+            torch.cuda.synchronize()
+            g = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(g):
+                for _ in range(rep):
+                    for i in idx:
+                        self.run_stage(self.stages[i])
+            for _ in range(3):
+                g.replay()
+            torch.cuda.synchronize()
+            e0, e1 = events()
+            e0.record()
+            for _ in range(reps):
+                g.replay()
+            e1.record()
+            torch.cuda.synchronize()
+            us = e0.elapsed_time(e1) * 1e3 / (reps * rep * len(idx))
+            nbytes = self.stages[idx[0]][4]
+            out.append({"K": K, "rows": N, "launches_per_step": len(idx), "bytes_per_launch": nbytes,
+                        "us_per_launch_in_graph": round(us, 3), "gbs": round(nbytes / (us * 1e-6) / 1e9, 1)})
+            del g
+        return out
+
     def per_launch_ms(self, reps=3):
         """Per-launch kernel durations (one launch per stage) from HIP events recorded on the
         stream the kernels are launched on (eager launches)."""
@@ -322,13 +364,15 @@ class ChainStep:
 
 
 def kernel_source_sha(*names):
-    """Hash of the kernel sources (and of the build script, which holds the compile flags) a
-    stored counter summary was taken with."""
+    """Hash of the kernel sources a stored counter summary was taken with, of the shared device
+    header, and of the compile flags (include paths left out: they name the checkout)."""
     import hashlib
+    from bit_packed_sign_amd.build import FLAGS
     h = hashlib.sha256()
-    for n in (*names, "../build.py"):
+    for n in (*names, "common.hpp"):
         with open(os.path.join(ROOT, "bit_packed_sign_amd", "csrc", n), "rb") as f:
             h.update(f.read())
+    h.update(" ".join(f for f in FLAGS if not os.path.isabs(f)).encode())
     return h.hexdigest()[:16]
 
 
@@ -777,6 +821,8 @@ def main():
     floor_us = graph_launch_floor_us(dev, nl)
     log(f"[bench] graph of {nl} dependent one-workgroup launches: {floor_us:.2f} us per launch")
     pct = step.replay_percentiles_us()
+    classes = step.per_class_graph_us()
+    log(f"[bench] per launch class: {classes}")
     big = max(range(nl), key=lambda i: step.stages[i][4])
     paths = {
         "graph": {"ms_per_step": round(ms_graph, 5), "gbs": round(wbytes / ms_graph / 1e6, 1),
@@ -811,7 +857,10 @@ def main():
                 "timing": "HIP events around the timed graph replays on the replay stream; launches run "
                           "back to back, so the average launch is the step time over 145 launches, the "
                           "dependent-launch gap included (graph_floor_us_per_launch under extra.step_paths "
-                          "is that gap for a one-workgroup kernel)"}
+                          "is that gap for a one-workgroup kernel)",
+                "per_launch_class": classes,
+                "per_launch_class_sum_us": round(sum(c["launches_per_step"] * c["us_per_launch_in_graph"]
+                                                     for c in classes), 1)}
     gbs = wbytes / (ms * 1e-3) / 1e9
     log(f"[bench] headline {head}: {ms * 1e3:.1f} us, {gbs:.0f} GB/s, {1e3 / ms:.0f} tok/s")
     del chain, step
