@@ -996,6 +996,8 @@ def run_only(args, dev):
         log(f"[bench] {o} patch {extra_patch27b(st, dev, False)} rank {extra_rank27b(st, dev)}")
     elif name == "pm1":
         log(f"[bench] {extra_pm1(dev, False)}")
+    elif name == "smallbatch":
+        log(f"[bench] {extra_small_batch_steps(dev, args.steps, False)}")
     elif name == "ternary":
         log(f"[bench] {extra_ternary(dev, args.steps, False)}")
     elif name == "copy":

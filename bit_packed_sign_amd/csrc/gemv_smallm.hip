@@ -314,11 +314,16 @@ hipError_t launch_sm_split(const uint16_t *x, const MxSet &set, int M, int K, in
                        tiles / G, tiles % G, G, set, part);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
-    hipLaunchKernelGGL(smallm_reduce_kernel, dim3((MN + 255) / 256), dim3(256), 0, st, part, nchunk, MN, set.y[0]);
-    return hipGetLastError();
+    return launch_smallm_reduce(part, nchunk, MN, set.y[0], st);
 }
 
 }  // namespace
+
+hipError_t launch_smallm_reduce(const float *part, int nchunk, int MN, uint16_t *y, hipStream_t st)
+{
+    hipLaunchKernelGGL(smallm_reduce_kernel, dim3((MN + 255) / 256), dim3(256), 0, st, part, nchunk, MN, y);
+    return hipGetLastError();
+}
 
 size_t smallm_split_bytes(int M, int K, int N)
 {
@@ -330,6 +335,7 @@ size_t smallm_split_bytes(int M, int K, int N)
 hipError_t launch_gemv_smallm(const uint16_t *x, const MxSet &set0, int M, int K, hipStream_t st, std::string *desc,
                               float *part)
 {
+    if (mxm_handles(M, K, set0.count, part != nullptr)) return launch_gemv_mxm(x, set0, M, K, st, desc, part);
     MxSet set = set0;
     int tiles = 0;
     for (int i = 0; i < set.count; ++i) {

@@ -22,7 +22,8 @@ def dev():
 
 
 # (path, M, K): M = 1 with an even and an odd number of scale groups, small batches, prefill
-PATHS = [("gemv", 1, 4096), ("gemv", 1, 3968), ("gemv", 1, 12288), ("gemv", 4, 4096), ("gemv", 16, 4224),
+PATHS = [("gemv", 1, 4096), ("gemv", 1, 3968), ("gemv", 1, 12288), ("gemv", 4, 4096), ("gemv", 7, 2048),
+         ("gemv", 16, 4224),
          ("prefill", 300, 1024), ("gemv_t2", 1, 4096), ("gemv_t2", 1, 3968), ("prefill_t2", 300, 1024)]
 
 

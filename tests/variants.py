@@ -70,12 +70,39 @@ SELECT_CASES = [("gemv", 1, 20608, [70], "gemv_select<1>", "long")]
 # small batch (2 <= M <= 16): tiles per workgroup TB and K chunks in flight D (D = 0: one chunk)
 SMALLM_CASES = [
     ("gemv", 16, 4096, [4096], "gemv_smallm<2,0>", "tb2"),
-    ("gemv", 5, 4096, [12288], "gemv_smallm<4,0>", "tb4"),
+    ("gemv", 12, 4096, [12288], "gemv_smallm<4,0>", "tb4"),
     ("gemv", 16, 4096, [12288, 12288], "gemv_smallm<6,0>", "tb6"),
     ("gemv", 16, 12288, [4096], "gemv_smallm<1,4>", "tb1d4"),
     ("gemv", 2, 8192, [8192], "gemv_smallm<2,3>", "tb2d3"),
     ("gemv", 8, 8192, [16384], "gemv_smallm<4,2>", "tb4d2"),
     ("gemv", 3, 3968, [1000, 2000, 3000], "gemv_smallm<2,0>", "group3"),
+]
+
+# 2 <= M <= 8 with K a multiple of 1024 (and K <= 4096 without a workspace): the block-scaled
+# small-batch kernel, MB token blocks of four (MB = 1 for M <= 4), P ring slots (1 with one tile
+# per workgroup, 4 past 512 tiles)
+# The block-scaled small-batch kernel is switched off in the dispatch (the 8B step at M = 5 built
+# from its launches faulted the GPU, cause not found); its cases stay here, skipped.
+MXM_OFF = "block-scaled small-batch kernel switched off: the 8B step at M = 5 faulted the GPU, cause not found"
+
+MXM_CASES = [
+    ("gemv", 2, 4096, [4096], "gemv_mxm<1,1>", "one"),
+    ("gemv", 3, 1024, [700], "gemv_mxm<1,1>", "k1024"),
+    ("gemv", 4, 2048, [20000], "gemv_mxm<1,4>", "ring"),
+    ("gemv", 5, 3072, [12288], "gemv_mxm<2,4>", "m5"),
+    ("gemv", 6, 1024, [100, 200, 300], "gemv_mxm<2,1>", "group3"),
+    ("gemv", 7, 4096, [1000, 1000, 1000, 1000], "gemv_mxm<2,1>", "group4"),
+    ("gemv", 8, 4096, [30000], "gemv_mxm<2,4>", "m8"),
+    ("gemv", 8, 4096, [6144], "gemv_mxm<2,1>", "qkv"),
+]
+
+MXM_WS_CASES = [
+    ("gemv_ws", 2, 8192, [300], "gemv_mxm_split<1,1>", "ragged"),
+    ("gemv_ws", 5, 20480, [5000], "gemv_mxm_split<2,4>", "mxm_p4"),
+    ("gemv_ws", 8, 12288, [4096], "gemv_mxm_split<2,2>", "mxm_down"),
+    ("gemv_ws", 4, 5120, [5120], "gemv_mxm_split<1,2>", "mxm_onepair"),
+    ("gemv_ws", 3, 17408, [5120], "gemv_mxm_split<1,4>", "mxm_down27b"),
+    ("gemv_ws", 2, 4096, [4096], "gemv_mxm<1,1>", "mxm_nosplit"),
 ]
 
 # prefill: 128-row tiles (two workgroups per CU) unless 256-row tiles fill the GPU twice over
@@ -91,7 +118,8 @@ PREFILL_CASES = [
 WS_CASES = [
     ("gemv_ws", 16, 12288, [4096], "gemv_smallm_split<4>", "down"),
     ("gemv_ws", 2, 8192, [300], "gemv_smallm_split<1>", "ragged"),
-    ("gemv_ws", 5, 20480, [5000], "gemv_smallm_split<8>", "tb8"),
+    ("gemv_ws", 5, 20480, [5000], "gemv_smallm_split<8>", "tb8m5"),
+    ("gemv_ws", 12, 20480, [5000], "gemv_smallm_split<8>", "tb8"),
     ("gemv_ws", 16, 17408, [5120], "gemv_smallm_split<8>", "down27b"),
     ("gemv_ws", 9, 4224, [1000], "gemv_smallm_split<1>", "partial"),
     ("gemv_ws", 16, 4096, [4096], "gemv_smallm<2,0>", "nosplit"),
@@ -100,6 +128,7 @@ WS_CASES = [
 ]
 
 ALL_CASES = DECODE_CASES + DECODE_T2_CASES + SELECT_CASES + SMALLM_CASES + PREFILL_CASES + WS_CASES
+OFF_CASES = MXM_CASES + MXM_WS_CASES
 
 
 def case_id(c):
