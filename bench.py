@@ -567,13 +567,15 @@ def extra_single(dev, check):
     return out
 
 
-def extra_step(wl, dev, steps, label, chain=False, check_stride=0, ternary=False):
+def extra_step(wl, dev, steps, label, chain=False, check_stride=0, ternary=False, classes=True):
     st = Step(wl, dev, ternary=ternary)
     st.capture()
     ms = st.timed(max(5, steps // 2), 2)
     out = {"workload": label, "ms_per_step": round(ms, 4),
            "gbs": round(st.weight_bytes / ms / 1e6, 1), "tok_s": round(1e3 / ms, 1),
            "pct_hbm_peak": round(100 * st.weight_bytes / ms / 1e6 / HBM_PEAK_GBS, 2), "path": "graph"}
+    if classes:                               # launches by shape, each class replayed alone
+        out["per_launch_class"] = st.per_class_graph_us()
     if chain:
         c = ChainStep(st)
         msc = c.timed(max(5, steps // 2), 2)
@@ -778,7 +780,8 @@ def extra_small_batch_steps(dev, steps, check):
     for M in (2, 5, 8):
         wl = synth._decoder(synth.WL_DECODE_8B, f"decode-8b-m{M}", M, 36, 4096, 4096, 1024, 4096, 12288,
                             lm_vocab=151936)
-        st, o = extra_step(wl, dev, steps, f"8B decode step, M={M}", check_stride=64 if check else 0)
+        st, o = extra_step(wl, dev, steps, f"8B decode step, M={M}", check_stride=64 if check else 0,
+                           classes=False)
         out[f"m{M}"] = {"ms_per_step": o["ms_per_step"], "gbs": o["gbs"],
                         "tokens_per_s": round(M * 1e3 / o["ms_per_step"], 1)}
         if check:

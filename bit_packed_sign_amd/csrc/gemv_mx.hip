@@ -170,7 +170,7 @@ struct Slot {
     uint16_t s1[R][SP];
 };
 
-template <int SP, int P, int R, bool ODD, bool T2, int NW, bool TWO, int TT>
+template <int SP, int P, int R, bool ODD, bool T2, int NW, bool TWO, int TT, bool AL>
 __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(NW / 4, 4)))
 void gemv_mx_kernel(const uint16_t *__restrict__ x, int Ktq, int trg, const uint32_t *W0, const uint16_t *S0,
                     const uint32_t *W1, const uint16_t *S1, int N0, int N1, MxSet set)
@@ -283,9 +283,12 @@ void gemv_mx_kernel(const uint16_t *__restrict__ x, int Ktq, int trg, const uint
     const int hi = (G == 2 + (g >> 1)) ? m * 32 + 16 * (g & 1) : kZero;
 
     // The wave's A operands (its K-slice of the limbs) stay in registers for the whole
-    // kernel: 8 x 8 registers per pair, read from LDS once.
-    int8v A[SP][2][4];
-    int scA[SP][2];
+    // kernel: 8 x 8 registers per pair, read from LDS once.  AL: only one pair's operands are
+    // held, read from LDS where the pair's products run (long rows with one tile per workgroup:
+    // the registers of the other pairs let more waves share a CU).
+    int8v A[AL ? 1 : SP][2][4];
+    int scA[AL ? 1 : SP][2];
+    if constexpr (!AL)
 #pragma unroll
     for (int q = 0; q < SP; ++q)
 #pragma unroll
@@ -315,6 +318,16 @@ void gemv_mx_kernel(const uint16_t *__restrict__ x, int Ktq, int trg, const uint
                 const int pr = wp + NWP * q;
                 if (pr < npair) {                     // wave-uniform
                     const int gam = 8 * pr + 2 * g;
+                    if constexpr (AL) {
+#pragma unroll
+                        for (int h = 0; h < 2; ++h) {
+                            const uint8_t *blk = lds + (2 * pr + h) * 4 * kBlk;
+#pragma unroll
+                            for (int t = 0; t < 4; ++t) A[0][h][t] = load_a(blk + t * kBlk, lo, hi);
+                            scA[0][h] = (int)sc[(2 * pr + h) * 16 + m];
+                        }
+                    }
+                    const int qa = AL ? 0 : q;        // the pair's operands
 #pragma unroll
                     for (int r = 0; r < R; ++r) {
                         const uint32_t sv = ring[p].s[r][q];
@@ -328,26 +341,26 @@ void gemv_mx_kernel(const uint16_t *__restrict__ x, int Ktq, int trg, const uint
                             // MFMA t takes the group's words 2t and 2t + 1 (32 weights)
                             const u4v a0 = ring[p].w[r][q][0][0], a1 = ring[p].w[r][q][0][T2 ? 1 : 0];
                             const u4v b0 = ring[p].w[r][q][1][0], b1 = ring[p].w[r][q][1][T2 ? 1 : 0];
-                            ca = mma_b<0>(A[q][0][0], unpack_t2(a0.x, a0.y), scA[q][0], ca);
-                            cb = mma_b<0>(A[q][1][0], unpack_t2(b0.x, b0.y), scA[q][1], cb);
-                            ca = mma_b<1>(A[q][0][1], unpack_t2(a0.z, a0.w), scA[q][0], ca);
-                            cb = mma_b<1>(A[q][1][1], unpack_t2(b0.z, b0.w), scA[q][1], cb);
-                            ca = mma_b<2>(A[q][0][2], unpack_t2(a1.x, a1.y), scA[q][0], ca);
-                            cb = mma_b<2>(A[q][1][2], unpack_t2(b1.x, b1.y), scA[q][1], cb);
-                            ca = mma_b<3>(A[q][0][3], unpack_t2(a1.z, a1.w), scA[q][0], ca);
-                            cb = mma_b<3>(A[q][1][3], unpack_t2(b1.z, b1.w), scA[q][1], cb);
+                            ca = mma_b<0>(A[qa][0][0], unpack_t2(a0.x, a0.y), scA[qa][0], ca);
+                            cb = mma_b<0>(A[qa][1][0], unpack_t2(b0.x, b0.y), scA[qa][1], cb);
+                            ca = mma_b<1>(A[qa][0][1], unpack_t2(a0.z, a0.w), scA[qa][0], ca);
+                            cb = mma_b<1>(A[qa][1][1], unpack_t2(b0.z, b0.w), scA[qa][1], cb);
+                            ca = mma_b<2>(A[qa][0][2], unpack_t2(a1.x, a1.y), scA[qa][0], ca);
+                            cb = mma_b<2>(A[qa][1][2], unpack_t2(b1.x, b1.y), scA[qa][1], cb);
+                            ca = mma_b<3>(A[qa][0][3], unpack_t2(a1.z, a1.w), scA[qa][0], ca);
+                            cb = mma_b<3>(A[qa][1][3], unpack_t2(b1.z, b1.w), scA[qa][1], cb);
                             acc[r] = fmaf(s0, (ca[0] + ca[1]) + (ca[2] + ca[3]), acc[r]);
                             acc[r] = fmaf(s1, (cb[0] + cb[1]) + (cb[2] + cb[3]), acc[r]);
                         } else {
                             const u4v wa = ring[p].w[r][q][0][0], wb = ring[p].w[r][q][1][0];
-                            ca = mma<0>(A[q][0][0], wa.x, scA[q][0], ca);
-                            cb = mma<0>(A[q][1][0], wb.x, scA[q][1], cb);
-                            ca = mma<1>(A[q][0][1], wa.y, scA[q][0], ca);
-                            cb = mma<1>(A[q][1][1], wb.y, scA[q][1], cb);
-                            ca = mma<2>(A[q][0][2], wa.z, scA[q][0], ca);
-                            cb = mma<2>(A[q][1][2], wb.z, scA[q][1], cb);
-                            ca = mma<3>(A[q][0][3], wa.w, scA[q][0], ca);
-                            cb = mma<3>(A[q][1][3], wb.w, scA[q][1], cb);
+                            ca = mma<0>(A[qa][0][0], wa.x, scA[qa][0], ca);
+                            cb = mma<0>(A[qa][1][0], wb.x, scA[qa][1], cb);
+                            ca = mma<1>(A[qa][0][1], wa.y, scA[qa][0], ca);
+                            cb = mma<1>(A[qa][1][1], wb.y, scA[qa][1], cb);
+                            ca = mma<2>(A[qa][0][2], wa.z, scA[qa][0], ca);
+                            cb = mma<2>(A[qa][1][2], wb.z, scA[qa][1], cb);
+                            ca = mma<3>(A[qa][0][3], wa.w, scA[qa][0], ca);
+                            cb = mma<3>(A[qa][1][3], wb.w, scA[qa][1], cb);
                             // B held -w, so a group's partial is -(c0+c1+c2+c3)
                             acc[r] = fmaf(-s0, (ca[0] + ca[1]) + (ca[2] + ca[3]), acc[r]);
                             acc[r] = fmaf(-s1, (cb[0] + cb[1]) + (cb[2] + cb[3]), acc[r]);
@@ -399,7 +412,7 @@ constexpr size_t shm_bytes(int K, int rows_per_wg, int NW)
     return (size_t)(2 * ((K + 1023) >> 10)) * (4 * kBlk + 64) + (size_t)rows_per_wg * NW * 4;
 }
 
-template <int SP, int P, int R, bool ODD, bool T2, int NW, bool TWO, int TT>
+template <int SP, int P, int R, bool ODD, bool T2, int NW, bool TWO, int TT, bool AL>
 hipError_t launch_mx_t(const uint16_t *x, const MxSet &set0, int K, hipStream_t st, std::string *desc)
 {
     constexpr int NWP = NW / TT;
@@ -423,9 +436,9 @@ hipError_t launch_mx_t(const uint16_t *x, const MxSet &set0, int K, hipStream_t 
     const bool two = set.count == 2;
     if (desc) {                                        // describe the launch instead of making it
         char buf[128];
-        if (TT > 1)
-            snprintf(buf, sizeof buf, "gemv_mx<%d,%d,%d,%d,%d,%d,%d,%d> grid=%d", SP, P, R, (int)ODD, (int)T2, NW,
-                     (int)TWO, TT, grid);
+        if (TT > 1 || AL)
+            snprintf(buf, sizeof buf, "gemv_mx<%d,%d,%d,%d,%d,%d,%d,%d%s> grid=%d", SP, P, R, (int)ODD, (int)T2, NW,
+                     (int)TWO, TT, AL ? ",AL" : "", grid);
         else
             snprintf(buf, sizeof buf, "gemv_mx<%d,%d,%d,%d,%d,%d,%d> grid=%d", SP, P, R, (int)ODD, (int)T2, NW,
                      (int)TWO, grid);
@@ -433,11 +446,11 @@ hipError_t launch_mx_t(const uint16_t *x, const MxSet &set0, int K, hipStream_t 
         return hipSuccess;
     }
     static const hipError_t attr = hipFuncSetAttribute(
-        reinterpret_cast<const void *>(&gemv_mx_kernel<SP, P, R, ODD, T2, NW, TWO, TT>),
+        reinterpret_cast<const void *>(&gemv_mx_kernel<SP, P, R, ODD, T2, NW, TWO, TT, AL>),
         hipFuncAttributeMaxDynamicSharedMemorySize,
         (int)std::min<size_t>(shm_bytes(kMaxPairs * 1024, kMaxTileRows, NWP), kMaxLds));
     if (attr != hipSuccess) return attr;
-    hipLaunchKernelGGL((gemv_mx_kernel<SP, P, R, ODD, T2, NW, TWO, TT>), dim3(grid), dim3(64 * NW),
+    hipLaunchKernelGGL((gemv_mx_kernel<SP, P, R, ODD, T2, NW, TWO, TT, AL>), dim3(grid), dim3(64 * NW),
                        shm_bytes(K, rows_per_wg, NWP), st, x, K | (tiles / grid) << 16, (tiles % grid) | grid << 16,
                        set.W[0], set.S[0], two ? set.W[1] : nullptr, two ? set.S[1] : nullptr, set.N[0],
                        two ? set.N[1] : 0, set);
@@ -447,11 +460,11 @@ hipError_t launch_mx_t(const uint16_t *x, const MxSet &set0, int K, hipStream_t 
 // Launches of at most two matrices take their whole tile table from scalar arguments; several
 // wave groups per workgroup (TT > 1) need that table, so three or four matrices fall back to one
 // group of NW / TT waves.
-template <int SP, int P, int R, bool ODD, bool T2, int NW = 4, int TT = 1>
+template <int SP, int P, int R, bool ODD, bool T2, int NW = 4, int TT = 1, bool AL = false>
 hipError_t launch_mx(const uint16_t *x, const MxSet &set, int K, hipStream_t st, std::string *desc)
 {
-    if (set.count <= 2) return launch_mx_t<SP, P, R, ODD, T2, NW, true, TT>(x, set, K, st, desc);
-    return launch_mx_t<SP, P, R, ODD, T2, NW / TT, false, 1>(x, set, K, st, desc);
+    if (set.count <= 2) return launch_mx_t<SP, P, R, ODD, T2, NW, true, TT, AL>(x, set, K, st, desc);
+    return launch_mx_t<SP, P, R, ODD, T2, NW / TT, false, 1, AL>(x, set, K, st, desc);
 }
 
 template <bool ODD, bool T2>
@@ -478,9 +491,16 @@ hipError_t dispatch_mx(const uint16_t *x, const MxSet &set, int K, hipStream_t s
                  : one   ? launch_mx<1, 1, 2, ODD, T2, 12, 3>(x, set, K, st, desc)
                  : few16 ? launch_mx<1, 3, 1, ODD, T2>(x, set, K, st, desc)
                          : launch_mx<1, 2, 2, ODD, T2, 12, 3>(x, set, K, st, desc);
+    // Binary weights, 5..8 pairs (K = 5120 at the 27B shapes): eight waves with one pair each on
+    // 32-row tiles, up to 512 workgroups (measured: fewer, taller tiles beat 16-row ones, and beat
+    // four waves with a second pair on some of them).  Ternary rows keep the layouts below.
     // One 16-row tile per workgroup: as many waves as pairs (up to 16), one pair each, so no wave
     // carries a second pair on the critical path (the wider workgroups fit fewer per CU).
-    case 2: return one16 ? launch_mx<1, 1, 1, ODD, T2, 8>(x, set, K, st, desc)
+    case 2:
+        if constexpr (!T2)
+            return t32 <= 3 * 512 ? launch_mx<1, 1, 2, ODD, T2, 8>(x, set, K, st, desc)
+                                  : launch_mx<1, 2, 2, ODD, T2, 8>(x, set, K, st, desc);
+        return one16 ? launch_mx<1, 1, 1, ODD, T2, 8>(x, set, K, st, desc)
                  : one   ? launch_mx<2, 1, 2, ODD, T2>(x, set, K, st, desc)
                  : few16 ? launch_mx<2, 2, 1, ODD, T2>(x, set, K, st, desc) : launch_mx<2, 2, 2, ODD, T2>(x, set, K, st, desc);
     case 3: return one16 ? launch_mx<1, 1, 1, ODD, T2, 12>(x, set, K, st, desc)
@@ -490,9 +510,13 @@ hipError_t dispatch_mx(const uint16_t *x, const MxSet &set, int K, hipStream_t s
         if (one16) return launch_mx<1, 1, 1, ODD, T2, 16>(x, set, K, st, desc);
         if constexpr (T2) return launch_mx<4, 1, 1, ODD, T2>(x, set, K, st, desc);
         else return launch_mx<4, 1, 2, ODD, T2>(x, set, K, st, desc);
+    // 17..20 pairs (K = 17408 at the 27B shapes), binary: twelve waves of at most two pairs, each
+    // pair's A operands read where they are used (AL), so the twelve waves fit a CU; one 32-row tile
+    // per workgroup, or 16-row tiles two at a time past 256 of them.
     default:
         if constexpr (T2) return launch_mx<5, 1, 1, ODD, T2>(x, set, K, st, desc);
-        else return launch_mx<5, 1, 2, ODD, T2>(x, set, K, st, desc);
+        else return t32 <= 256 ? launch_mx<2, 1, 2, ODD, T2, 12, 1, true>(x, set, K, st, desc)
+                               : launch_mx<2, 2, 1, ODD, T2, 12, 1, true>(x, set, K, st, desc);
     }
 }
 

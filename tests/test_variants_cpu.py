@@ -32,21 +32,23 @@ def test_query_names_the_expected_variant(b1, case):
 def test_every_decode_branch_is_reached():
     """Each (pairs per wave, ring slots, rows per tile, waves) branch of the batch-1 kernel occurs
     with even and odd K / 128, with a partial last pair, and with one/two and three/four matrices."""
-    for cases in (DECODE_CASES, DECODE_T2_CASES):
+    for cases, expected_branches in ((DECODE_CASES, 6 + 2 + 3 + 2 + 2), (DECODE_T2_CASES, 6 + 4 + 3 + 2 + 1)):
+        # (SP 1: the two three-or-four-matrix fallbacks too; binary rows of 5..8 and 17..20 pairs
+        # have layouts of their own)
         seen = {}
         for op, M, K, Ns, exp, kind in cases:
             core = exp.split("<")[1].rstrip(">").split(",")
             branch = tuple(core[i] for i in (0, 1, 2, 5))   # SP, P, R, NW
             seen.setdefault(branch, set()).add((kind, core[3], core[6]))
-        expected_branches = 6 + 4 + 3 + 2 + 1          # SP 1: the two three-or-four-matrix fallbacks too
         assert len(seen) == expected_branches, sorted(seen)
         for branch, kinds in seen.items():
             assert {k for k, _, _ in kinds} == {"even", "odd", "part"}, (branch, kinds)
             assert {o for _, o, _ in kinds} == {"0", "1"}, (branch, kinds)
     # matrices past the scalar tile table occur in every pairs-per-wave class
     for cases in (DECODE_CASES, DECODE_T2_CASES):
-        classes = {((c[2] + 1023) // 1024 + 3) // 4 for c in cases if c[4].endswith(",0>")}
-        nws = {c[4].split(",")[5] for c in cases if c[4].endswith(",0>")}
+        table = [c for c in cases if c[4].split("<")[1].split(",")[6].rstrip(">") == "0"]
+        classes = {((c[2] + 1023) // 1024 + 3) // 4 for c in table}
+        nws = {c[4].split(",")[5] for c in table}
         assert classes == {1, 2, 3, 4, 5} and nws >= {"4", "12"}
 
 

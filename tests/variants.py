@@ -23,8 +23,8 @@ SP_K = {
 }
 
 
-def _mx(sp, p, r, odd, t2, nw, two, tt=1):
-    tail = f",{tt}" if tt > 1 else ""
+def _mx(sp, p, r, odd, t2, nw, two, tt=1, al=False):
+    tail = (f",{tt}" if tt > 1 or al else "") + (",AL" if al else "")
     return f"gemv_mx<{sp},{p},{r},{int(odd)},{int(t2)},{nw},{int(two)}{tail}>"
 
 
@@ -41,6 +41,10 @@ def _decode_cases(t2):
                         ([40000], (1, 2, 2, 12, 3)), ([100, 200, 300], (1, 1, 1, 4)),
                         ([10000, 10000, 10000], (1, 3, 1, 4)), ([7000, 7000, 7000], (1, 1, 2, 4)),
                         ([15000, 15000, 15000], (1, 2, 2, 4))]
+        elif sp == 2 and not t2:
+            # binary: eight waves of one pair on 32-row tiles; a two-slot ring past 1536 of them
+            branches = [([1000], (1, 1, 2, 8)), ([30000], (1, 1, 2, 8)), ([60000], (1, 2, 2, 8)),
+                        ([3000, 3000, 3000], (1, 1, 2, 8)), ([20000, 20000, 20000], (1, 2, 2, 8))]
         elif sp == 2:
             branches = [([1000], (1, 1, 1, 8)), ([10000], (2, 1, 2, 4)), ([20000], (2, 2, 1, 4)),
                         ([30000], (2, 2, 2, 4)), ([3000, 3000, 3000], (2, 1, 2, 4))]
@@ -50,14 +54,19 @@ def _decode_cases(t2):
         elif sp == 4:
             branches = [([1000], (1, 1, 1, 16)), ([6000], (4, 1, 1 if t2 else 2, 4)),
                         ([2000, 2000, 2000], (4, 1, 1 if t2 else 2, 4))]
+        elif t2:
+            branches = [([1000], (5, 1, 1, 4)), ([300, 400, 500], (5, 1, 1, 4))]
         else:
-            branches = [([1000], (5, 1, 1 if t2 else 2, 4)), ([300, 400, 500], (5, 1, 1 if t2 else 2, 4))]
+            # binary: twelve waves of up to two pairs, A operands read per pair (AL)
+            branches = [([1000], (2, 1, 2, 12, 1, True)), ([300, 400, 500], (2, 1, 2, 12, 1, True)),
+                        ([10000], (2, 2, 1, 12, 1, True)), ([3000, 3000, 3000], (2, 2, 1, 12, 1, True))]
         # the even-K class carries every branch; the odd and partial-pair classes every branch too,
         # but with smaller matrices where a branch allows it
         for Ns, br in branches:
             s_, p_, r_, nw_ = br[:4]
             tt = br[4] if len(br) > 4 else 1
-            cases.append((op, 1, K, Ns, _mx(s_, p_, r_, odd, t2, nw_, len(Ns) <= 2, tt), f"{kind}"))
+            al = br[5] if len(br) > 5 else False
+            cases.append((op, 1, K, Ns, _mx(s_, p_, r_, odd, t2, nw_, len(Ns) <= 2, tt, al), f"{kind}"))
     return cases
 
 
