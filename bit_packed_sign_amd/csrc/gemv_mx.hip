@@ -487,7 +487,15 @@ hipError_t dispatch_mx(const uint16_t *x, const MxSet &set, int K, hipStream_t s
     switch (SP) {
     // Past one tile per workgroup, one workgroup per CU of three groups of four waves: x is
     // loaded and converted once per CU instead of once per co-resident workgroup.
-    case 1: return one16 ? launch_mx<1, 1, 1, ODD, T2>(x, set, K, st, desc)
+    // Binary rows: past 256 16-row tiles, one 32-row tile per workgroup while that fits 256
+    // workgroups, then three wave groups per workgroup on 16-row tiles (measured on the 8B q|k|v
+    // and gate|up shapes).
+    case 1:
+        if (t16 > 256 && t32 <= 256) return launch_mx<1, 1, 2, ODD, T2>(x, set, K, st, desc);
+        if (t16 > 256 && t32 <= cap) return launch_mx<1, 1, 1, ODD, T2, 12, 3>(x, set, K, st, desc);
+        if constexpr (!T2)
+            if (!few16) return launch_mx<1, 1, 2, ODD, T2, 12, 3>(x, set, K, st, desc);
+        return one16 ? launch_mx<1, 1, 1, ODD, T2>(x, set, K, st, desc)
                  : one   ? launch_mx<1, 1, 2, ODD, T2, 12, 3>(x, set, K, st, desc)
                  : few16 ? launch_mx<1, 3, 1, ODD, T2>(x, set, K, st, desc)
                          : launch_mx<1, 2, 2, ODD, T2, 12, 3>(x, set, K, st, desc);

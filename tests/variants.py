@@ -36,11 +36,17 @@ def _decode_cases(t2):
         odd = (K // 128) % 2 == 1
         # (Ns, expected (SP, P, R, NW)) per branch of this pairs-per-wave class
         if sp == 1:
-            # past one tile per workgroup, three groups of four waves per workgroup (TT = 3)
-            branches = [([100], (1, 1, 1, 4)), ([20000], (1, 1, 2, 12, 3)), ([30000], (1, 3, 1, 4)),
-                        ([40000], (1, 2, 2, 12, 3)), ([100, 200, 300], (1, 1, 1, 4)),
-                        ([10000, 10000, 10000], (1, 3, 1, 4)), ([7000, 7000, 7000], (1, 1, 2, 4)),
-                        ([15000, 15000, 15000], (1, 2, 2, 4))]
+            # up to 256 16-row tiles one per workgroup; then one 32-row tile per workgroup; then
+            # three groups of four waves per workgroup (TT = 3) on 16-row tiles; a three-slot ring
+            # of 16-row tiles; past that 32-row tiles in three wave groups (a one-slot ring for
+            # binary rows, two slots for ternary ones).  Three or four matrices: one group of four
+            # waves in the same tiles.
+            big = (1, 2, 2, 12, 3) if t2 else (1, 1, 2, 12, 3)
+            big3 = (1, 2, 2, 4) if t2 else (1, 1, 2, 4)
+            branches = [([100], (1, 1, 1, 4)), ([6000], (1, 1, 2, 4)), ([20000], (1, 1, 1, 12, 3)),
+                        ([30000], (1, 3, 1, 4)), ([40000], big), ([100, 200, 300], (1, 1, 1, 4)),
+                        ([2000, 2000, 2000], (1, 1, 2, 4)), ([7000, 7000, 7000], (1, 1, 1, 4)),
+                        ([10000, 10000, 10000], (1, 3, 1, 4)), ([15000, 15000, 15000], big3)]
         elif sp == 2 and not t2:
             # binary: eight waves of one pair on 32-row tiles; a two-slot ring past 1536 of them
             branches = [([1000], (1, 1, 2, 8)), ([30000], (1, 1, 2, 8)), ([60000], (1, 2, 2, 8)),
@@ -133,7 +139,7 @@ WS_CASES = [
     ("gemv_ws", 9, 4224, [1000], "gemv_smallm_split<1>", "partial"),
     ("gemv_ws", 16, 4096, [4096], "gemv_smallm<2,0>", "nosplit"),
     ("gemv_ws", 1, 12288, [4096], "gemv_mx<1,1,1,0,0,12,1>", "m1"),
-    ("gemv_ws", 1, 4096, [151936], "gemv_mx<1,2,2,0,0,12,1,3>", "lmhead"),
+    ("gemv_ws", 1, 4096, [151936], "gemv_mx<1,1,2,0,0,12,1,3>", "lmhead"),
 ]
 
 ALL_CASES = DECODE_CASES + DECODE_T2_CASES + SELECT_CASES + SMALLM_CASES + PREFILL_CASES + WS_CASES
