@@ -277,6 +277,22 @@ class Step:
         t = np.sort([a.elapsed_time(b) * 1e3 for a, b in ev])
         return {f"p{q}": round(float(np.percentile(t, q)), 1) for q in (10, 50, 90)}
 
+    def shared_layer_ms(self, steps, warmup, layer_stages):
+        """The same dependent launches with every layer's projections replaced by layer 0's (its
+        weights then stay in the caches; lm_head keeps its own): the step's cost when no launch
+        waits on HBM for its weights.  layer_stages = stages per layer; the graph is rebuilt
+        afterwards with the real stages."""
+        orig = list(self.stages)
+        nl = (len(orig) // layer_stages) * layer_stages
+        self.stages = [(x, orig[s % layer_stages][1], orig[s % layer_stages][2], ys, nb) if s < nl
+                       else orig[s] for s, (x, Ws, Ss, ys, nb) in enumerate(orig)]
+        try:
+            self.capture()
+            return self.timed(steps, warmup)
+        finally:
+            self.stages = orig
+            self.capture()
+
     def per_class_graph_us(self, reps=10):
         """Launches grouped by shape (K and rows per launch): each group's launches of one step,
         in step order, captured into a graph of their own and replayed; HIP events on the replay
@@ -826,6 +842,8 @@ def main():
     pct = step.replay_percentiles_us()
     classes = step.per_class_graph_us()
     log(f"[bench] per launch class: {classes}")
+    ms_shared = step.shared_layer_ms(args.steps, args.warmup, 4)
+    log(f"[bench] same launches, every layer on layer 0's cache-resident weights: {ms_shared * 1e3:.1f} us")
     big = max(range(nl), key=lambda i: step.stages[i][4])
     paths = {
         "graph": {"ms_per_step": round(ms_graph, 5), "gbs": round(wbytes / ms_graph / 1e6, 1),
@@ -833,6 +851,10 @@ def main():
                   "launches": nl, "avg_launch_us_in_graph": round(ms_graph * 1e3 / nl, 3),
                   "eager_launch_sum_us": round(float(per.sum() * 1e3), 1),
                   "graph_floor_us_per_launch": round(floor_us, 3),
+                  "cache_resident_layer_us": round(ms_shared * 1e3, 1),
+                  "cache_resident_note": "the same 145 dependent launches with every layer reusing layer 0's "
+                                         "weights (27 MB, kept in L2 / MALL) and lm_head its own: the step's "
+                                         "cost when no launch waits on HBM for its weights",
                   "single_replay_us": pct,
                   "largest_launch_eager": {"stage": "lm_head 4096x151936", "bytes": step.stages[big][4],
                                            "us": round(float(per[big] * 1e3), 2),

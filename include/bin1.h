@@ -125,8 +125,9 @@ int bin1_gemv_noalloc(const void *x, const uint32_t *Wbits, const void *scales, 
 
 /* Prefill product, same arguments and result as bin1_gemv; tuned for M >= 256 (the
  * pages note that prompt processing is compute-bound: ["Bonsai 27B", section "Low-bit
- * kernels for hybrid attention"]).  Bit tiles are unpacked into LDS as fp16 +-scale
- * and contracted on the matrix cores with fp32 accumulation.  Correct for any M >= 1. */
+ * kernels for hybrid attention"]).  The sign bits are expanded in registers into fp16 +-|scale|
+ * matrix-core operands (activations staged through LDS) and contracted with fp32
+ * accumulation.  Correct for any M >= 1. */
 int bin1_gemm_prefill(const void *x, const uint32_t *Wbits, const void *scales, void *y,
                       int M, int K, int N, void *stream);
 
