@@ -386,20 +386,28 @@ done:
         tab.y = (unsigned long long)(tile >= te0 ? set.y[1] : set.y[0]);
     }
     __syncthreads();
-    // Merge: thread t finishes rows t, t+NT, ... of the workgroup's tiles in order.
-    for (int e = tid; e < my_tiles * 16 * R; e += NT) {
-        const int it = e / (16 * R), j = e - it * (16 * R);
+    // Merge: thread t finishes rows t, t+NT, ... of the workgroup's tiles in order.  The passes
+    // are workgroup-uniform and every lane takes part in the table shuffles (a lane outside a
+    // branch would read 0 from them); only the stores are per lane.
+    const int total = my_tiles * 16 * R;
+    for (int base = 0; base < total; base += NT) {
+        const int e = base + tid;
+        const bool live = e < total;
+        const int ec = live ? e : total - 1;
+        const int it = ec / (16 * R), j = ec - it * (16 * R);
         const int row = __shfl(tab.row0, it, kWave) + j, N = __shfl(tab.N, it, kWave);
         const unsigned long long yp = ((unsigned long long)(unsigned)__shfl((unsigned)(tab.y >> 32), it, kWave) << 32) |
                                       (unsigned)__shfl((unsigned)tab.y, it, kWave);
-        const float4v pr4 = *reinterpret_cast<const float4v *>(red + e * NWP);
-        float tot = (pr4[0] + pr4[1]) + (pr4[2] + pr4[3]);
+        if (live) {
+            const float4v pr4 = *reinterpret_cast<const float4v *>(red + e * NWP);
+            float tot = (pr4[0] + pr4[1]) + (pr4[2] + pr4[3]);
 #pragma unroll
-        for (int v = 4; v < NWP; v += 4) {            // waves 4.. of a wider pair split
-            const float4v prv = *reinterpret_cast<const float4v *>(red + e * NWP + v);
-            tot += (prv[0] + prv[1]) + (prv[2] + prv[3]);
+            for (int v = 4; v < NWP; v += 4) {        // waves 4.. of a wider pair split
+                const float4v prv = *reinterpret_cast<const float4v *>(red + e * NWP + v);
+                tot += (prv[0] + prv[1]) + (prv[2] + prv[3]);
+            }
+            if (row < N) reinterpret_cast<uint16_t *>(yp)[row] = f2h_rne(tot);
         }
-        if (row < N) reinterpret_cast<uint16_t *>(yp)[row] = f2h_rne(tot);
     }
 }
 

@@ -251,22 +251,23 @@ void gemv_mxm_kernel(const uint16_t *__restrict__ x, int M, int K, int tq, int t
         }
     }
     __syncthreads();
-    // ---- merge the 4 waves (fixed order) and store: entry e = (tile, block, lane)
+    // ---- merge the 4 waves (fixed order) and store: entry e = (tile, block, lane).  The entry
+    // count is a multiple of 64, so a pass covers whole waves, and the table shuffles come before
+    // any lane-dependent branch: a shuffle from a lane outside a branch reads 0.
     for (int e = threadIdx.x; e < nb * MB * 64; e += 256) {
         const int it = e / (MB * 64), rem = e - it * MB * 64, b = rem >> 6, l = rem & 63;
+        const int L = it & 63;
+        const int row = __shfl(tabl.row0, L, kWave) + (l & 15), N = __shfl(tabl.N, L, kWave);
+        const unsigned long long yp =
+            ((unsigned long long)(unsigned)__shfl((unsigned)(reinterpret_cast<unsigned long long>(tabl.y) >> 32), L, kWave)
+             << 32) |
+            (unsigned)__shfl((unsigned)reinterpret_cast<unsigned long long>(tabl.y), L, kWave);
         const float *src = red + ((it * MB + b) * 4) * 64 + l;
         const float tot = ((src[0] + src[64]) + src[128]) + src[192];
         const int tok = 4 * b + (l >> 4);
-        const int L = it & 63;
-        const int row = __shfl(tabl.row0, L, kWave) + (l & 15), N = __shfl(tabl.N, L, kWave);
         if (tok < M && row < N) {
-            if constexpr (SPLIT) {
-                part[((size_t)cw * M + tok) * N + row] = tot;
-            } else {
-                const unsigned long long yp = ((unsigned long long)(unsigned)__shfl((unsigned)(reinterpret_cast<unsigned long long>(tabl.y) >> 32), L, kWave) << 32) |
-                                              (unsigned)__shfl((unsigned)reinterpret_cast<unsigned long long>(tabl.y), L, kWave);
-                reinterpret_cast<uint16_t *>(yp)[(size_t)tok * N + row] = f2h_rne(tot);
-            }
+            if constexpr (SPLIT) part[((size_t)cw * M + tok) * N + row] = tot;
+            else reinterpret_cast<uint16_t *>(yp)[(size_t)tok * N + row] = f2h_rne(tot);
         }
     }
 }
@@ -319,11 +320,13 @@ hipError_t launch_p(const uint16_t *x, const MxSet &set, int M, int K, int tiles
 
 }  // namespace
 
-// Switched off: every single launch of this kernel that was run matched the oracle, but the 8B
-// decode step at M = 5 made of its launches faulted the GPU, and the cause is not known.  Until it
-// is, the dispatch sends every small batch to the fp16 kernel; launch_gemv_mxm stays for the
-// investigation (it checks the same conditions itself).
-constexpr bool kMxmEnabled = false;
+// The dispatch routes 2 <= M <= 8 here (mxm_handles) for tall products only: every workgroup
+// first turns its pair of every token's activations into limbs (about ten VALU operations per
+// element, at one wave per SIMD), which only pays off over many tiles.  Measured on the 8B step
+// at M = 8 (each launch class replayed alone): lm_head (9496 tiles, 38 per workgroup) 39.3 us
+// against 51.3 us on the fp16 kernel, but q|k|v 15.0 against 4.8, o 8.3 against 4.8, gate|up
+// 12.5 against 9.2, down 18.5 against 9.1.
+constexpr int kMxmMinTiles = 4096;
 
 bool mxm_shape_ok(int M, int K, int count, bool have_part)
 {
@@ -331,9 +334,11 @@ bool mxm_shape_ok(int M, int K, int count, bool have_part)
     return K <= kChunk || (have_part && count == 1);
 }
 
-bool mxm_handles(int M, int K, int count, bool have_part)
+bool mxm_handles(int M, int K, const MxSet &set, bool have_part)
 {
-    return kMxmEnabled && mxm_shape_ok(M, K, count, have_part);
+    int tiles = 0;
+    for (int i = 0; i < set.count; ++i) tiles += (set.N[i] + 15) / 16;
+    return tiles >= kMxmMinTiles && mxm_shape_ok(M, K, set.count, have_part);
 }
 
 hipError_t launch_gemv_mxm(const uint16_t *x, const MxSet &set0, int M, int K, hipStream_t st, std::string *desc,

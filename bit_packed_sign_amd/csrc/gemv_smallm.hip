@@ -335,7 +335,7 @@ size_t smallm_split_bytes(int M, int K, int N)
 hipError_t launch_gemv_smallm(const uint16_t *x, const MxSet &set0, int M, int K, hipStream_t st, std::string *desc,
                               float *part)
 {
-    if (mxm_handles(M, K, set0.count, part != nullptr)) return launch_gemv_mxm(x, set0, M, K, st, desc, part);
+    if (mxm_handles(M, K, set0, part != nullptr)) return launch_gemv_mxm(x, set0, M, K, st, desc, part);
     MxSet set = set0;
     int tiles = 0;
     for (int i = 0; i < set.count; ++i) {

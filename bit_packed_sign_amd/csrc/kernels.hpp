@@ -84,8 +84,8 @@ size_t smallm_split_bytes(int M, int K, int N);
 hipError_t launch_smallm_reduce(const float *part, int nchunk, int MN, uint16_t *y, hipStream_t st);
 // 2 <= M <= 8 on the block-scaled matrix cores (gemv_mxm.hip): K a multiple of 1024, and K <= 4096
 // unless a one-matrix product brings the split scratch.  launch_gemv_smallm routes such shapes there
-// while the kernel is enabled (mxm_handles); it is switched off at present.
-bool mxm_handles(int M, int K, int count, bool have_part);
+// when they are tall enough to pay for the kernel's activation conversion (mxm_handles).
+bool mxm_handles(int M, int K, const MxSet &set, bool have_part);
 hipError_t launch_gemv_mxm(const uint16_t *x, const MxSet &set, int M, int K, hipStream_t st, std::string *desc,
                            float *part);
 hipError_t launch_prefill(const uint16_t *x, const uint32_t *W, const uint16_t *S, uint16_t *y,

@@ -11,7 +11,7 @@ import torch
 import bit_packed_sign_amd as b1
 from bit_packed_sign_amd import synth
 from parity import TOL, dev_tensors, norm_err
-from variants import ALL_CASES, MXM_OFF, OFF_CASES, case_id
+from variants import ALL_CASES, case_id
 
 pytestmark = pytest.mark.gpu
 
@@ -34,8 +34,7 @@ def _inputs(seed, M, K, Ns, t2):
     return x, mats
 
 
-@pytest.mark.parametrize("case", ALL_CASES + [pytest.param(c, id=case_id(c), marks=pytest.mark.skip(reason=MXM_OFF))
-                                  for c in OFF_CASES], ids=case_id)
+@pytest.mark.parametrize("case", ALL_CASES, ids=case_id)
 def test_dispatch_branch_matches_oracle(orc, dev, case):
     op, M, K, Ns, expect, _ = case
     t2 = op.endswith("t2")

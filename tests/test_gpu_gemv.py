@@ -255,3 +255,57 @@ def test_empty_products_are_no_ops(orc, dev):
                              Wd).shape) == (0, 40)
     score, order = b1.rank_rows_by_scale(Sd[:0])
     assert score.numel() == 0 and order.numel() == 0
+
+
+def _tile_rows(grid, locals_, wgs, N):
+    """Rows of the workgroups' local tiles (tile = local * grid + workgroup, 16 rows each)."""
+    rows = [r for k in locals_ for b in wgs for r in range((k * grid + b) * 16, (k * grid + b) * 16 + 16)]
+    return np.array(sorted({r for r in rows if r < N}))
+
+
+@pytest.mark.parametrize("op,K,N", [("gemv", 17408, 139264), ("gemv_t2", 16384, 139264)])
+def test_tall_matrix_every_tile_of_a_workgroup(orc, dev, op, K, N):
+    """Tall products on the 16-row-tile layouts give a workgroup 34 tiles, so the last merge pass
+    covers tiles 32 and 33 with only lanes 0..31 active.  The tile table is read by lane shuffles
+    in every pass, with every lane taking part; every output must be written (the buffer starts as
+    NaN), and the rows of local tiles 31..33 of several workgroups match the oracle."""
+    t2 = op == "gemv_t2"
+    desc = b1.kernel_variant(op, 1, K, [N])
+    grid = int(desc.split("grid=")[1])
+    assert (N // 16 + grid - 1) // grid == 34, desc
+    r = synth.rng_for(0, synth.WL_TEST, 7700 + K)
+    x = synth.activations(r, 1, K)
+    W = synth.ternary_words_fast(r, N, K) if t2 else synth.sign_words(r, N, K)
+    S = synth.group_scales(r, N, K)
+    xd, Wd, Sd = dev_tensors(dev, x, W, S)
+    y = torch.full((1, N), float("nan"), dtype=torch.float16, device=dev)
+    (b1.gemv_t2 if t2 else b1.gemv)(xd, Wd, Sd, out=y)
+    yy = y.float().cpu().numpy()
+    assert np.all(np.isfinite(yy)), f"{int(np.sum(~np.isfinite(yy)))} outputs not written"
+    rows = np.union1d(_tile_rows(grid, [0, 31, 32, 33], [0, 1, grid // 2, grid - 1], N),
+                      sample_rows(synth.rng_for(0, synth.WL_TEST, 7701 + K), N))
+    ref, nrm = (orc.gemv_t2_rows if t2 else orc.gemv_rows)(x, W, S, rows)
+    assert norm_err(yy[:, rows], ref, nrm) <= TOL
+
+
+@pytest.mark.parametrize("M", [2, 5, 7])
+def test_small_batch_many_tiles_per_workgroup(orc, dev, M):
+    """The block-scaled small-batch kernel at an lm_head shape gives each workgroup 37 or 38 tiles;
+    with M not a multiple of 4 the last token block leaves lanes idle at the store, and the merge
+    must still read every tile's output pointer and rows with all lanes.  Every output written,
+    sampled rows of tiles 15..37 against the oracle."""
+    K, N = 4096, 151936
+    desc = b1.kernel_variant("gemv", M, K, [N])
+    assert desc.startswith("gemv_mxm<"), desc
+    grid = int(desc.split("grid=")[1])
+    r = synth.rng_for(0, synth.WL_TEST, 7800 + M)
+    x, W, S = synth.activations(r, M, K), synth.sign_words(r, N, K), synth.group_scales(r, N, K)
+    xd, Wd, Sd = dev_tensors(dev, x, W, S)
+    y = torch.full((M, N), float("nan"), dtype=torch.float16, device=dev)
+    b1.gemv(xd, Wd, Sd, out=y)
+    yy = y.float().cpu().numpy()
+    assert np.all(np.isfinite(yy)), f"{int(np.sum(~np.isfinite(yy)))} outputs not written"
+    rows = np.union1d(_tile_rows(grid, [0, 15, 16, 17, 31, 36, 37], [0, 1, 23, grid - 1], N),
+                      sample_rows(synth.rng_for(0, synth.WL_TEST, 7801 + M), N))
+    ref, nrm = orc.gemv_rows(x, W, S, rows)
+    assert norm_err(yy[:, rows], ref, nrm) <= TOL

@@ -9,8 +9,9 @@ captured into a HIP graph and replayed.
 * the ternary 8B step (2-bit slots), every output;
 * the 8B MLP at batch 16 (72 stages on the small-batch kernel; down splits K over workgroups with
   the step's workspace), all 16 tokens of every eighth row plus the edge rows of every product;
-* the 8B step at M = 5 on the block-scaled small-batch kernel, every 16th row of every product
-  (skipped while that kernel is switched off).
+* the 8B step at M = 5, every 16th row of every product; its lm_head launch runs on the
+  block-scaled small-batch kernel with 38 tiles per workgroup (the merge's tile-table shuffles
+  past lane 16 with part of a token block idle).
 Every replay must reproduce the eager outputs bit for bit, with eager work between replays.
 Concurrent calls on two streams give the same outputs as one stream."""
 import numpy as np
@@ -102,15 +103,13 @@ def test_step_mlp16_every_product(orc, dev):
                 {0: "gemv_smallm<6,0>", 1: "gemv_smallm_split<4>"})
 
 
-@pytest.mark.skip(reason="block-scaled small-batch kernel switched off: this step built from its launches "
-                         "faulted the GPU, cause not found")
 def test_step_8b_m5_sampled_rows(orc, dev):
     """The 8B decode step at M = 5 tokens (the verify pass of speculative decoding with four drafted
     tokens) as the benchmark times it: all five tokens of every 16th row of every product."""
     wl = synth._decoder(synth.WL_DECODE_8B, "decode-8b-m5", 5, 36, 4096, 4096, 1024, 4096, 12288,
                         lm_vocab=151936)
     _check_step(orc, dev, wl, False, 16,
-                {0: "gemv_mxm<2,1>", 1: "gemv_mxm<2,1>", 2: "gemv_mxm<2,4>", 3: "gemv_mxm_split<2,2>",
+                {0: "gemv_smallm<2,0>", 1: "gemv_smallm<2,0>", 2: "gemv_smallm<6,0>", 3: "gemv_smallm_split<4>",
                  144: "gemv_mxm<2,4>"})
 
 

@@ -4,7 +4,7 @@ Here (no GPU) the table is checked against the query, and the table is checked t
 branch of the dispatch."""
 import pytest
 
-from variants import ALL_CASES, DECODE_CASES, DECODE_T2_CASES, MXM_OFF, OFF_CASES, case_id
+from variants import ALL_CASES, DECODE_CASES, DECODE_T2_CASES, case_id
 
 
 @pytest.fixture(scope="module")
@@ -17,8 +17,7 @@ def b1():
     return b1
 
 
-@pytest.mark.parametrize("case", ALL_CASES + [pytest.param(c, id=case_id(c), marks=pytest.mark.skip(reason=MXM_OFF))
-                                  for c in OFF_CASES], ids=case_id)
+@pytest.mark.parametrize("case", ALL_CASES, ids=case_id)
 def test_query_names_the_expected_variant(b1, case):
     op, M, K, Ns, expect, _ = case
     got = b1.kernel_variant(op, M, K, Ns)

@@ -93,31 +93,25 @@ SMALLM_CASES = [
     ("gemv", 3, 3968, [1000, 2000, 3000], "gemv_smallm<2,0>", "group3"),
 ]
 
-# 2 <= M <= 8 with K a multiple of 1024 (and K <= 4096 without a workspace): the block-scaled
-# small-batch kernel, MB token blocks of four (MB = 1 for M <= 4), P ring slots (1 with one tile
-# per workgroup, 4 past 512 tiles)
-# The block-scaled small-batch kernel is switched off in the dispatch (the 8B step at M = 5 built
-# from its launches faulted the GPU, cause not found); its cases stay here, skipped.
-MXM_OFF = "block-scaled small-batch kernel switched off: the 8B step at M = 5 faulted the GPU, cause not found"
-
+# 2 <= M <= 8 with K a multiple of 1024 (and K <= 4096 without a workspace) and at least 4096
+# tiles of 16 rows: the block-scaled small-batch kernel, MB token blocks of four (MB = 1 for
+# M <= 4), a four-slot ring (every such product gives a workgroup 16 tiles or more); past 43 tiles
+# per workgroup (MB = 2) the grid grows.  One tile fewer stays on the fp16 kernel.
 MXM_CASES = [
-    ("gemv", 2, 4096, [4096], "gemv_mxm<1,1>", "one"),
-    ("gemv", 3, 1024, [700], "gemv_mxm<1,1>", "k1024"),
-    ("gemv", 4, 2048, [20000], "gemv_mxm<1,4>", "ring"),
-    ("gemv", 5, 3072, [12288], "gemv_mxm<2,4>", "m5"),
-    ("gemv", 6, 1024, [100, 200, 300], "gemv_mxm<2,1>", "group3"),
-    ("gemv", 7, 4096, [1000, 1000, 1000, 1000], "gemv_mxm<2,1>", "group4"),
-    ("gemv", 8, 4096, [30000], "gemv_mxm<2,4>", "m8"),
-    ("gemv", 8, 4096, [6144], "gemv_mxm<2,1>", "qkv"),
+    ("gemv", 2, 4096, [65536], "gemv_mxm<1,4>", "tall"),
+    ("gemv", 3, 1024, [70000], "gemv_mxm<1,4>", "k1024"),
+    ("gemv", 5, 4096, [70000], "gemv_mxm<2,4>", "m5"),
+    ("gemv", 6, 2048, [30000, 30000, 10000], "gemv_mxm<2,4>", "group3"),
+    ("gemv", 7, 4096, [20000, 20000, 20000, 10000], "gemv_mxm<2,4>", "group4"),
+    ("gemv", 8, 4096, [180000], "gemv_mxm<2,4>", "capped"),
+    ("gemv", 8, 4096, [65520], "gemv_smallm<6,0>", "below"),
 ]
 
 MXM_WS_CASES = [
-    ("gemv_ws", 2, 8192, [300], "gemv_mxm_split<1,1>", "ragged"),
-    ("gemv_ws", 5, 20480, [5000], "gemv_mxm_split<2,4>", "mxm_p4"),
-    ("gemv_ws", 8, 12288, [4096], "gemv_mxm_split<2,2>", "mxm_down"),
-    ("gemv_ws", 4, 5120, [5120], "gemv_mxm_split<1,2>", "mxm_onepair"),
-    ("gemv_ws", 3, 17408, [5120], "gemv_mxm_split<1,4>", "mxm_down27b"),
-    ("gemv_ws", 2, 4096, [4096], "gemv_mxm<1,1>", "mxm_nosplit"),
+    ("gemv_ws", 2, 8192, [65536], "gemv_mxm_split<1,4>", "split2"),
+    ("gemv_ws", 5, 12288, [70000], "gemv_mxm_split<2,4>", "split3"),
+    ("gemv_ws", 3, 5120, [66000], "gemv_mxm_split<1,4>", "onepair"),
+    ("gemv_ws", 2, 8192, [300], "gemv_smallm_split<1>", "ragged"),
 ]
 
 # prefill: 128-row tiles (two workgroups per CU) unless 256-row tiles fill the GPU twice over
@@ -132,8 +126,6 @@ PREFILL_CASES = [
 # chunk, TB tiles each) then the chunk reduction; shapes without a split run as bin1_gemv
 WS_CASES = [
     ("gemv_ws", 16, 12288, [4096], "gemv_smallm_split<4>", "down"),
-    ("gemv_ws", 2, 8192, [300], "gemv_smallm_split<1>", "ragged"),
-    ("gemv_ws", 5, 20480, [5000], "gemv_smallm_split<8>", "tb8m5"),
     ("gemv_ws", 12, 20480, [5000], "gemv_smallm_split<8>", "tb8"),
     ("gemv_ws", 16, 17408, [5120], "gemv_smallm_split<8>", "down27b"),
     ("gemv_ws", 9, 4224, [1000], "gemv_smallm_split<1>", "partial"),
@@ -142,8 +134,8 @@ WS_CASES = [
     ("gemv_ws", 1, 4096, [151936], "gemv_mx<1,1,2,0,0,12,1,3>", "lmhead"),
 ]
 
-ALL_CASES = DECODE_CASES + DECODE_T2_CASES + SELECT_CASES + SMALLM_CASES + PREFILL_CASES + WS_CASES
-OFF_CASES = MXM_CASES + MXM_WS_CASES
+ALL_CASES = (DECODE_CASES + DECODE_T2_CASES + SELECT_CASES + SMALLM_CASES + MXM_CASES + PREFILL_CASES + WS_CASES
+             + MXM_WS_CASES)
 
 
 def case_id(c):
