@@ -120,6 +120,9 @@ struct TileTab {
     int row0, N;
 };
 
+typedef int int4v __attribute__((ext_vector_type(4)));
+constexpr int kTabBytes = 64 * 16;                   // the merge's copy of the table in LDS
+
 template <int R>
 __device__ __forceinline__ TileTab tile_tab(const MxSet &set, int tile)
 {
@@ -277,7 +280,10 @@ void gemv_mx_kernel(const uint16_t *__restrict__ x, int Ktq, int trg, const uint
     __syncthreads();                                  // limbs visible
 
     const uint32_t *sc = reinterpret_cast<const uint32_t *>(lds + nseg * 4 * kBlk);
-    float *red = reinterpret_cast<float *>(lds + nseg * (4 * kBlk + 64));   // merge table, after the limbs
+    // after the limbs: the tile table for the merge (64 entries of row0, N, output pointer), then
+    // the merge table
+    int4v *tabl = reinterpret_cast<int4v *>(lds + nseg * (4 * kBlk + 64));
+    float *red = reinterpret_cast<float *>(lds + nseg * (4 * kBlk + 64) + kTabBytes);
     const int m = lane & 15, G = m >> 2;
     const int lo = (G == (g >> 1)) ? m * 32 + 16 * (g & 1) : kZero;
     const int hi = (G == 2 + (g >> 1)) ? m * 32 + 16 * (g & 1) : kZero;
@@ -385,39 +391,39 @@ done:
         const int tile = blockIdx.x + lane * grid;
         tab.y = (unsigned long long)(tile >= te0 ? set.y[1] : set.y[0]);
     }
+    if (wave == 0) tabl[lane] = int4v{tab.row0, tab.N, (int)(unsigned)tab.y, (int)(unsigned)(tab.y >> 32)};
     __syncthreads();
-    // Merge: thread t finishes rows t, t+NT, ... of the workgroup's tiles in order.  The passes
-    // are workgroup-uniform and every lane takes part in the table shuffles (a lane outside a
-    // branch would read 0 from them); only the stores are per lane.
-    const int total = my_tiles * 16 * R;
-    for (int base = 0; base < total; base += NT) {
-        const int e = base + tid;
-        const bool live = e < total;
-        const int ec = live ? e : total - 1;
-        const int it = ec / (16 * R), j = ec - it * (16 * R);
-        const int row = __shfl(tab.row0, it, kWave) + j, N = __shfl(tab.N, it, kWave);
-        const unsigned long long yp = ((unsigned long long)(unsigned)__shfl((unsigned)(tab.y >> 32), it, kWave) << 32) |
-                                      (unsigned)__shfl((unsigned)tab.y, it, kWave);
-        if (live) {
-            const float4v pr4 = *reinterpret_cast<const float4v *>(red + e * NWP);
-            float tot = (pr4[0] + pr4[1]) + (pr4[2] + pr4[3]);
+    // Merge: thread t finishes rows t, t+NT, ... of the workgroup's tiles in order, with the
+    // tile's entry read from the LDS table (per lane: no lane depends on another being active).
+    // The empty asm takes the entry and the partials together, so both LDS reads are issued
+    // before one wait (left alone, the compiler moves the partials' read into the store's
+    // branch, behind the entry's wait).
+    for (int e = tid; e < my_tiles * 16 * R; e += NT) {
+        const int it = e / (16 * R), j = e - it * (16 * R);
+        const int4v t = tabl[it];
+        float4v pr[NWP / 4];                          // waves 4.. of a wider pair split in pr[1]
 #pragma unroll
-            for (int v = 4; v < NWP; v += 4) {        // waves 4.. of a wider pair split
-                const float4v prv = *reinterpret_cast<const float4v *>(red + e * NWP + v);
-                tot += (prv[0] + prv[1]) + (prv[2] + prv[3]);
-            }
-            if (row < N) reinterpret_cast<uint16_t *>(yp)[row] = f2h_rne(tot);
-        }
+        for (int v = 0; v < NWP / 4; ++v) pr[v] = *reinterpret_cast<const float4v *>(red + e * NWP + 4 * v);
+#pragma unroll
+        for (int v = 0; v < NWP / 4; ++v) asm volatile("" ::"v"(pr[v]));
+        asm volatile("" ::"v"(t));
+        float tot = (pr[0][0] + pr[0][1]) + (pr[0][2] + pr[0][3]);
+#pragma unroll
+        for (int v = 1; v < NWP / 4; ++v) tot += (pr[v][0] + pr[v][1]) + (pr[v][2] + pr[v][3]);
+        const int row = t[0] + j;
+        if (row < t[1])
+            reinterpret_cast<uint16_t *>(((unsigned long long)(unsigned)t[3] << 32) | (unsigned)t[2])[row] = f2h_rne(tot);
     }
 }
 
 constexpr int kMaxPairs = 20;                         // K <= 20480 (A operands fit in registers)
 constexpr int kMaxTileRows = 2048;                     // rows per workgroup held in the merge table
 constexpr size_t kMaxLds = 160 * 1024;                 // LDS per workgroup on gfx950
-// LDS: limb blocks and exponents for K, then the merge table [tile][16R rows][NW waves] fp32.
+// LDS: limb blocks and exponents for K, the tile table, then the merge table
+// [tile][16R rows][NW waves] fp32.
 constexpr size_t shm_bytes(int K, int rows_per_wg, int NW)
 {
-    return (size_t)(2 * ((K + 1023) >> 10)) * (4 * kBlk + 64) + (size_t)rows_per_wg * NW * 4;
+    return (size_t)(2 * ((K + 1023) >> 10)) * (4 * kBlk + 64) + kTabBytes + (size_t)rows_per_wg * NW * 4;
 }
 
 template <int SP, int P, int R, bool ODD, bool T2, int NW, bool TWO, int TT, bool AL>
@@ -436,20 +442,25 @@ hipError_t launch_mx_t(const uint16_t *x, const MxSet &set0, int K, hipStream_t 
     // table.
     const int cap = TT > 1 ? 256
                   : NW == 4 ? (SP == 1 ? 3 * 256 : SP == 2 ? 2 * 256 : 256) : (NW == 8 && SP == 1 ? 2 * 256 : 256);
-    // tiles per workgroup: at most what the merge table holds and the one-per-lane tile table
+    // tiles per workgroup: at most what the one-per-lane tile table holds, and what the merge
+    // table holds (kMaxTileRows, and the LDS left after this K's limbs)
     constexpr int kMaxT = kMaxTileRows / (16 * R) < 64 ? kMaxTileRows / (16 * R) : 64;
-    const int need = (tiles + kMaxT - 1) / kMaxT, units = (tiles + TT - 1) / TT;
+    const int ldsT = (int)((kMaxLds - shm_bytes(K, 0, NWP)) / ((size_t)16 * R * NWP * 4));
+    const int maxT = ldsT < kMaxT ? ldsT : kMaxT;
+    const int need = (tiles + maxT - 1) / maxT, units = (tiles + TT - 1) / TT;
     const int grid = units < cap ? units : (need > cap ? need : cap);
     const int rows_per_wg = (tiles + grid - 1) / grid * 16 * R;
+    const size_t shm = shm_bytes(K, rows_per_wg, NWP);
+    if (shm > kMaxLds) return hipErrorInvalidValue;
     const bool two = set.count == 2;
     if (desc) {                                        // describe the launch instead of making it
-        char buf[128];
+        char buf[160];
         if (TT > 1 || AL)
-            snprintf(buf, sizeof buf, "gemv_mx<%d,%d,%d,%d,%d,%d,%d,%d%s> grid=%d", SP, P, R, (int)ODD, (int)T2, NW,
-                     (int)TWO, TT, AL ? ",AL" : "", grid);
+            snprintf(buf, sizeof buf, "gemv_mx<%d,%d,%d,%d,%d,%d,%d,%d%s> lds=%zu grid=%d", SP, P, R, (int)ODD,
+                     (int)T2, NW, (int)TWO, TT, AL ? ",AL" : "", shm, grid);
         else
-            snprintf(buf, sizeof buf, "gemv_mx<%d,%d,%d,%d,%d,%d,%d> grid=%d", SP, P, R, (int)ODD, (int)T2, NW,
-                     (int)TWO, grid);
+            snprintf(buf, sizeof buf, "gemv_mx<%d,%d,%d,%d,%d,%d,%d> lds=%zu grid=%d", SP, P, R, (int)ODD, (int)T2,
+                     NW, (int)TWO, shm, grid);
         desc->append(desc->empty() ? "" : ";").append(buf);
         return hipSuccess;
     }
@@ -459,7 +470,7 @@ hipError_t launch_mx_t(const uint16_t *x, const MxSet &set0, int K, hipStream_t 
         (int)std::min<size_t>(shm_bytes(kMaxPairs * 1024, kMaxTileRows, NWP), kMaxLds));
     if (attr != hipSuccess) return attr;
     hipLaunchKernelGGL((gemv_mx_kernel<SP, P, R, ODD, T2, NW, TWO, TT, AL>), dim3(grid), dim3(64 * NW),
-                       shm_bytes(K, rows_per_wg, NWP), st, x, K | (tiles / grid) << 16, (tiles % grid) | grid << 16,
+                       shm, st, x, K | (tiles / grid) << 16, (tiles % grid) | grid << 16,
                        set.W[0], set.S[0], two ? set.W[1] : nullptr, two ? set.S[1] : nullptr, set.N[0],
                        two ? set.N[1] : 0, set);
     return hipGetLastError();

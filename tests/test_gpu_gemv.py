@@ -266,9 +266,10 @@ def _tile_rows(grid, locals_, wgs, N):
 @pytest.mark.parametrize("op,K,N", [("gemv", 17408, 139264), ("gemv_t2", 16384, 139264)])
 def test_tall_matrix_every_tile_of_a_workgroup(orc, dev, op, K, N):
     """Tall products on the 16-row-tile layouts give a workgroup 34 tiles, so the last merge pass
-    covers tiles 32 and 33 with only lanes 0..31 active.  The tile table is read by lane shuffles
-    in every pass, with every lane taking part; every output must be written (the buffer starts as
-    NaN), and the rows of local tiles 31..33 of several workgroups match the oracle."""
+    covers tiles 32 and 33 with only lanes 0..31 active, and those lanes need the table entries of
+    tiles 32 and 33 (held by lanes 32 and 33 of the tile table, read from its LDS copy).  Every
+    output must be written (the buffer starts as NaN), and the rows of local tiles 31..33 of
+    several workgroups match the oracle."""
     t2 = op == "gemv_t2"
     desc = b1.kernel_variant(op, 1, K, [N])
     grid = int(desc.split("grid=")[1])

@@ -2,6 +2,7 @@
 variant the dispatch code picks; the GPU tests then run exactly those shapes against the oracle.
 Here (no GPU) the table is checked against the query, and the table is checked to reach every
 branch of the dispatch."""
+import numpy as np
 import pytest
 
 from variants import ALL_CASES, DECODE_CASES, DECODE_T2_CASES, case_id
@@ -61,3 +62,26 @@ def test_query_rejects_bad_arguments(b1):
         b1.kernel_variant("prefill", 4, 128, [10, 20])        # prefill takes one matrix
     with pytest.raises(Bin1Error):
         b1.kernel_variant("gemv", 1, 128, [1, 2, 3, 4, 5])    # at most four matrices
+
+
+def test_batch1_launches_fit_the_lds(b1):
+    """The batch-1 kernel holds a K-long slice of limbs, a tile table and one fp32 partial per
+    (row, wave) of its tiles in LDS; the launcher bounds the tiles per workgroup so that this stays
+    within the 160 KB a workgroup can have, also at the longest rows (K = 20480) and the tallest
+    matrices the argument rules allow (N < 2^24 - 64, the bits under 2 GiB).  Every launch of a
+    sweep over K and N must describe an LDS size within the limit."""
+    lim = 160 * 1024
+    seen = 0
+    for op, bits in (("gemv", 1), ("gemv_t2", 2)):
+        for K in (128, 1024, 3968, 4096, 5120, 8192, 12288, 16384, 17408, 19456, 20352, 20480):
+            nmax = min((1 << 24) - 65, ((1 << 31) - 1) // (K * bits // 8))
+            Ns = sorted({int(n) for n in np.geomspace(1, nmax, 48)} | {nmax})
+            for N in Ns:
+                for group in ([N], [N // 2 + 1, N // 2 + 1], [N // 3 + 1] * 3):
+                    desc = b1.kernel_variant(op, 1, K, group)
+                    for launch in desc.split(";"):
+                        if launch.startswith("gemv_mx<"):
+                            lds = int(launch.split("lds=")[1].split()[0])
+                            assert 0 < lds <= lim, (op, K, group, launch)
+                            seen += 1
+    assert seen > 1000
