@@ -122,6 +122,29 @@ def stream_read(device, nbytes=4 << 30, reps=10):
             "kernel": "bin1_stream_read (16-byte nontemporal loads, a contiguous 16*grid*256-byte front per round)"}
 
 
+def mfma_rate(device, reps=10):
+    """The fp16 matrix-core rate this GPU sustains, measured with the library's calibration kernel
+    (bin1_mfma_rate: independent 32x32x16 fp16 products and nothing else, 1024 workgroups of one
+    or two waves per SIMD).  The part's clock follows its power, which follows the operands' bit
+    activity, so the reference uses normally distributed fp16 operands (as activations and
+    expanded +-scales are); products of all-ones operands are reported beside it."""
+    import torch
+    import bit_packed_sign_amd as b1
+    grid, iters = 1024, 1000
+    g = torch.Generator().manual_seed(0)
+    ops = {"random": torch.randn((2, 64, 8), generator=g).half().to(device),
+           "ones": torch.ones((2, 64, 8), dtype=torch.float16, device=device)}
+    out = {}
+    for name, op in ops.items():
+        for waves in (4, 8):
+            sink = torch.empty(grid * waves, dtype=torch.float32, device=device)
+            ms = time_fn(lambda: b1.mfma_rate(op, sink, grid, waves, iters), reps, warm=PREFILL_WARM)
+            out[f"{name}_waves_per_simd_{waves // 4}"] = round(grid * waves * iters * 12 * 32768 / (ms * 1e-3) / 1e12, 1)
+    best = max(v for k, v in out.items() if k.startswith("random"))
+    return {"tflops": best, "frac_of_nominal_peak": round(best / FP16_MFMA_PEAK_TFLOPS, 4), "by_operands": out,
+            "kernel": "bin1_mfma_rate (v_mfma_f32_32x32x16_f16 on 12 independent accumulators, no other work)"}
+
+
 def gpu_info():
     """ROCm version, device name and clocks as the tools report them (None where they do not)."""
     import subprocess
@@ -764,6 +787,10 @@ def extra_prefill(dev, check):
         rms = time_fn(fn, reps=50, warm=PREFILL_WARM)
         ref[name] = {"us": round(rms * 1e3, 2), "tflops": round(2.0 * M * K * N / (rms * 1e-3) / 1e12, 1)}
     out["dense_fp16_gemm_same_shape_torch"] = ref
+    rate = mfma_rate(dev)
+    out["measured_fp16_mfma_rate"] = rate
+    out["frac_of_measured_mfma_rate"] = round(tf / rate["tflops"], 4)
+    out["m512"]["frac_of_measured_mfma_rate"] = round(tf5 / rate["tflops"], 4)
     return out
 
 

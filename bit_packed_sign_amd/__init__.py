@@ -5,4 +5,5 @@ functions below are its thin torch binding.  ``synth`` holds the seeded input ge
 """
 from .binding import (Bin1Error, ChainPlan, PatchTable, gemm_prefill, gemm_prefill_t2, gemv, gemv_group,  # noqa: F401
                       gemv_group_t2, gemv_noalloc, gemv_pm1, gemv_t2, gemv_workspace_bytes, gemv_ws, kernel_variant, lib,
-                      rank_rows_by_scale, stream_read, xor_bits_apply, xor_patch_apply, xor_patch_apply_multi)
+                      mfma_rate, rank_rows_by_scale, stream_read, xor_bits_apply, xor_patch_apply,
+                      xor_patch_apply_multi)

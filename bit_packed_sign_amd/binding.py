@@ -42,6 +42,7 @@ _SIGS = {
     "bin1_gemv_chain": [_p, _p],
     "bin1_chain_status": [_p, _p, _p],
     "bin1_stream_read": [_p, ctypes.c_size_t, _p, _i, _i, _p],
+    "bin1_mfma_rate": [_p, _p, _i, _i, _i, _p],
     "bin1_kernel_variant": [_i, _i, _i, _i, _p, _p, _i],
     "bin1_gemv_workspace_bytes": [_i, _i, _i],
     "bin1_gemv_ws": [_p, _p, _p, _p, _i, _i, _i, _p, ctypes.c_size_t, _p],
@@ -446,6 +447,21 @@ def stream_read(buf: torch.Tensor, sink: Optional[torch.Tensor] = None, grid: in
         raise ValueError("sink needs 4 * grid entries")
     nbytes = buf.numel() * buf.element_size()
     _call("bin1_stream_read", buf.get_device(), buf.data_ptr(), nbytes, sink.data_ptr(), grid, unroll, _stream(buf))
+    return sink
+
+
+def mfma_rate(operands: torch.Tensor, sink: torch.Tensor, grid: int = 1024, waves: int = 4, iters: int = 1000):
+    """Issue grid * waves * iters * 12 independent fp16 32x32x16 matrix-core products on the lane
+    fragments in ``operands`` (device float16 [2, 64, 8]: A then B) -- a measurement of the sustained
+    MFMA rate, no arithmetic of the method.  ``sink``: device float32 [grid * waves], which receives
+    12 * iters * (A B)[0, 0] per wave (exact for small integer operands)."""
+    _need(operands, "operands", (torch.float16,), 3)
+    if tuple(operands.shape) != (2, 64, 8):
+        raise ValueError("operands must be [2, 64, 8]")
+    _need(sink, "sink", (torch.float32,), 1)
+    if sink.numel() < grid * waves:
+        raise ValueError("sink needs grid * waves entries")
+    _call("bin1_mfma_rate", sink.get_device(), operands.data_ptr(), sink.data_ptr(), grid, waves, iters, _stream(sink))
     return sink
 
 

@@ -648,6 +648,21 @@ int bin1_stream_read(const void *buf, size_t bytes, uint32_t *sink, int grid, in
                     "bin1_stream_read");
 }
 
+int bin1_mfma_rate(const void *operands, float *sink, int grid, int waves, int iters, void *stream)
+{
+    if (grid < 1 || grid > 65536 || (waves != 4 && waves != 8) || iters < 1 || iters > 1000000)
+        return fail(BIN1_ERR_SHAPE, "need 1 <= grid <= 65536, waves 4 or 8, 1 <= iters <= 1000000 (got %d, %d, %d)",
+                    grid, waves, iters);
+    if (!operands || !sink) return fail(BIN1_ERR_NULL, "operands and sink must be non-NULL");
+    if (!aligned16(operands) || reinterpret_cast<uintptr_t>(sink) & 3u)
+        return fail(BIN1_ERR_ALIGN, "operands must be 16-byte aligned and sink 4-byte aligned");
+    if (overlap(sink, (size_t)grid * waves * 4, operands, 2048)) return fail(BIN1_ERR_ALIAS, "sink overlaps operands");
+    int st;
+    if ((st = check_device(operands, "operands")) || (st = check_device(sink, "sink"))) return st;
+    return launched(bin1::launch_mfma_rate(operands, sink, grid, waves, iters, static_cast<hipStream_t>(stream)),
+                    "bin1_mfma_rate");
+}
+
 int bin1_kernel_variant(int op, int M, int K, int count, const int *N, char *name, int len)
 {
     if (!N || !name) return fail(BIN1_ERR_NULL, "N and name must be non-NULL");

@@ -1,7 +1,9 @@
-// calib.hip -- a plain streaming read of device memory: the HBM read rate that the decode
-// kernels' achieved bandwidth is compared against.  It does none of the method's arithmetic;
-// it only reads every 16-byte chunk once and folds the data into a digest so that the loads
-// cannot be dropped.
+// calib.hip -- two on-device references, neither doing any of the method's arithmetic:
+//  * a plain streaming read of device memory: the HBM read rate that the decode kernels'
+//    achieved bandwidth is compared against (every 16-byte chunk read once, folded into a digest
+//    so that the loads cannot be dropped);
+//  * a stream of independent fp16 matrix-core products: the MFMA rate this GPU sustains at the
+//    clock it holds under such a load, which the prefill product is compared against.
 #include "common.hpp"
 #include "kernels.hpp"
 
@@ -36,7 +38,42 @@ __global__ __launch_bounds__(256) void stream_read_kernel(const u4v *__restrict_
     if ((threadIdx.x & 63) == 0) sink[blockIdx.x * 4 + (threadIdx.x >> 6)] = acc;
 }
 
+typedef _Float16 half8v __attribute__((ext_vector_type(8)));
+typedef float f16v __attribute__((ext_vector_type(16)));
+
+// Every wave issues iters x 12 v_mfma_f32_32x32x16_f16 on 12 independent accumulators, nothing
+// else inside the loop.  Lane l takes its A and B fragments (8 fp16 each) from ab[l] and ab[64 + l]:
+// the operand values set how many multiplier bits toggle, and with them the power drawn and the
+// clock the part holds.  Lane 0 of a wave writes the sum over the 12 accumulators of their element
+// 0 (row 0, column 0 of the 32 x 32 product), 12 * iters * D00, to sink[global wave index].
+__global__ __launch_bounds__(512) void mfma_rate_kernel(const half8v *__restrict__ ab, float *__restrict__ sink,
+                                                        int iters)
+{
+    const int lane = threadIdx.x & 63;
+    const half8v a = ab[lane], b = ab[64 + lane];
+    f16v acc[12];
+#pragma unroll
+    for (int j = 0; j < 12; ++j)
+#pragma unroll
+        for (int v = 0; v < 16; ++v) acc[j][v] = 0.f;
+    for (int it = 0; it < iters; ++it) {
+#pragma unroll
+        for (int j = 0; j < 12; ++j) acc[j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(a, b, acc[j], 0, 0, 0);
+    }
+    float s = 0.f;
+#pragma unroll
+    for (int j = 0; j < 12; ++j) s += acc[j][0];
+    if (lane == 0) sink[blockIdx.x * (blockDim.x >> 6) + (threadIdx.x >> 6)] = s;
+}
+
 }  // namespace
+
+hipError_t launch_mfma_rate(const void *ab, float *sink, int grid, int waves, int iters, hipStream_t st)
+{
+    hipLaunchKernelGGL(mfma_rate_kernel, dim3(grid), dim3(64 * waves), 0, st, static_cast<const half8v *>(ab), sink,
+                       iters);
+    return hipGetLastError();
+}
 
 hipError_t launch_stream_read(const void *buf, size_t bytes, uint32_t *sink, int grid, int unroll, hipStream_t st)
 {

@@ -106,6 +106,7 @@ hipError_t launch_xor_patch_multi(uint32_t *const *Wtab, const int32_t *Ktab, co
 
 // Streaming read of `bytes` (multiple of 16) into a per-wave digest sink[4 * grid].
 hipError_t launch_stream_read(const void *buf, size_t bytes, uint32_t *sink, int grid, int unroll, hipStream_t st);
+hipError_t launch_mfma_rate(const void *ab, float *sink, int grid, int waves, int iters, hipStream_t st);
 
 // Shared by the entry points (defined with the C ABI's validation): the thread-local error text,
 // and bin1_gemv with a scratch area for the split-K path (caller_ws: a caller's workspace, checked

@@ -265,6 +265,20 @@ int bin1_chain_status(const bin1_chain_plan *plan, int *runs, int *error);
  * aligned, bytes a positive multiple of 16, 1 <= grid <= 65536, and sink not overlapping buf. */
 int bin1_stream_read(const void *buf, size_t bytes, uint32_t *sink, int grid, int unroll, void *stream);
 
+/* Measurement helper (does none of the method's arithmetic): `grid` workgroups of `waves` waves
+ * (4: one per SIMD, or 8: two) each issue iters x 12 independent fp16 matrix-core products
+ * (32 x 32 x 16, 32768 flops each) with nothing else in the loop.  Timing it gives the fp16 MFMA
+ * rate this GPU sustains, the reference for the prefill product, which is compute-bound
+ * ("Bonsai 27B" page, section "Low-bit kernels for hybrid attention").  The rate depends on the
+ * operand values (their bit activity sets the power drawn and so the clock held), so the caller
+ * supplies them: operands is device fp16 [2][64][8], lane l's A fragment (row l % 32, k = 8 (l / 32)
+ * .. + 7) then its B fragment (k = 8 (l / 32) .. + 7, column l % 32).  Writes, for every wave w,
+ * sink[w] = the fp32 sum over the 12 accumulators of their row-0, column-0 element, which is
+ * 12 * iters * D00 (D = A B) when all partial sums are exact in fp32 (small integer operands).
+ * Requires 1 <= grid <= 65536, waves 4 or 8, 1 <= iters <= 1000000, operands 16-byte aligned,
+ * sink (device float [grid * waves]) 4-byte aligned and not overlapping operands. */
+int bin1_mfma_rate(const void *operands, float *sink, int grid, int waves, int iters, void *stream);
+
 /* Diagnostic: the kernel variant(s) and grid that a product call would launch for these shapes,
  * from the same dispatch code the calls run (nothing is launched; no device is needed).
  * op: 0 = bin1_gemv (count == 1) or bin1_gemv_group, 1 = bin1_gemv_t2 or bin1_gemv_group_t2,

@@ -186,3 +186,22 @@ def test_workspace_product_validation(L):
     assert f(x, W, S, y, 16, 12288, 4096, W, need, None) == -4         # covers the weights
     assert f(x, W, S, y, 0, 12288, 4096, None, 0, None) == 0           # no outputs: nothing to do
 
+
+
+def test_calibration_validation(L):
+    """The two measurement helpers reject bad sizes, NULL and misaligned pointers before launch."""
+    assert L.bin1_stream_read(FAKE, 0, FAKE * 2, 1, 8, None) == -2            # no bytes
+    assert L.bin1_stream_read(FAKE, 24, FAKE * 2, 1, 8, None) == -2           # not a multiple of 16
+    assert L.bin1_stream_read(FAKE, 64, FAKE * 2, 0, 8, None) == -2           # grid
+    assert L.bin1_stream_read(FAKE, 64, FAKE * 2, 1, 5, None) == -2           # unroll
+    assert L.bin1_stream_read(None, 64, FAKE * 2, 1, 8, None) == -1
+    assert L.bin1_stream_read(FAKE + 4, 64, FAKE * 2, 1, 8, None) == -3
+    assert L.bin1_stream_read(FAKE, 64, FAKE + 32, 1, 8, None) == -4          # sink inside buf
+    assert L.bin1_mfma_rate(FAKE, FAKE * 2, 0, 4, 10, None) == -2            # grid
+    assert L.bin1_mfma_rate(FAKE, FAKE * 2, 1, 5, 10, None) == -2            # waves
+    assert L.bin1_mfma_rate(FAKE, FAKE * 2, 1, 4, 0, None) == -2             # iters
+    assert L.bin1_mfma_rate(None, FAKE * 2, 1, 4, 10, None) == -1
+    assert L.bin1_mfma_rate(FAKE, None, 1, 4, 10, None) == -1
+    assert L.bin1_mfma_rate(FAKE + 4, FAKE * 2, 1, 4, 10, None) == -3         # operands not 16-byte aligned
+    assert L.bin1_mfma_rate(FAKE, FAKE * 2 + 2, 1, 4, 10, None) == -3
+    assert L.bin1_mfma_rate(FAKE, FAKE + 1024, 1, 4, 10, None) == -4         # sink inside the operands
