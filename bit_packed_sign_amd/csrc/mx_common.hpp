@@ -106,6 +106,8 @@ __device__ __forceinline__ void a_offsets(int lane, int &lo, int &hi)
 //  * ternary (unpack_t2): weight k(j) = 16 (j/16) + 2 (j%8) + (j/8)%2, so activation i sits at
 //    byte 16h + 8 (i%2) + i/2 -- dword 4h + c holds activations 8m + e, 8m + 2 + e, 8m + 4 + e,
 //    8m + 6 + e for c = 2e + m.
+typedef _Float16 h2v __attribute__((ext_vector_type(2)));
+
 template <bool T2 = false>
 __device__ __forceinline__ void convert16(const u4v p0, const u4v p1, float mx, uint8_t *blk, int G, int h,
                                           uint8_t *scbyte)
@@ -113,10 +115,62 @@ __device__ __forceinline__ void convert16(const u4v p0, const u4v p1, float mx, 
     // activation of byte b of dword slot c
     auto idx = [](int c, int b) { return T2 ? 8 * (c & 1) + 2 * b + (c >> 1) : 4 * b + c; };
     const uint32_t hw[8] = {p0.x, p0.y, p0.z, p0.w, p1.x, p1.y, p1.z, p1.w};
+    const int e0 = mx > 0.f ? __builtin_amdgcn_frexp_expf(mx) - 1 : 0;   // 2^e0 <= mx
+    if (e0 >= -4 && e0 <= 7) {
+        // The same limbs in packed fp16, for blocks whose largest magnitude lies in [2^-4, 2^8):
+        // there u = x 2^(7 - e0) scales x up (exact), and every value below is exact in fp16.
+        //  * limb 0: the scaled conversion divides by its scale, fp8(x / 2^(e0 - 7)) = fp8(u),
+        //    with the same rounding as the f32 conversion (checked over every fp16 value);
+        //  * the next limb's input 16 (u - q): the back conversion multiplies by its scale (a
+        //    power of two; its sign is not used), so scale 16 gives 16 q exactly, and one fma of x
+        //    by 2^(11 - e0) <= 2^15 less that is 16 u - 16 q, exact (u - q carries at most 8
+        //    significant bits).
+        // Pairs are regrouped first so that each conversion fills the two bytes its dword holds.
+        h2v P[4][2];
+#pragma unroll
+        for (int c = 0; c < 4; ++c)
+#pragma unroll
+            for (int q = 0; q < 2; ++q) {
+                const int i0 = idx(c, 2 * q), i1 = idx(c, 2 * q + 1);   // same parity
+                P[c][q] = __builtin_bit_cast(h2v, __builtin_amdgcn_perm(hw[i1 >> 1], hw[i0 >> 1],
+                                                                         (i0 & 1) ? 0x07060302u : 0x05040100u));
+            }
+        const float s0 = __builtin_ldexpf(1.0f, e0 - 7);
+        const _Float16 f16 = (_Float16)__builtin_ldexpf(1.0f, 11 - e0);
+        const h2v f16v = {f16, f16}, sixteen = {(_Float16)16.0f, (_Float16)16.0f};
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+            int d[4];
+#pragma unroll
+            for (int c = 0; c < 4; ++c) {
+                if (r < 3) {
+                    const float sc = r == 0 ? s0 : 1.0f;
+                    typedef short s2v __attribute__((ext_vector_type(2)));
+                    s2v v = {0, 0};
+                    v = __builtin_amdgcn_cvt_scalef32_pk_fp8_f16(v, P[c][0], sc, false);
+                    v = __builtin_amdgcn_cvt_scalef32_pk_fp8_f16(v, P[c][1], sc, true);
+                    d[c] = __builtin_bit_cast(int, v);
+                } else {
+                    d[c] = 0;
+                }
+                *reinterpret_cast<int *>(blk + (4 * G + r) * 32 + (T2 ? 4 * h + c : 2 * c + h) * 4) = d[c];
+            }
+            if (h == 0) scbyte[r * 4] = (uint8_t)(127 + e0 - 7 - 4 * r);
+            if (r < 2) {
+#pragma unroll
+                for (int c = 0; c < 4; ++c) {
+                    const h2v m0 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8((unsigned)d[c], 16.0f, false);
+                    const h2v m1 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8((unsigned)d[c], 16.0f, true);
+                    P[c][0] = __builtin_elementwise_fma(P[c][0], r == 0 ? f16v : sixteen, -m0);
+                    P[c][1] = __builtin_elementwise_fma(P[c][1], r == 0 ? f16v : sixteen, -m1);
+                }
+            }
+        }
+        return;
+    }
     float u[16];
 #pragma unroll
     for (int i = 0; i < 16; ++i) u[i] = h2f((uint16_t)(hw[i >> 1] >> (16 * (i & 1))));
-    const int e0 = mx > 0.f ? __builtin_amdgcn_frexp_expf(mx) - 1 : 0;   // 2^e0 <= mx
     const float mul = __builtin_ldexpf(1.0f, 7 - e0);
 #pragma unroll
     for (int i = 0; i < 16; ++i) u[i] *= mul;        // |u| < 256, exact
@@ -155,7 +209,6 @@ __device__ __forceinline__ void convert16(const u4v p0, const u4v p1, float mx, 
 }
 
 // max |x| over 16 fp16 values (packed fp16 max: exact, and a quarter of the scalar ops)
-typedef _Float16 h2v __attribute__((ext_vector_type(2)));
 __device__ __forceinline__ float absmax16(const u4v p0, const u4v p1)
 {
     const uint32_t hw[8] = {p0.x, p0.y, p0.z, p0.w, p1.x, p1.y, p1.z, p1.w};
