@@ -72,3 +72,33 @@ def test_power_of_two_onehot_is_bit_exact(orc, dev, path, M, K):
     assert np.array_equal(want.astype(np.float64), ref), "the exact product does not fit fp16"
     # equal as numbers: every bit of every nonzero output (a zero may carry either sign)
     assert np.array_equal(y.astype(np.float64), want.astype(np.float64))
+
+
+@pytest.mark.parametrize("path,K", [("gemv", 4096), ("gemv", 3968), ("gemv", 12288), ("gemv_t2", 4096),
+                                    ("gemv_t2", 3968)])
+def test_limb_conversion_paths_agree(dev, path, K):
+    """Batch-1 activations are split into fp8 limbs in packed fp16 when a block's largest magnitude
+    lies in [2^-4, 2^8), and in fp32 otherwise.  The split is invariant under power-of-two scaling,
+    so activations whose every 32-block maximum is in [2, 4) (packed path) and the same activations
+    times 2^7 (maxima in [256, 512): fp32 path) must give outputs exactly 2^7 apart."""
+    N = 6144
+    r = synth.rng_for(0, synth.WL_TEST, 9300 + K + (7 if path == "gemv_t2" else 0))
+    x = r.standard_normal((1, K))
+    blk = x.reshape(1, K // 32, 32)
+    blk *= (2.0 + 1.999 * r.random((1, K // 32, 1))) / np.abs(blk).max(axis=2, keepdims=True)
+    x = blk.reshape(1, K).astype(np.float16)
+    mx = np.abs(x.astype(np.float64)).reshape(K // 32, 32).max(axis=1)
+    assert mx.min() >= 2.0 and mx.max() < 4.0
+    W = synth.ternary_words_fast(r, N, K) if path == "gemv_t2" else synth.sign_words(r, N, K)
+    S = synth.group_scales(r, N, K)
+    xd, Wd, Sd = dev_tensors(dev, x, W, S)
+    xs = torch.from_numpy((x.astype(np.float64) * 128.0).astype(np.float16)).to(dev)
+    fn = b1.gemv_t2 if path == "gemv_t2" else b1.gemv
+    y = fn(xd, Wd, Sd).float().cpu().numpy().astype(np.float64)
+    ys = fn(xs, Wd, Sd).float().cpu().numpy().astype(np.float64)
+    # fp16 rounding commutes with the 2^7 scaling wherever y is zero or normal and 2^7 y does not
+    # overflow; an fp16-subnormal y (a rare near-cancellation) is left out of the comparison
+    assert np.all(np.abs(y) < 500)
+    normal = (y == 0) | (np.abs(y) >= 2.0 ** -14)
+    assert normal.mean() > 0.99
+    assert np.array_equal(ys[normal], y[normal] * 128.0)
