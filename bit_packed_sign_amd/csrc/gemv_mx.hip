@@ -178,7 +178,14 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(NW / 4,
 void gemv_mx_kernel(const uint16_t *__restrict__ x, int Ktq, int trg, const uint32_t *W0, const uint16_t *S0,
                     const uint32_t *W1, const uint16_t *S1, int N0, int N1, MxSet set)
 {
-    const int K = Ktq & 0xFFFF, tq = Ktq >> 16, tr = trg & 0xFFFF, grid = trg >> 16;
+    const int K = Ktq & 0xFFFF, tq = (Ktq >> 16) & 0xFF, tr = trg & 0xFFFF, grid = trg >> 16;
+    // Several tokens (2 <= M <= 8): the grid holds one copy of the one-token grid per token, and
+    // workgroup b serves token b / grid with the one-token work of workgroup b % grid.
+    const int mt1 = (Ktq >> 24) & 7;                  // tokens - 1
+    int token = 0;
+    for (int j = 1; j <= mt1; ++j) token += blockIdx.x >= (unsigned)(j * grid) ? 1 : 0;
+    const unsigned bid = blockIdx.x - (unsigned)(token * grid);
+    x += (size_t)token * K;
     const int te0 = (N0 + 16 * R - 1) / (16 * R);   // matrix 0's tiles
     extern __shared__ __attribute__((aligned(16))) uint8_t lds[];
     const int tid = threadIdx.x, lane = tid & 63;
@@ -201,7 +208,7 @@ void gemv_mx_kernel(const uint16_t *__restrict__ x, int Ktq, int trg, const uint
     // first loads.  With at most two matrices (TWO) the whole tile table comes from these
     // scalars; otherwise a workgroup whose first tile is in matrix 0 starts its weight loads
     // without waiting for the argument table.
-    const int my_tiles = tq + (blockIdx.x < (unsigned)tr ? 1 : 0);         // <= 64
+    const int my_tiles = tq + (bid < (unsigned)tr ? 1 : 0);                // <= 64
 
     Slot<SP, R, T2> ring[P];
 
@@ -251,7 +258,7 @@ void gemv_mx_kernel(const uint16_t *__restrict__ x, int Ktq, int trg, const uint
     __builtin_amdgcn_sched_barrier(0);               // x loads go out before the argument-table loads
     TileTab tab;
     if constexpr (TWO) {
-        tab = tile_tab2<R>(W0, S0, N0, te0, W1, S1, N1, blockIdx.x + lane * grid);
+        tab = tile_tab2<R>(W0, S0, N0, te0, W1, S1, N1, bid + lane * grid);
 #pragma unroll
         for (int p = 0; p < P; ++p) issue(tab, tt + TT * p, ring[p]);
         limbs_fill<NT>(K, lds);
@@ -259,9 +266,9 @@ void gemv_mx_kernel(const uint16_t *__restrict__ x, int Ktq, int trg, const uint
         // only the scalars are chosen under the (uniform) branch: one issue after it, so no
         // load sits on either side of a join
         unsigned long long Wp = (unsigned long long)W0, Sp = (unsigned long long)S0;
-        int row0 = (int)blockIdx.x * 16 * R, Nt = N0;
-        if (blockIdx.x >= (unsigned)te0) {
-            const TileTab t0 = tile_tab<R>(set, blockIdx.x);
+        int row0 = (int)bid * 16 * R, Nt = N0;
+        if (bid >= (unsigned)te0) {
+            const TileTab t0 = tile_tab<R>(set, bid);
             Wp = t0.W;
             Sp = t0.S;
             row0 = t0.row0;
@@ -269,7 +276,7 @@ void gemv_mx_kernel(const uint16_t *__restrict__ x, int Ktq, int trg, const uint
         }
         issue_t(row0, my_tiles > 0 ? Nt : 0, Wp, Sp, ring[0]);
         limbs_fill<NT>(K, lds);
-        tab = tile_tab<R>(set, blockIdx.x + lane * grid);
+        tab = tile_tab<R>(set, bid + lane * grid);
 #pragma unroll
         for (int p = 1; p < P; ++p) issue(tab, p, ring[p]);
     }
@@ -388,7 +395,7 @@ void gemv_mx_kernel(const uint16_t *__restrict__ x, int Ktq, int trg, const uint
     }
 done:
     if constexpr (TWO) {                              // the outputs, for the merge
-        const int tile = blockIdx.x + lane * grid;
+        const int tile = bid + lane * grid;
         tab.y = (unsigned long long)(tile >= te0 ? set.y[1] : set.y[0]);
     }
     if (wave == 0) tabl[lane] = int4v{tab.row0, tab.N, (int)(unsigned)tab.y, (int)(unsigned)(tab.y >> 32)};
@@ -412,7 +419,8 @@ done:
         for (int v = 1; v < NWP / 4; ++v) tot += (pr[v][0] + pr[v][1]) + (pr[v][2] + pr[v][3]);
         const int row = t[0] + j;
         if (row < t[1])
-            reinterpret_cast<uint16_t *>(((unsigned long long)(unsigned)t[3] << 32) | (unsigned)t[2])[row] = f2h_rne(tot);
+            reinterpret_cast<uint16_t *>(((unsigned long long)(unsigned)t[3] << 32) | (unsigned)t[2])
+                [(size_t)token * t[1] + row] = f2h_rne(tot);                 // y: [tokens][N]
     }
 }
 
@@ -427,7 +435,7 @@ constexpr size_t shm_bytes(int K, int rows_per_wg, int NW)
 }
 
 template <int SP, int P, int R, bool ODD, bool T2, int NW, bool TWO, int TT, bool AL>
-hipError_t launch_mx_t(const uint16_t *x, const MxSet &set0, int K, hipStream_t st, std::string *desc)
+hipError_t launch_mx_t(const uint16_t *x, const MxSet &set0, int K, int mt, hipStream_t st, std::string *desc)
 {
     constexpr int NWP = NW / TT;
     MxSet set = set0;
@@ -455,12 +463,14 @@ hipError_t launch_mx_t(const uint16_t *x, const MxSet &set0, int K, hipStream_t 
     const bool two = set.count == 2;
     if (desc) {                                        // describe the launch instead of making it
         char buf[160];
+        char tok[16] = "";
+        if (mt > 1) snprintf(tok, sizeof tok, " tokens=%d", mt);
         if (TT > 1 || AL)
-            snprintf(buf, sizeof buf, "gemv_mx<%d,%d,%d,%d,%d,%d,%d,%d%s> lds=%zu grid=%d", SP, P, R, (int)ODD,
-                     (int)T2, NW, (int)TWO, TT, AL ? ",AL" : "", shm, grid);
+            snprintf(buf, sizeof buf, "gemv_mx<%d,%d,%d,%d,%d,%d,%d,%d%s>%s lds=%zu grid=%d", SP, P, R, (int)ODD,
+                     (int)T2, NW, (int)TWO, TT, AL ? ",AL" : "", tok, shm, grid * mt);
         else
-            snprintf(buf, sizeof buf, "gemv_mx<%d,%d,%d,%d,%d,%d,%d> lds=%zu grid=%d", SP, P, R, (int)ODD, (int)T2,
-                     NW, (int)TWO, shm, grid);
+            snprintf(buf, sizeof buf, "gemv_mx<%d,%d,%d,%d,%d,%d,%d>%s lds=%zu grid=%d", SP, P, R, (int)ODD, (int)T2,
+                     NW, (int)TWO, tok, shm, grid * mt);
         desc->append(desc->empty() ? "" : ";").append(buf);
         return hipSuccess;
     }
@@ -469,8 +479,8 @@ hipError_t launch_mx_t(const uint16_t *x, const MxSet &set0, int K, hipStream_t 
         hipFuncAttributeMaxDynamicSharedMemorySize,
         (int)std::min<size_t>(shm_bytes(kMaxPairs * 1024, kMaxTileRows, NWP), kMaxLds));
     if (attr != hipSuccess) return attr;
-    hipLaunchKernelGGL((gemv_mx_kernel<SP, P, R, ODD, T2, NW, TWO, TT, AL>), dim3(grid), dim3(64 * NW),
-                       shm, st, x, K | (tiles / grid) << 16, (tiles % grid) | grid << 16,
+    hipLaunchKernelGGL((gemv_mx_kernel<SP, P, R, ODD, T2, NW, TWO, TT, AL>), dim3(grid * mt), dim3(64 * NW),
+                       shm, st, x, K | (tiles / grid) << 16 | (mt - 1) << 24, (tiles % grid) | grid << 16,
                        set.W[0], set.S[0], two ? set.W[1] : nullptr, two ? set.S[1] : nullptr, set.N[0],
                        two ? set.N[1] : 0, set);
     return hipGetLastError();
@@ -480,14 +490,14 @@ hipError_t launch_mx_t(const uint16_t *x, const MxSet &set0, int K, hipStream_t 
 // wave groups per workgroup (TT > 1) need that table, so three or four matrices fall back to one
 // group of NW / TT waves.
 template <int SP, int P, int R, bool ODD, bool T2, int NW = 4, int TT = 1, bool AL = false>
-hipError_t launch_mx(const uint16_t *x, const MxSet &set, int K, hipStream_t st, std::string *desc)
+hipError_t launch_mx(const uint16_t *x, const MxSet &set, int K, int mt, hipStream_t st, std::string *desc)
 {
-    if (set.count <= 2) return launch_mx_t<SP, P, R, ODD, T2, NW, true, TT, AL>(x, set, K, st, desc);
-    return launch_mx_t<SP, P, R, ODD, T2, NW / TT, false, 1, AL>(x, set, K, st, desc);
+    if (set.count <= 2) return launch_mx_t<SP, P, R, ODD, T2, NW, true, TT, AL>(x, set, K, mt, st, desc);
+    return launch_mx_t<SP, P, R, ODD, T2, NW / TT, false, 1, AL>(x, set, K, mt, st, desc);
 }
 
 template <bool ODD, bool T2>
-hipError_t dispatch_mx(const uint16_t *x, const MxSet &set, int K, hipStream_t st, std::string *desc)
+hipError_t dispatch_mx(const uint16_t *x, const MxSet &set, int K, int mt, hipStream_t st, std::string *desc)
 {
     const int SP = (((K + 1023) >> 10) + 3) / 4;        // pairs per wave
     // One tile per workgroup (the grid covers all tiles): a one-slot ring, so that no dead
@@ -510,14 +520,14 @@ hipError_t dispatch_mx(const uint16_t *x, const MxSet &set, int K, hipStream_t s
     // workgroups, then three wave groups per workgroup on 16-row tiles (measured on the 8B q|k|v
     // and gate|up shapes).
     case 1:
-        if (t16 > 256 && t32 <= 256) return launch_mx<1, 1, 2, ODD, T2>(x, set, K, st, desc);
-        if (t16 > 256 && t32 <= cap) return launch_mx<1, 1, 1, ODD, T2, 12, 3>(x, set, K, st, desc);
+        if (t16 > 256 && t32 <= 256) return launch_mx<1, 1, 2, ODD, T2>(x, set, K, mt, st, desc);
+        if (t16 > 256 && t32 <= cap) return launch_mx<1, 1, 1, ODD, T2, 12, 3>(x, set, K, mt, st, desc);
         if constexpr (!T2)
-            if (!few16) return launch_mx<1, 1, 2, ODD, T2, 12, 3>(x, set, K, st, desc);
-        return one16 ? launch_mx<1, 1, 1, ODD, T2>(x, set, K, st, desc)
-                 : one   ? launch_mx<1, 1, 2, ODD, T2, 12, 3>(x, set, K, st, desc)
-                 : few16 ? launch_mx<1, 3, 1, ODD, T2>(x, set, K, st, desc)
-                         : launch_mx<1, 2, 2, ODD, T2, 12, 3>(x, set, K, st, desc);
+            if (!few16) return launch_mx<1, 1, 2, ODD, T2, 12, 3>(x, set, K, mt, st, desc);
+        return one16 ? launch_mx<1, 1, 1, ODD, T2>(x, set, K, mt, st, desc)
+                 : one   ? launch_mx<1, 1, 2, ODD, T2, 12, 3>(x, set, K, mt, st, desc)
+                 : few16 ? launch_mx<1, 3, 1, ODD, T2>(x, set, K, mt, st, desc)
+                         : launch_mx<1, 2, 2, ODD, T2, 12, 3>(x, set, K, mt, st, desc);
     // Binary weights, 5..8 pairs (K = 5120 at the 27B shapes): eight waves with one pair each on
     // 32-row tiles, up to 512 workgroups (measured: fewer, taller tiles beat 16-row ones, and beat
     // four waves with a second pair on some of them).  Ternary rows keep the layouts below.
@@ -525,25 +535,25 @@ hipError_t dispatch_mx(const uint16_t *x, const MxSet &set, int K, hipStream_t s
     // carries a second pair on the critical path (the wider workgroups fit fewer per CU).
     case 2:
         if constexpr (!T2)
-            return t32 <= 3 * 512 ? launch_mx<1, 1, 2, ODD, T2, 8>(x, set, K, st, desc)
-                                  : launch_mx<1, 2, 2, ODD, T2, 8>(x, set, K, st, desc);
-        return one16 ? launch_mx<1, 1, 1, ODD, T2, 8>(x, set, K, st, desc)
-                 : one   ? launch_mx<2, 1, 2, ODD, T2>(x, set, K, st, desc)
-                 : few16 ? launch_mx<2, 2, 1, ODD, T2>(x, set, K, st, desc) : launch_mx<2, 2, 2, ODD, T2>(x, set, K, st, desc);
-    case 3: return one16 ? launch_mx<1, 1, 1, ODD, T2, 12>(x, set, K, st, desc)
-                 : one   ? launch_mx<3, 1, 2, ODD, T2>(x, set, K, st, desc) : launch_mx<3, 2, 2, ODD, T2>(x, set, K, st, desc);
+            return t32 <= 3 * 512 ? launch_mx<1, 1, 2, ODD, T2, 8>(x, set, K, mt, st, desc)
+                                  : launch_mx<1, 2, 2, ODD, T2, 8>(x, set, K, mt, st, desc);
+        return one16 ? launch_mx<1, 1, 1, ODD, T2, 8>(x, set, K, mt, st, desc)
+                 : one   ? launch_mx<2, 1, 2, ODD, T2>(x, set, K, mt, st, desc)
+                 : few16 ? launch_mx<2, 2, 1, ODD, T2>(x, set, K, mt, st, desc) : launch_mx<2, 2, 2, ODD, T2>(x, set, K, mt, st, desc);
+    case 3: return one16 ? launch_mx<1, 1, 1, ODD, T2, 12>(x, set, K, mt, st, desc)
+                 : one   ? launch_mx<3, 1, 2, ODD, T2>(x, set, K, mt, st, desc) : launch_mx<3, 2, 2, ODD, T2>(x, set, K, mt, st, desc);
     // (ternary rows are twice as many bytes: 16-row tiles keep the ring in registers)
     case 4:
-        if (one16) return launch_mx<1, 1, 1, ODD, T2, 16>(x, set, K, st, desc);
-        if constexpr (T2) return launch_mx<4, 1, 1, ODD, T2>(x, set, K, st, desc);
-        else return launch_mx<4, 1, 2, ODD, T2>(x, set, K, st, desc);
+        if (one16) return launch_mx<1, 1, 1, ODD, T2, 16>(x, set, K, mt, st, desc);
+        if constexpr (T2) return launch_mx<4, 1, 1, ODD, T2>(x, set, K, mt, st, desc);
+        else return launch_mx<4, 1, 2, ODD, T2>(x, set, K, mt, st, desc);
     // 17..20 pairs (K = 17408 at the 27B shapes), binary: twelve waves of at most two pairs, each
     // pair's A operands read where they are used (AL), so the twelve waves fit a CU; one 32-row tile
     // per workgroup, or 16-row tiles two at a time past 256 of them.
     default:
-        if constexpr (T2) return launch_mx<5, 1, 1, ODD, T2>(x, set, K, st, desc);
-        else return t32 <= 256 ? launch_mx<2, 1, 2, ODD, T2, 12, 1, true>(x, set, K, st, desc)
-                               : launch_mx<2, 2, 1, ODD, T2, 12, 1, true>(x, set, K, st, desc);
+        if constexpr (T2) return launch_mx<5, 1, 1, ODD, T2>(x, set, K, mt, st, desc);
+        else return t32 <= 256 ? launch_mx<2, 1, 2, ODD, T2, 12, 1, true>(x, set, K, mt, st, desc)
+                               : launch_mx<2, 2, 1, ODD, T2, 12, 1, true>(x, set, K, mt, st, desc);
     }
 }
 
@@ -551,14 +561,29 @@ hipError_t dispatch_mx(const uint16_t *x, const MxSet &set, int K, hipStream_t s
 
 int mx_max_k() { return kMaxPairs * 1024; }
 
-hipError_t launch_gemv_mx(const uint16_t *x, const MxSet &set, int K, hipStream_t st, std::string *desc)
+// Two tokens on short products: two copies of the one-token grid beat the small-batch kernels
+// where the one-token grid is small (8B step, each class's launches replayed alone: o 3.70
+// against 4.66 us, down (K = 12288) 7.15 against 8.75 us; q|k|v, 384 tiles, 4.77 against 4.73;
+// gate|up 8.85 against 8.53).  From three tokens on, the copies cost about one one-token launch
+// each and lose everywhere.
+bool mx_tokens_handles(int M, int K, const MxSet &set)
 {
-    return ((K >> 7) & 1) ? dispatch_mx<true, false>(x, set, K, st, desc) : dispatch_mx<false, false>(x, set, K, st, desc);
+    if (M != 2 || K > mx_max_k()) return false;
+    int tiles = 0;
+    for (int i = 0; i < set.count; ++i) tiles += (set.N[i] + 15) / 16;
+    return tiles <= 256;
 }
 
-hipError_t launch_gemv_mx_t2(const uint16_t *x, const MxSet &set, int K, hipStream_t st, std::string *desc)
+hipError_t launch_gemv_mx(const uint16_t *x, const MxSet &set, int K, hipStream_t st, std::string *desc, int mt)
 {
-    return ((K >> 7) & 1) ? dispatch_mx<true, true>(x, set, K, st, desc) : dispatch_mx<false, true>(x, set, K, st, desc);
+    return ((K >> 7) & 1) ? dispatch_mx<true, false>(x, set, K, mt, st, desc)
+                          : dispatch_mx<false, false>(x, set, K, mt, st, desc);
+}
+
+hipError_t launch_gemv_mx_t2(const uint16_t *x, const MxSet &set, int K, hipStream_t st, std::string *desc, int mt)
+{
+    return ((K >> 7) & 1) ? dispatch_mx<true, true>(x, set, K, mt, st, desc)
+                          : dispatch_mx<false, true>(x, set, K, mt, st, desc);
 }
 
 }  // namespace bin1

@@ -336,6 +336,7 @@ hipError_t launch_gemv_smallm(const uint16_t *x, const MxSet &set0, int M, int K
                               float *part)
 {
     if (mxm_handles(M, K, set0, part != nullptr)) return launch_gemv_mxm(x, set0, M, K, st, desc, part);
+    if (mx_tokens_handles(M, K, set0)) return launch_gemv_mx(x, set0, K, st, desc, M);
     MxSet set = set0;
     int tiles = 0;
     for (int i = 0; i < set.count; ++i) {

@@ -65,10 +65,15 @@ hipError_t launch_gemv_chain(ChainHeader *hdr, int *done, const ChainStage *tabl
 
 // Largest K the block-scaled decode kernel takes (longer rows use the select kernel).
 int mx_max_k();
-hipError_t launch_gemv_mx(const uint16_t *x, const MxSet &set, int K, hipStream_t st, std::string *desc = nullptr);
+// Whether a 2 <= M <= 8 product runs as M copies of the one-token grid (launch_gemv_mx, mt = M).
+bool mx_tokens_handles(int M, int K, const MxSet &set);
+// mt tokens (1..8): x is [mt][K] and every y of the set [mt][N]; the one-token grid is launched
+// mt times over, one copy per token.
+hipError_t launch_gemv_mx(const uint16_t *x, const MxSet &set, int K, hipStream_t st, std::string *desc = nullptr,
+                          int mt = 1);
 // The same product for ternary weights in 2-bit slots (W pointers of the set: uint32 [N][K/16]).
 hipError_t launch_gemv_mx_t2(const uint16_t *x, const MxSet &set, int K, hipStream_t st,
-                             std::string *desc = nullptr);
+                             std::string *desc = nullptr, int mt = 1);
 
 hipError_t launch_gemv(const uint16_t *x, const uint32_t *W, const uint16_t *S, uint16_t *y,
                        int M, int K, int N, hipStream_t st, std::string *desc = nullptr);

@@ -23,6 +23,8 @@ def test_query_names_the_expected_variant(b1, case):
     op, M, K, Ns, expect, _ = case
     got = b1.kernel_variant(op, M, K, Ns)
     assert got.split(" ")[0] == expect, (got, expect)
+    if expect.startswith("gemv_mx<"):                # batch-1 kernel: one grid copy per token
+        assert (f" tokens={M} " in got) == (M > 1), got
     if "split" in expect:                       # the partial-sum kernel, then the chunk reduction
         assert got.count(";") == 1 and got.split(";")[1].startswith("smallm_reduce")
     else:

@@ -111,7 +111,20 @@ MXM_WS_CASES = [
     ("gemv_ws", 2, 8192, [65536], "gemv_mxm_split<1,4>", "split2"),
     ("gemv_ws", 5, 12288, [70000], "gemv_mxm_split<2,4>", "split3"),
     ("gemv_ws", 3, 5120, [66000], "gemv_mxm_split<1,4>", "onepair"),
-    ("gemv_ws", 2, 8192, [300], "gemv_smallm_split<1>", "ragged"),
+    ("gemv_ws", 3, 8192, [300], "gemv_smallm_split<1>", "ragged"),
+]
+
+# two tokens on short products (at most 256 tiles of 16 rows): two copies of the one-token grid,
+# workgroup b serving token b / grid (the variant's " tokens=2" is checked beside its name)
+TOKEN_CASES = [
+    ("gemv", 2, 4096, [4096], "gemv_mx<1,1,1,0,0,4,1>", "o"),
+    ("gemv", 2, 4096, [4112], "gemv_smallm<2,0>", "past256"),
+    ("gemv", 2, 12288, [4096], "gemv_mx<1,1,1,0,0,12,1>", "down"),
+    ("gemv", 2, 3968, [1000], "gemv_mx<1,1,1,1,0,4,1>", "odd"),
+    ("gemv", 2, 4096, [1000, 2000, 1000], "gemv_mx<1,1,1,0,0,4,0>", "group3"),
+    ("gemv", 2, 4096, [2000, 2000], "gemv_mx<1,1,1,0,0,4,1>", "group2"),
+    ("gemv_ws", 2, 12288, [4096], "gemv_mx<1,1,1,0,0,12,1>", "ws"),
+    ("gemv", 2, 17408, [4000], "gemv_mx<2,1,2,0,0,12,1,1,AL>", "al"),
 ]
 
 # prefill: 128-row tiles (two workgroups per CU) unless 256-row tiles fill the GPU twice over
@@ -135,7 +148,7 @@ WS_CASES = [
 ]
 
 ALL_CASES = (DECODE_CASES + DECODE_T2_CASES + SELECT_CASES + SMALLM_CASES + MXM_CASES + PREFILL_CASES + WS_CASES
-             + MXM_WS_CASES)
+             + MXM_WS_CASES + TOKEN_CASES)
 
 
 def case_id(c):
