@@ -51,7 +51,7 @@ def parse():
     ap.add_argument("--no-extra", action="store_true")
     ap.add_argument("--only", default=None,
                     help="run one workload alone (for profiling): step8b, chain8b, lmhead, single, mlp16, "
-                         "prefill, step27b, pm1, bits, ternary, copy")
+                         "prefill, step27b, pm1, bits, ternary, floor, copy")
     return ap.parse_args()
 
 
@@ -1052,6 +1052,10 @@ def run_only(args, dev):
         log(f"[bench] {extra_small_batch_steps(dev, args.steps, False)}")
     elif name == "ternary":
         log(f"[bench] {extra_ternary(dev, args.steps, False)}")
+    elif name == "floor":
+        # the dependent-launch floor alone (145 one-workgroup fills in a graph), so that a kernel
+        # trace shows what the profiler itself adds to a launch that does no work
+        log(f"[bench] floor {graph_launch_floor_us(dev, 145, reps=args.steps):.2f} us per launch")
     elif name == "copy":
         # a plain device copy of known size, to scale the HBM traffic counters
         src = torch.empty(256 << 20, dtype=torch.uint8, device=dev).fill_(1)

@@ -43,10 +43,10 @@ def test_prefill_full_size_sampled(orc, dev):
 
 
 @pytest.mark.parametrize("M,K,N", [(512, 4096, 12288), (2100, 256, 12300), (1030, 640, 6000)])
-def test_prefill_both_tile_shapes_sampled(orc, dev, M, K, N):
-    """256-row tiles when they fill the GPU twice over, 128-row tiles below that: a 512-token
-    prompt at full width (128-row tiles), ragged M and N on 256-row tiles (2100 x 12300: 585 of
-    them), and a ragged case between; sampled weight rows checked for every token."""
+def test_prefill_wide_and_ragged_sampled(orc, dev, M, K, N):
+    """A 512-token prompt at full width, ragged M and N over many tiles (2100 x 12300: 1071
+    tiles of 128 x 192, the last row and column tiles partial), and an odd step count (K = 640,
+    five 128-wide steps); sampled weight rows checked for every token."""
     x, W, S = _case(5300 + M + K + N, M, K, N)
     y = b1.gemm_prefill(*dev_tensors(dev, x, W, S)).float().cpu().numpy()
     rows = sample_rows(synth.rng_for(0, synth.WL_TEST, 5301 + M), N, k=48, edge=16)
@@ -60,3 +60,25 @@ def test_gemv_routes_large_m_to_prefill(orc, dev):
     x, W, S = _case(5200, M, K, N)
     ref, nrm = orc.gemv(x, W, S)
     assert norm_err(b1.gemv(*dev_tensors(dev, x, W, S)), ref, nrm) <= TOL
+
+
+def test_prefill_scale_edge_cases(orc, dev):
+    """Negative scales (folded into the sign bits), zero, -0 and subnormal scales, an all-zero
+    token row, on the prefill kernel: one 128 x 192 tile, ragged, with every lane group's k-slots
+    of a step carrying a different scale sign."""
+    M, K, N = 100, 1024, 150
+    x, W, S = _case(5400, M, K, N)
+    S = S.copy()
+    S[::3] = -S[::3]
+    S[1, ::2] = -S[1, ::2]
+    S[2] = 0
+    S[4, 1] = np.float16(-0.0)
+    S[5] = np.float16(2.0 ** -24)
+    S[6, 3:] = np.float16(-3.0e-6)
+    x = x.copy()
+    x[7] = 0
+    ref, nrm = orc.gemv(x, W, S)
+    y = b1.gemm_prefill(*dev_tensors(dev, x, W, S))
+    assert norm_err(y, ref, nrm) <= TOL
+    yn = y.float().cpu().numpy()
+    assert np.all(yn[:, 2] == 0) and np.all(yn[7] == 0)

@@ -127,12 +127,12 @@ TOKEN_CASES = [
     ("gemv", 2, 17408, [4000], "gemv_mx<2,1,2,0,0,12,1,1,AL>", "al"),
 ]
 
-# prefill: 128-row tiles (two workgroups per CU) unless 256-row tiles fill the GPU twice over
+# prefill: 128-row tiles (two workgroups per CU) at every M; a short and a full-width M
 PREFILL_CASES = [
-    ("prefill", 300, 1024, [777], "prefill<128,2,2,2,0>", "small"),
-    ("prefill", 2048, 1024, [12288], "prefill<256,2,2,1,0>", "large"),
-    ("prefill_t2", 300, 1024, [777], "prefill<128,2,2,2,1>", "small"),
-    ("prefill_t2", 2048, 1024, [12288], "prefill<256,2,2,1,1>", "large"),
+    ("prefill", 300, 1024, [777], "prefill<128,2,0>", "small"),
+    ("prefill", 2048, 1024, [12288], "prefill<128,2,0>", "large"),
+    ("prefill_t2", 300, 1024, [777], "prefill<128,2,1>", "small"),
+    ("prefill_t2", 2048, 1024, [12288], "prefill<128,2,1>", "large"),
 ]
 
 # small batch with a workspace: K split into 4096-wide chunks over workgroups (G tile groups per
