@@ -20,8 +20,8 @@
 //    per 128 rows).  A packed 16-bit shift of the half-word holding a lane's bits (read by both
 //    halves) puts adjacent bits on bits 15 and 31, so an operand dword pairs consecutive k and
 //    the staged activations need no permute; one and-or then lays both signs over |s| (a
-//    negative scale is folded into the sign bits first).  Each lane takes its k-slots from one
-//    word of a step (binary) or four contiguous words (ternary), so it loads 4 or 16 bytes of a
+//    negative scale is folded into the sign bits first).  Each lane takes its k-slots from two
+//    words of a step (binary) or four contiguous words (ternary), so it loads 8 or 16 bytes of a
 //    row per step.
 //  * Workgroup b takes M-tile b % tiles_m: with 16 M-tiles each XCD keeps two activation
 //    panels in its L2.
@@ -37,12 +37,13 @@ namespace bin1 {
 namespace {
 
 typedef unsigned u4v __attribute__((ext_vector_type(4)));
+typedef unsigned u2v __attribute__((ext_vector_type(2)));
 typedef unsigned short us2v __attribute__((ext_vector_type(2)));
 typedef _Float16 half8v __attribute__((ext_vector_type(8)));
 typedef float f4v __attribute__((ext_vector_type(4)));
 
 constexpr int BN = 192, BK = 128;
-constexpr int LDK = BK + 8;                       // LDS row stride in halves (272 B: conflict-free)
+constexpr int LDK = BK + 16;                      // LDS row stride in halves (288 B)
 constexpr int kRsrcFlags = 0x00020000;
 constexpr unsigned kOob = 0x80000000u;
 
@@ -52,7 +53,7 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t rsrc(const void *p, unsigned b
 }
 
 // B-operand dword p of a lane (binary): fp16 pair (+-|s| for bit B + 2p, +-|s| for bit B + 2p + 1)
-// of nw, where bit 1 of nw means a negative product and B is 0, 8, 16 or 24.  One packed 16-bit
+// of nw, where bit 1 of nw means a negative product and B is 0 or 16.  One packed 16-bit
 // shift of the 16-bit half holding those bits (read by both halves) puts the pair on bits 15 and
 // 31; one and-or keeps those two sign bits over |s| in both halves.
 template <int B, int P>
@@ -117,14 +118,15 @@ void prefill_kernel(const uint16_t *__restrict__ x, const uint32_t *__restrict__
     const int m0 = bm * BM, n0 = bn * BN;
     const int wpr = T2 ? K >> 4 : K >> 5, spr = K >> 7, nk = K / BK;
     // MFMA operand lanes: lane (c, g) holds row / column c of its fragment and MFMA k-slots
-    // 8g .. 8g + 7.  Which activations those slots take in substep sub is chosen so that a lane
-    // reads few weight words per step (A and B follow the same map, so the sum over k is
-    // unchanged): binary, k = 32g + 8 sub + e -- bits 8 sub .. 8 sub + 7 of the step's word g;
-    // ternary, k = 64(g / 2) + 16 sub + 8(g % 2) + e -- slots 8(g % 2) .. 8(g % 2) + 7 of word
-    // 4(g / 2) + sub, so a lane's four words of a step are contiguous.
+    // 8g .. 8g + 7.  In substep sub those slots take k = 64(g / 2) + 16 sub + 8(g % 2) + e (A and
+    // B follow the same map, so the sum over k is unchanged).  A lane then needs two words of a
+    // step (binary: bits 8(g % 2) .. of words 2(g / 2) and 2(g / 2) + 1) or four (ternary: slots
+    // 8(g % 2) .. of words 4(g / 2) .. 4(g / 2) + 3), one load; and the two lane groups of a
+    // half-wave read A at k offsets 8 apart, which at the 144-half row stride conflict on half as
+    // many LDS banks as other offsets or strides tried.
     const int fc = lane & 15, fg = lane >> 4;
-    const int ak = T2 ? 64 * (fg >> 1) + 8 * (fg & 1) : 32 * fg;   // this lane's first k of substep 0
-    constexpr int kSubK = T2 ? 16 : 8;                 // k advance of a lane per substep
+    const int ak = 64 * (fg >> 1) + 8 * (fg & 1);     // this lane's first k of substep 0
+    constexpr int kSubK = 16;                          // k advance of a lane per substep
 
     const __amdgpu_buffer_rsrc_t rx = rsrc(x, (unsigned)M * (unsigned)K * 2u);
     const __amdgpu_buffer_rsrc_t rW = rsrc(W, (unsigned)N * (unsigned)wpr * 4u);
@@ -165,24 +167,24 @@ void prefill_kernel(const uint16_t *__restrict__ x, const uint32_t *__restrict__
         for (int i = 0; i < kAUnits; ++i) store_a1(buf, i, ra[i]);
     };
     // ---- weight bits of this wave's FJ column fragments: row n0 + TN wn + 16 j + fc, this lane's
-    // word (ternary: four words) of a step and the group scale.  Rows past N lie past the
+    // two words (ternary: four words) of a step and the group scale.  Rows past N lie past the
     // buffer's range and load zeros; past the last step a uniform 2^31 is added to every offset
     // (no per-lane select, which the compiler would turn into a branch around each load).
     unsigned b_wofs[FJ], b_sofs[FJ];                   // byte offsets of this lane's rows at step 0
 #pragma unroll
     for (int j = 0; j < FJ; ++j) {
         const unsigned n = (unsigned)(n0 + wn * TN + 16 * j + fc);
-        b_wofs[j] = n * (unsigned)wpr * 4u + (T2 ? 16u * (unsigned)(fg >> 1) : 4u * (unsigned)fg);
+        b_wofs[j] = n * (unsigned)wpr * 4u + (T2 ? 16u : 8u) * (unsigned)(fg >> 1);
         b_sofs[j] = n * (unsigned)spr * 2u;
     }
-    using WordT = std::conditional_t<T2, u4v, uint32_t>;
+    using WordT = std::conditional_t<T2, u4v, u2v>;
     auto load_b = [&](int ks, WordT (&rw)[FJ], uint32_t (&rs)[FJ]) {
         const unsigned sw = ks < nk ? (unsigned)((T2 ? 32 : 16) * ks) : 0x80000000u;
         const unsigned ss = ks < nk ? (unsigned)(2 * ks) : 0x80000000u;
 #pragma unroll
         for (int j = 0; j < FJ; ++j) {
             if constexpr (T2) rw[j] = __builtin_amdgcn_raw_buffer_load_b128(rW, b_wofs[j] + sw, 0, 0);
-            else rw[j] = __builtin_amdgcn_raw_buffer_load_b32(rW, b_wofs[j] + sw, 0, 0);
+            else rw[j] = __builtin_amdgcn_raw_buffer_load_b64(rW, b_wofs[j] + sw, 0, 0);
             rs[j] = __builtin_amdgcn_raw_buffer_load_b16(rS, b_sofs[j] + ss, 0, 0);
         }
     };
@@ -213,9 +215,9 @@ void prefill_kernel(const uint16_t *__restrict__ x, const uint32_t *__restrict__
         constexpr int P = decltype(P_c)::value;
         const uint16_t *cur = lds + P * BUF_HALVES;
         uint16_t *nxt = lds + (P ^ 1) * BUF_HALVES;
-        // this step's weights: fold each scale's sign into the bits (ternary: and move this
-        // lane's eight slots of each word to the bottom)
-        uint32_t nw[FJ][T2 ? 4 : 1], s2[FJ];
+        // this step's weights: fold each scale's sign into the bits and move this lane's eight
+        // bits (ternary: slots) of each half-word to the bottom
+        uint32_t nw[FJ][T2 ? 4 : 2], s2[FJ];
 #pragma unroll
         for (int j = 0; j < FJ; ++j) {
             const uint32_t sv = rs[j] & 0xFFFFu;
@@ -227,7 +229,8 @@ void prefill_kernel(const uint16_t *__restrict__ x, const uint32_t *__restrict__
             } else {
                 const uint32_t flip = (sv & 0x8000u) ? 0u : 0xFFFFFFFFu;   // bit 1 of nw: negative product
                 s2[j] = (sv & 0x7FFFu) * 0x00010001u;
-                nw[j][0] = rw[j] ^ flip;
+#pragma unroll
+                for (int w = 0; w < 2; ++w) nw[j][w] = (rw[j][w] ^ flip) >> (8 * (fg & 1));
             }
         }
         load_b(ks + 1, rw, rs);                       // (past the last step: loads nothing)
@@ -235,7 +238,7 @@ void prefill_kernel(const uint16_t *__restrict__ x, const uint32_t *__restrict__
         auto expand = [&](int j, auto sub_c) {
             constexpr int sub = decltype(sub_c)::value;
             if constexpr (T2) return expand_t2(nw[j][sub], s2[j]);
-            else return expand_b1<8 * sub>(nw[j][0], s2[j]);
+            else return expand_b1<16 * (sub & 1)>(nw[j][sub >> 1], s2[j]);
         };
         // A fragment r = FI sub + i is row block i of substep sub; it is read from LDS kAhead
         // fragments before its three MFMAs, so only kAhead + 1 fragments are live at a time.
