@@ -548,11 +548,13 @@ hipError_t dispatch_mx(const uint16_t *x, const MxSet &set, int K, int mt, hipSt
         if constexpr (T2) return launch_mx<4, 1, 1, ODD, T2>(x, set, K, mt, st, desc);
         else return launch_mx<4, 1, 2, ODD, T2>(x, set, K, mt, st, desc);
     // 17..20 pairs (K = 17408 at the 27B shapes), binary: twelve waves of at most two pairs, each
-    // pair's A operands read where they are used (AL), so the twelve waves fit a CU; one 32-row tile
-    // per workgroup, or 16-row tiles two at a time past 256 of them.
+    // pair's A operands read where they are used (AL), so the twelve waves fit a CU; 16-row tiles
+    // on up to 256 workgroups with a one-slot ring while there are at most 256 32-row tiles, a
+    // two-slot ring past that.  (27B down, 320 16-row tiles, replayed alone: 7.69 us per launch
+    // against 8.33 on 160 workgroups of one 32-row tile and 8.56 with the two-slot ring.)
     default:
         if constexpr (T2) return launch_mx<5, 1, 1, ODD, T2>(x, set, K, mt, st, desc);
-        else return t32 <= 256 ? launch_mx<2, 1, 2, ODD, T2, 12, 1, true>(x, set, K, mt, st, desc)
+        else return t32 <= 256 ? launch_mx<2, 1, 1, ODD, T2, 12, 1, true>(x, set, K, mt, st, desc)
                                : launch_mx<2, 2, 1, ODD, T2, 12, 1, true>(x, set, K, mt, st, desc);
     }
 }

@@ -89,7 +89,7 @@ def test_step_8b_every_output(orc, dev):
 def test_step_27b_every_output(orc, dev):
     _check_step(orc, dev, synth.decode_27b(), False, 1,
                 {0: "gemv_mx<1,1,2,0,0,8,1>", 1: "gemv_mx<1,1,2,0,0,8,1>", 2: "gemv_mx<1,1,2,0,0,8,1>",
-                 3: "gemv_mx<2,1,2,0,0,12,1,1,AL>"})
+                 3: "gemv_mx<2,1,1,0,0,12,1,1,AL>"})
 
 
 def test_step_ternary_8b_every_output(orc, dev):

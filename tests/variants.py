@@ -63,8 +63,10 @@ def _decode_cases(t2):
         elif t2:
             branches = [([1000], (5, 1, 1, 4)), ([300, 400, 500], (5, 1, 1, 4))]
         else:
-            # binary: twelve waves of up to two pairs, A operands read per pair (AL)
-            branches = [([1000], (2, 1, 2, 12, 1, True)), ([300, 400, 500], (2, 1, 2, 12, 1, True)),
+            # binary: twelve waves of up to two pairs, A operands read per pair (AL), on 16-row
+            # tiles: a one-slot ring up to 256 32-row tiles, two slots past that
+            branches = [([1000], (2, 1, 1, 12, 1, True)), ([6000], (2, 1, 1, 12, 1, True)),
+                        ([300, 400, 500], (2, 1, 1, 12, 1, True)),
                         ([10000], (2, 2, 1, 12, 1, True)), ([3000, 3000, 3000], (2, 2, 1, 12, 1, True))]
         # the even-K class carries every branch; the odd and partial-pair classes every branch too,
         # but with smaller matrices where a branch allows it
@@ -124,7 +126,7 @@ TOKEN_CASES = [
     ("gemv", 2, 4096, [1000, 2000, 1000], "gemv_mx<1,1,1,0,0,4,0>", "group3"),
     ("gemv", 2, 4096, [2000, 2000], "gemv_mx<1,1,1,0,0,4,1>", "group2"),
     ("gemv_ws", 2, 12288, [4096], "gemv_mx<1,1,1,0,0,12,1>", "ws"),
-    ("gemv", 2, 17408, [4000], "gemv_mx<2,1,2,0,0,12,1,1,AL>", "al"),
+    ("gemv", 2, 17408, [4000], "gemv_mx<2,1,1,0,0,12,1,1,AL>", "al"),
 ]
 
 # prefill: 128-row tiles (two workgroups per CU) at every M; a short and a full-width M
