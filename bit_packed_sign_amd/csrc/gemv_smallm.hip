@@ -11,13 +11,14 @@
 // costs each lane one 16-byte load and one scale load, and the group scale goes straight into
 // the B operand as fp16 +-|s| (a negative scale is folded into the sign bits).
 //
-// k order inside an MFMA: for MFMA t = 4j + q of a group (word j, quarter q), lane (n, b)'s
-// B pair p holds the signs of bits 4q + p and 4q + p + 16 of word j -- one shift and one
-// and-or per fp16 pair -- and its A pair p holds x at the same two positions.
+// k order inside an MFMA: MFMA t = 4j + q of a group (word j, quarter q) covers k = 32j + 8q ..
+// 32j + 8q + 7 in natural order: lane (n, b)'s B pair p holds the signs of bits 8q + 2p and
+// 8q + 2p + 1 of word j -- one packed 16-bit shift of the half-word holding them (read by both
+// halves) and one and-or per fp16 pair -- and its A operand is those 8 activations as stored.
 //
 // x goes through LDS: the workgroup copies each 4096-wide K chunk of the 16 token rows
-// (128 KB) with contiguous 16-byte loads, all in flight at once; each wave then reads and
-// interleaves its A operands once per chunk and reuses them for every tile of the batch.
+// (128 KB) with contiguous 16-byte loads, all in flight at once; each wave then reads its A
+// operands once per chunk and reuses them for every tile of the batch.
 // Read straight from memory, every A load would touch 64 cache lines.  The merge table
 // reuses the same LDS once the batch's last chunk is done.
 #include <cstdio>
@@ -31,6 +32,7 @@ namespace bin1 {
 namespace {
 
 typedef unsigned u4v __attribute__((ext_vector_type(4)));
+typedef unsigned short us2v __attribute__((ext_vector_type(2)));
 
 constexpr int kRsrcFlags = 0x00020000;
 constexpr unsigned kOob = 0x80000000u;
@@ -50,24 +52,19 @@ static_assert(kChunkK == 8 * 64 * kWaves, "one 512-column slice of the chunk per
 constexpr int kXBytes = 16 * kXRow * 2;              // 16 token rows
 static_assert(kChunkK == 8 * 64 * kWaves && kWaves == 8, "one 16-byte load per thread per token row");
 
-// out dword p = (lo[p], hi[p]) for the 8 fp16 of lo and hi
-__device__ __forceinline__ void interleave(const u4v lo, const u4v hi, half8 &o0, half8 &o1)
-{
-    const u4v a{__builtin_amdgcn_perm(hi.x, lo.x, 0x05040100u), __builtin_amdgcn_perm(hi.x, lo.x, 0x07060302u),
-                __builtin_amdgcn_perm(hi.y, lo.y, 0x05040100u), __builtin_amdgcn_perm(hi.y, lo.y, 0x07060302u)};
-    const u4v b{__builtin_amdgcn_perm(hi.z, lo.z, 0x05040100u), __builtin_amdgcn_perm(hi.z, lo.z, 0x07060302u),
-                __builtin_amdgcn_perm(hi.w, lo.w, 0x05040100u), __builtin_amdgcn_perm(hi.w, lo.w, 0x07060302u)};
-    o0 = __builtin_bit_cast(half8, a);
-    o1 = __builtin_bit_cast(half8, b);
-}
-
-// B operand of quarter Q: pair p = (+-|s| for bit 4Q + p, for bit 4Q + p + 16) of nw, bit 1 of
+// B operand of quarter Q: pair p = (+-|s| for bit 8Q + 2p, for bit 8Q + 2p + 1) of nw, bit 1 of
 // nw meaning a negative product.
 template <int Q>
 __device__ __forceinline__ half8 expand_q(uint32_t nw, uint32_t s2abs)
 {
-    const u4v d{((nw << (15 - 4 * Q)) & 0x80008000u) | s2abs, ((nw << (14 - 4 * Q)) & 0x80008000u) | s2abs,
-                ((nw << (13 - 4 * Q)) & 0x80008000u) | s2abs, ((nw << (12 - 4 * Q)) & 0x80008000u) | s2abs};
+    const us2v v = us2v((unsigned short)(Q < 2 ? nw : nw >> 16));
+    u4v d;
+#pragma unroll
+    for (int p = 0; p < 4; ++p) {
+        const int bit = 8 * (Q & 1) + 2 * p;
+        const us2v sh{(unsigned short)(15 - bit), (unsigned short)(14 - bit)};
+        d[p] = (__builtin_bit_cast(uint32_t, v << sh) & 0x80008000u) | s2abs;
+    }
     return __builtin_bit_cast(half8, d);
 }
 
@@ -197,17 +194,10 @@ void gemv_smallm_kernel(const uint16_t *__restrict__ x, int M, int K, int tq, in
         for (int d = 0; d < DS; ++d) {
             const int c = c0 + d;
             if (c >= nloop) break;                    // uniform
-            // this wave's A operands for chunk c
+            // this wave's A operands for chunk c: 8 activations of each token row per MFMA
             const uint16_t *xa = xs + n * kXRow + 128 * (4 * wave + b);
 #pragma unroll
-            for (int j = 0; j < 4; ++j) {
-                const u4v l0 = *reinterpret_cast<const u4v *>(xa + 32 * j);
-                const u4v l1 = *reinterpret_cast<const u4v *>(xa + 32 * j + 8);
-                const u4v h0 = *reinterpret_cast<const u4v *>(xa + 32 * j + 16);
-                const u4v h1 = *reinterpret_cast<const u4v *>(xa + 32 * j + 24);
-                interleave(l0, h0, A[4 * j + 0], A[4 * j + 1]);
-                interleave(l1, h1, A[4 * j + 2], A[4 * j + 3]);
-            }
+            for (int j = 0; j < 16; ++j) A[j] = *reinterpret_cast<const half8 *>(xa + 8 * j);
 #pragma unroll
             for (int t = 0; t < TB; ++t) {
                 SmSlot &sl = ring[d][t];
