@@ -6,6 +6,7 @@ Every call recompiles; objects go to bit_packed_sign_amd/_build/.
 """
 from __future__ import annotations
 
+import ctypes
 import os
 import subprocess
 import sys
@@ -53,6 +54,13 @@ def build(verbose: bool = False) -> str:
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError(f"link failed:\n{r.stdout}\n{r.stderr}")
+    # every symbol must resolve now, not at the first call on a GPU machine (a kernel template the
+    # host pass failed to instantiate links but leaves its stub undefined)
+    try:
+        ctypes.CDLL(tmp, mode=os.RTLD_NOW)
+    except OSError as e:
+        os.remove(tmp)
+        raise RuntimeError(f"{LIB} does not load: {e}") from None
     os.replace(tmp, LIB)
     return LIB
 

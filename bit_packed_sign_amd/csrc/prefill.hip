@@ -12,8 +12,8 @@
 // advances 128 (one scale group) per step, in four 32-wide substeps.
 //
 //  * Activations go through LDS (two buffers, one barrier per step), in natural k order: the
-//    next step's 16-byte chunks are prefetched into registers and stored while the MFMAs read
-//    the current buffer.
+//    next step's activations are loaded straight into the other buffer (buffer_load ... lds,
+//    no registers and no LDS stores) while the MFMAs read the current one.
 //  * Weights never touch LDS: every wave expands the bits of its own 48 columns straight into
 //    B-operand registers, so each weight column is expanded exactly once per workgroup and each
 //    expanded operand serves all 8 row blocks of the tile (two VALU operations per fp16 pair
@@ -45,7 +45,6 @@ typedef float f4v __attribute__((ext_vector_type(4)));
 constexpr int BN = 192, BK = 128;
 constexpr int LDK = BK + 16;                      // LDS row stride in halves (288 B)
 constexpr int kRsrcFlags = 0x00020000;
-constexpr unsigned kOob = 0x80000000u;
 
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t rsrc(const void *p, unsigned bytes)
 {
@@ -107,8 +106,7 @@ void prefill_kernel(const uint16_t *__restrict__ x, const uint32_t *__restrict__
                     const uint16_t *__restrict__ S, uint16_t *__restrict__ y, int M, int K, int N,
                     int tiles_m)
 {
-    constexpr int kThreads = 256, TN = BN / 4;
-    constexpr int kAUnits = BM * 8 / kThreads;    // (row, 16-wide chunk) staging units per thread
+    constexpr int TN = BN / 4;
     constexpr int FI = BM / 16, FJ = TN / 16;
     constexpr int BUF_HALVES = BM * LDK;          // one activation buffer
     extern __shared__ __attribute__((aligned(16))) uint16_t lds[];
@@ -132,39 +130,30 @@ void prefill_kernel(const uint16_t *__restrict__ x, const uint32_t *__restrict__
     const __amdgpu_buffer_rsrc_t rW = rsrc(W, (unsigned)N * (unsigned)wpr * 4u);
     const __amdgpu_buffer_rsrc_t rS = rsrc(S, (unsigned)N * (unsigned)spr * 2u);
 
-    // ---- activation staging, in natural k order.  Unit i of a thread is the 16 activations
-    // [16 idx, 16 idx + 16) of one row in a step (32 bytes, two 16-byte loads and stores): row
-    // block i % kRB (64 rows each), chunk idx = (t & 3) + 4 (i / kRB).  Eight consecutive lanes
-    // take chunks 0..3 of two adjacent rows, so the rows' 68-dword LDS stride puts their 16-byte
-    // writes in distinct banks.
-    constexpr int kRB = BM / 64;
-    unsigned a_gofs[kRB];                             // byte offset of the row block's unit in x at step 0
-    int a_lofs[kRB];                                  // half offset of the unit in an LDS buffer
+    // ---- activation staging: straight from memory into LDS (`buffer_load_dwordx4 ... lds`, no
+    // registers, no LDS stores).  One such load writes 64 consecutive 16-byte slots of the padded
+    // LDS image of a step (row r, slot q at 16 (18 r + q) bytes; slots 16 and 17 of a row are
+    // padding), lane l the l-th slot.  Wave w issues loads w kDma .. w kDma + kDma - 1 of a
+    // step's kDma * 4.  A lane's global offset is fixed per load and the step's offset is a
+    // uniform add, so the loads cost no VALU work; padding slots and rows past M point at the end
+    // of x (out of range: zeros), and past the last step a uniform 2^31 is added.
+    constexpr int kRowSlots = LDK / 8;                 // 16-byte slots per LDS row (16 + 2 padding)
+    constexpr int kDma = BM * kRowSlots / 64 / 4;      // loads per wave per step
+    static_assert(BM * kRowSlots % 256 == 0, "the padded image is a whole number of loads per wave");
+    const unsigned xbytes = (unsigned)M * (unsigned)K * 2u;
+    unsigned a_vofs[kDma];
 #pragma unroll
-    for (int i = 0; i < kRB; ++i) {
-        const int row = 64 * i + 2 * (t >> 3) + ((t >> 2) & 1), idx = t & 3;
+    for (int i = 0; i < kDma; ++i) {
+        const int slot = (wn * kDma + i) * 64 + lane, row = slot / kRowSlots, q = slot % kRowSlots;
         const int m = m0 + row;
-        a_gofs[i] = m < M ? ((unsigned)m * (unsigned)K + 16u * (unsigned)idx) * 2u : kOob;
-        a_lofs[i] = row * LDK + 16 * idx;
+        a_vofs[i] = (q < 16 && m < M) ? ((unsigned)m * (unsigned)K + 8u * (unsigned)q) * 2u : xbytes;
     }
-    auto load_a1 = [&](int ks, int i, u4v (&r)[2]) {
-        const bool ok = a_gofs[i % kRB] != kOob && ks < nk;
-        const unsigned off = a_gofs[i % kRB] + (unsigned)(ks * BK * 2 + 128 * (i / kRB));
-        r[0] = __builtin_amdgcn_raw_buffer_load_b128(rx, ok ? off : kOob, 0, 0);
-        r[1] = __builtin_amdgcn_raw_buffer_load_b128(rx, ok ? off + 16u : kOob, 0, 0);
-    };
-    auto store_a1 = [&](uint16_t *buf, int i, const u4v (&r)[2]) {
-        u4v *dst = reinterpret_cast<u4v *>(buf + a_lofs[i % kRB] + 64 * (i / kRB));
-        dst[0] = r[0];
-        dst[1] = r[1];
-    };
-    auto load_a = [&](int ks, u4v (&ra)[kAUnits][2]) {
+    auto dma_a = [&](int ks, uint16_t *buf) {
+        const unsigned so = ks < nk ? (unsigned)(ks * BK * 2) : 0x80000000u;
 #pragma unroll
-        for (int i = 0; i < kAUnits; ++i) load_a1(ks, i, ra[i]);
-    };
-    auto store_a = [&](uint16_t *buf, const u4v (&ra)[kAUnits][2]) {
-#pragma unroll
-        for (int i = 0; i < kAUnits; ++i) store_a1(buf, i, ra[i]);
+        for (int i = 0; i < kDma; ++i)
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(
+                rx, (__attribute__((address_space(3))) void *)(buf + (wn * kDma + i) * 512), 16, (int)a_vofs[i], (int)so, 0, 0);
     };
     // ---- weight bits of this wave's FJ column fragments: row n0 + TN wn + 16 j + fc, this lane's
     // two words (ternary: four words) of a step and the group scale.  Rows past N lie past the
@@ -195,26 +184,24 @@ void prefill_kernel(const uint16_t *__restrict__ x, const uint32_t *__restrict__
 #pragma unroll
         for (int j = 0; j < FJ; ++j) acc[i][j] = f4v{0.f, 0.f, 0.f, 0.f};
 
-    // Activations are loaded one K-step before they are stored to LDS, weights one step before
-    // use: every workgroup of an XCD reads the same activation panel at about the same time, so
-    // a step's first touch comes from HBM.  Loads and stores are unconditional (out-of-range
-    // offsets past the last step) so the loop is straight-line and each wait covers only the
-    // loads it needs.
-    u4v ra[kAUnits][2];
+    // Activations and weights are requested one K-step before use; the barrier that ends a step
+    // waits for both (so the next step's activations are in LDS for every wave).  Loads are
+    // unconditional (out-of-range offsets past the last step) so the loop is straight-line.
     WordT rw[FJ];
     uint32_t rs[FJ];
-    load_a(0, ra);
+    dma_a(0, lds);
     load_b(0, rw, rs);
-    store_a(lds, ra);
+    __builtin_amdgcn_s_waitcnt(0x0F70);                // vmcnt(0): step 0's activations are in LDS
     __syncthreads();
-    load_a(1, ra);
 
-    // one K-step on buffer P: its weights are folded and step ks + 1's requested in their place;
-    // the activations of step ks + 1 go to the other buffer and step ks + 2's are requested
+    // one K-step on buffer P: the activations of step ks + 1 are requested into the other buffer
+    // (every wave finished reading it before the barrier that ended the previous step), this
+    // step's weights are folded and step ks + 1's requested in their place
     auto step = [&](int ks, auto P_c) {
         constexpr int P = decltype(P_c)::value;
         const uint16_t *cur = lds + P * BUF_HALVES;
         uint16_t *nxt = lds + (P ^ 1) * BUF_HALVES;
+        dma_a(ks + 1, nxt);
         // this step's weights: fold each scale's sign into the bits and move this lane's eight
         // bits (ternary: slots) of each half-word to the bottom
         uint32_t nw[FJ][T2 ? 4 : 2], s2[FJ];
@@ -242,11 +229,8 @@ void prefill_kernel(const uint16_t *__restrict__ x, const uint32_t *__restrict__
         };
         // A fragment r = FI sub + i is row block i of substep sub; it is read from LDS kAhead
         // fragments before its three MFMAs, so only kAhead + 1 fragments are live at a time.
-        // A substep's B operands are expanded at its start (expanding them a substep ahead held
-        // 12 more registers, and the register allocator then parked staging data in AGPRs).  Each
-        // substep also carries a share of the staging work (LDS store of the next step's
-        // activations, loads two steps ahead).  Every wave finished reading the other buffer
-        // before the barrier that ended the previous step.
+        // A substep's B operands are expanded at its start (expanding them a substep ahead was
+        // no faster).
         constexpr int kAhead = 4;
         auto read_a = [&](int r) { return *reinterpret_cast<const half8v *>(as + 16 * (r % FI) * LDK + kSubK * (r / FI)); };
         half8v a[4 * FI], b[FJ];
@@ -264,17 +248,15 @@ void prefill_kernel(const uint16_t *__restrict__ x, const uint32_t *__restrict__
                 for (int j = 0; j < FJ; ++j)
                     acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_f16(a[r], b[j], acc[i][j], 0, 0, 0);
             }
-#pragma unroll
-            for (int i = sub; i < kAUnits; i += 4) {
-                store_a1(nxt, i, ra[i]);
-                load_a1(ks + 2, i, ra[i]);
-            }
             __builtin_amdgcn_sched_barrier(0);
         };
         substep(std::integral_constant<int, 0>{});
         substep(std::integral_constant<int, 1>{});
         substep(std::integral_constant<int, 2>{});
         substep(std::integral_constant<int, 3>{});
+        // every load of this step (the next step's activations into LDS, its weights) has
+        // landed before the barrier: s_waitcnt vmcnt(0), the other counters left alone
+        __builtin_amdgcn_s_waitcnt(0x0F70);
         __syncthreads();
     };
     // (an odd step count runs one extra step on all-zero operands, which adds exactly 0)
