@@ -231,7 +231,7 @@ void prefill_kernel(const uint16_t *__restrict__ x, const uint32_t *__restrict__
         // fragments before its three MFMAs, so only kAhead + 1 fragments are live at a time.
         // A substep's B operands are expanded at its start (expanding them a substep ahead was
         // no faster).
-        constexpr int kAhead = 4;
+        constexpr int kAhead = 8;
         auto read_a = [&](int r) { return *reinterpret_cast<const half8v *>(as + 16 * (r % FI) * LDK + kSubK * (r / FI)); };
         half8v a[4 * FI], b[FJ];
 #pragma unroll
