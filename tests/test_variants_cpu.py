@@ -34,9 +34,8 @@ def test_query_names_the_expected_variant(b1, case):
 def test_every_decode_branch_is_reached():
     """Each (pairs per wave, ring slots, rows per tile, waves) branch of the batch-1 kernel occurs
     with even and odd K / 128, with a partial last pair, and with one/two and three/four matrices."""
-    for cases, expected_branches in ((DECODE_CASES, 5 + 2 + 3 + 2 + 2), (DECODE_T2_CASES, 6 + 4 + 3 + 2 + 1)):
-        # (SP 1: the three-or-four-matrix fallback of the two-slot layout too, for ternary rows;
-        # binary rows of 5..8 and 17..20 pairs have layouts of their own)
+    for cases, expected_branches in ((DECODE_CASES, 5 + 2 + 3 + 2 + 2), (DECODE_T2_CASES, 5 + 4 + 3 + 2 + 1)):
+        # (binary rows of 5..8 and 17..20 pairs have layouts of their own)
         seen = {}
         for op, M, K, Ns, exp, kind in cases:
             core = exp.split("<")[1].rstrip(">").split(",")
