@@ -260,7 +260,7 @@ int bin1_chain_status(const bin1_chain_plan *plan, int *runs, int *error);
  * buf once, with 16-byte nontemporal loads spread over `grid` workgroups of 256 threads, `unroll`
  * loads in flight per thread (4, 8 or 16), and writes one XOR digest per wave into sink (device
  * uint32 [4 * grid]).  Timing it gives the HBM read rate this GPU sustains, the reference against
- * which the decode products' bandwidth is judged (decode speed is bounded by bandwidth over weight
+ * which the decode products' bandwidth is measured (decode speed is bounded by bandwidth over weight
  * bytes: "Bonsai 27B" page, section "Low-bit kernels for hybrid attention").  Requires buf 16-byte
  * aligned, bytes a positive multiple of 16, 1 <= grid <= 65536, and sink not overlapping buf. */
 int bin1_stream_read(const void *buf, size_t bytes, uint32_t *sink, int grid, int unroll, void *stream);
