@@ -54,7 +54,7 @@ def build(verbose: bool = False) -> str:
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError(f"link failed:\n{r.stdout}\n{r.stderr}")
-    # every symbol must resolve now, not at the first call on a GPU machine (a kernel template the
+    # every symbol must resolve now, not at the first call on a GPU (a kernel template the
     # host pass failed to instantiate links but leaves its stub undefined)
     try:
         ctypes.CDLL(tmp, mode=os.RTLD_NOW)
