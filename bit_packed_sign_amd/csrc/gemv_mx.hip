@@ -522,8 +522,13 @@ hipError_t dispatch_mx(const uint16_t *x, const MxSet &set, int K, int mt, hipSt
     case 1:
         if (t16 > 256 && t32 <= 256) return launch_mx<1, 1, 2, ODD, T2>(x, set, K, mt, st, desc);
         if (t16 > 256 && t32 <= cap) return launch_mx<1, 1, 1, ODD, T2, 12, 3>(x, set, K, mt, st, desc);
-        // (ternary lm_head, 4096 x 151936: 47.8 us on this one-slot ring against 49.3 on two slots)
-        if (!few16) return launch_mx<1, 1, 2, ODD, T2, 12, 3>(x, set, K, mt, st, desc);
+        // Past three 16-row tiles per workgroup slot: binary rows on 32-row tiles in three wave
+        // groups; ternary rows (twice the bytes) on 16-row tiles in two groups (4096 x 151936:
+        // 44.1 us against 47.8 us on the binary layout, 49.3 us with a two-slot ring).
+        if (!few16) {
+            if constexpr (T2) return launch_mx<1, 1, 1, ODD, T2, 8, 2>(x, set, K, mt, st, desc);
+            else return launch_mx<1, 1, 2, ODD, T2, 12, 3>(x, set, K, mt, st, desc);
+        }
         return one16 ? launch_mx<1, 1, 1, ODD, T2>(x, set, K, mt, st, desc)
                  : one   ? launch_mx<1, 1, 2, ODD, T2, 12, 3>(x, set, K, mt, st, desc)
                          : launch_mx<1, 3, 1, ODD, T2>(x, set, K, mt, st, desc);

@@ -95,7 +95,7 @@ def test_step_27b_every_output(orc, dev):
 def test_step_ternary_8b_every_output(orc, dev):
     _check_step(orc, dev, synth.decode_8b(), True, 1,
                 {0: "gemv_mx<1,1,2,0,1,4,1>", 2: "gemv_mx<1,1,1,0,1,12,1,3>", 3: "gemv_mx<1,1,1,0,1,12,1>",
-                 144: "gemv_mx<1,1,2,0,1,12,1,3>"})
+                 144: "gemv_mx<1,1,1,0,1,8,1,2>"})
 
 
 def test_step_mlp16_every_product(orc, dev):

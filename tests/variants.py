@@ -38,10 +38,11 @@ def _decode_cases(t2):
         if sp == 1:
             # up to 256 16-row tiles one per workgroup; then one 32-row tile per workgroup; then
             # three groups of four waves per workgroup (TT = 3) on 16-row tiles; a three-slot ring
-            # of 16-row tiles; past that 32-row tiles in three wave groups on a one-slot ring.
+            # of 16-row tiles; past that 32-row tiles in three wave groups on a one-slot ring
+            # (ternary rows: 16-row tiles in two wave groups).
             # Three or four matrices: one group of four waves in the same tiles.
-            big = (1, 1, 2, 12, 3)
-            big3 = (1, 1, 2, 4)
+            big = (1, 1, 1, 8, 2) if t2 else (1, 1, 2, 12, 3)
+            big3 = (1, 1, 1, 4) if t2 else (1, 1, 2, 4)
             branches = [([100], (1, 1, 1, 4)), ([6000], (1, 1, 2, 4)), ([20000], (1, 1, 1, 12, 3)),
                         ([30000], (1, 3, 1, 4)), ([40000], big), ([100, 200, 300], (1, 1, 1, 4)),
                         ([2000, 2000, 2000], (1, 1, 2, 4)), ([7000, 7000, 7000], (1, 1, 1, 4)),
